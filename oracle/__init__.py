@@ -1,0 +1,188 @@
+"""CPU oracle for the BlockFFN layer forward (router + chunk-union expert FFN).
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
+CPU-baseline leg use this package; the GPU library never imports, links or calls it,
+and shares no code with it. The arithmetic lives in ``blockffn_oracle.c`` (plain
+loops, double accumulation); this module builds it with gcc, loads it with ctypes
+and adds the sparsity meter used to check the synthetic masks.
+
+Pages followed (BlockFFN, arXiv 2507.08771):
+  * skill page "BlockFFN: Sparse Mixture-of-Experts Optimized for End-Device
+    Deployment": "Core Concept" (union of active experts over n tokens, masking after
+    the computation), "Architecture Overview" (ReLU + RMSNorm router, non-gated Swish
+    experts), "Router Architecture Setup" (no router bias, RMSNorm over experts),
+    "Chunk Sparsification Loss" (aligned chunks, ceil(S/L) of them).
+  * paper card, Abstract: TLS and 8-token CLS as the sparsity measures.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "blockffn_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+
+# torch.nn.RMSNorm's default eps for fp32 inputs (torch.finfo(torch.float32).eps):
+# the pages construct the norm without an eps, so the module default applies.
+FP32_EPS = float(np.finfo(np.float32).eps)
+
+
+def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
+    """Compile the oracle with gcc (-O2, no fast-math, no FMA contraction, OpenMP)."""
+    cmd = ["gcc", "-O2", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-std=c11", "-Wall", "-Wextra", "-shared", "-fPIC", src, "-o", out, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return out
+
+
+_lib = None
+
+
+def use_library(path: str | None):
+    """Load the oracle from another build of the C file (the mutation tests use this
+    to check that the pins reject planted mistakes); None restores the default."""
+    global _lib
+    _lib = None
+    if path is not None:
+        _bind(ctypes.CDLL(path))
+
+
+def _load():
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH) or (
+            os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
+        build()
+    return _bind(ctypes.CDLL(_LIB_PATH))
+
+
+def _bind(lib):
+    global _lib
+    P = ctypes.c_void_p
+    I64 = ctypes.c_int64
+    lib.oracle_num_threads.restype = ctypes.c_int
+    lib.oracle_router.argtypes = [P, P, P, P, ctypes.c_double, I64, I64, I64, P, P]
+    lib.oracle_router.restype = None
+    lib.oracle_chunk_union.argtypes = [P, I64, I64, I64, P, P, P]
+    lib.oracle_chunk_union.restype = None
+    lib.oracle_chunk_ffn.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, P, P, P, P, P]
+    lib.oracle_chunk_ffn.restype = None
+    lib.oracle_token_ffn.argtypes = [P, P, P, P, I64, I64, I64, I64, P, P]
+    lib.oracle_token_ffn.restype = None
+    _lib = lib
+    return lib
+
+
+def _f32(a) -> np.ndarray:
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def num_threads() -> int:
+    return int(_load().oracle_num_threads())
+
+
+def router(x, w_r, gain=None, bias=None, eps: float = FP32_EPS):
+    """Return (logits, scores), both float64 [T, E]. See oracle_router in the C file."""
+    lib = _load()
+    x = _f32(x)
+    w_r = _f32(w_r)
+    T, d_h = x.shape
+    E = w_r.shape[0]
+    assert w_r.shape == (E, d_h)
+    gain = None if gain is None else _f32(gain)
+    bias = None if bias is None else _f32(bias)
+    logits = np.empty((T, E), np.float64)
+    scores = np.empty((T, E), np.float64)
+    lib.oracle_router(_ptr(x), _ptr(w_r), _ptr(gain), _ptr(bias), float(eps),
+                      T, d_h, E, _ptr(logits), _ptr(scores))
+    return logits, scores
+
+
+def chunk_union(scores, n: int):
+    """Return (masks uint64 [C, W], lists int32 [C, E], counts int32 [C])."""
+    lib = _load()
+    scores = _f32(scores)
+    T, E = scores.shape
+    C = -(-T // n)
+    W = -(-E // 64)
+    masks = np.empty((C, W), np.uint64)
+    lists = np.empty((C, E), np.int32)
+    counts = np.empty((C,), np.int32)
+    lib.oracle_chunk_union(_ptr(scores), T, E, n, _ptr(masks), _ptr(lists), _ptr(counts))
+    return masks, lists, counts
+
+
+def _check_ffn_shapes(x, scores, w1, w2):
+    T, d_h = x.shape
+    E, d_e, d_h1 = w1.shape
+    assert d_h1 == d_h and w2.shape == (E, d_h, d_e) and scores.shape == (T, E)
+    return T, d_h, E, d_e
+
+
+def chunk_ffn(x, scores, w1, w2, n: int) -> np.ndarray:
+    """Union-then-mask FFN, float64 [T, d_h]."""
+    lib = _load()
+    x, scores, w1, w2 = _f32(x), _f32(scores), _f32(w1), _f32(w2)
+    T, d_h, E, d_e = _check_ffn_shapes(x, scores, w1, w2)
+    C = -(-T // n)
+    y = np.empty((T, d_h), np.float64)
+    masks = np.empty((C, -(-E // 64)), np.uint64)
+    lists = np.empty((C, E), np.int32)
+    counts = np.empty((C,), np.int32)
+    h = np.empty((lib.oracle_num_threads(), d_e), np.float64)
+    lib.oracle_chunk_ffn(_ptr(x), _ptr(scores), _ptr(w1), _ptr(w2), T, d_h, E, d_e, n,
+                         _ptr(y), _ptr(masks), _ptr(lists), _ptr(counts), _ptr(h))
+    return y
+
+
+def token_ffn(x, scores, w1, w2) -> np.ndarray:
+    """Per-token brute force over each token's own active experts, float64 [T, d_h]."""
+    lib = _load()
+    x, scores, w1, w2 = _f32(x), _f32(scores), _f32(w1), _f32(w2)
+    T, d_h, E, d_e = _check_ffn_shapes(x, scores, w1, w2)
+    y = np.empty((T, d_h), np.float64)
+    h = np.empty((lib.oracle_num_threads(), d_e), np.float64)
+    lib.oracle_token_ffn(_ptr(x), _ptr(scores), _ptr(w1), _ptr(w2), T, d_h, E, d_e,
+                         _ptr(y), _ptr(h))
+    return y
+
+
+# --------------------------------------------------------------------------------
+# Sparsity meter. The pages name token-level sparsity (TLS) and L-token chunk-level
+# sparsity (CLS) without defining them in formulas; the readings used here are:
+#   TLS   = fraction of (token, expert) pairs that are inactive;
+#   CLS_L = 1 - mean over aligned, non-overlapping L-token chunks of |U|/E,
+#           i.e. the fraction of experts left out of a chunk's union (paper-card
+#           Abstract: the union of consecutive tokens is what CLS measures; chunks as
+#           in "Chunk Sparsification Loss"). A partial last chunk counts as a chunk.
+# --------------------------------------------------------------------------------
+
+def tls(active: np.ndarray) -> float:
+    active = np.asarray(active, dtype=bool)
+    return 1.0 - float(active.sum()) / active.size
+
+
+def union_fraction(active: np.ndarray, L: int) -> np.ndarray:
+    """|U_c| / E for every aligned L-token chunk c."""
+    active = np.asarray(active, dtype=bool)
+    T, E = active.shape
+    C = -(-T // L)
+    out = np.empty(C)
+    for c in range(C):
+        out[c] = active[c * L:min(c * L + L, T)].any(axis=0).sum() / E
+    return out
+
+
+def cls(active: np.ndarray, L: int) -> float:
+    return 1.0 - float(union_fraction(active, L).mean())

@@ -1,0 +1,216 @@
+/*
+ * CPU oracle for the BlockFFN layer forward: router and chunk-union expert FFN.
+ *
+ * THIS FILE IS TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg load it. The GPU library shares no code with it and
+ * never calls it.
+ *
+ * It is a plain, slow, obviously correct restatement of what the layer computes:
+ * straight loops, every sum accumulated in double precision in ascending index
+ * order, no blocking, no fusion, no reordering. Inputs are fp32 arrays; bf16 inputs
+ * are widened to fp32 by the caller, which is exact.
+ *
+ * Sources (web pages on BlockFFN, arXiv 2507.08771):
+ *  [S1] "BlockFFN: Sparse Mixture-of-Experts Optimized for End-Device Deployment"
+ *       (skill page), section "Architecture Overview": the router is a linear map
+ *       with ReLU followed by RMSNorm; experts are non-gated MLPs with Swish and a
+ *       width d_e much smaller than d_h.
+ *  [S2] same page, section "Core Concept": the accelerator computes only the union
+ *       of experts activated across n consecutive tokens and masks the unneeded
+ *       activations after the computation; the "CUTLASS Acceleration Kernel" item
+ *       of "Architecture Overview" fixes n = 32 tokens.
+ *  [S3] same page, "Router Architecture Setup": the router linear has no bias,
+ *       RMSNorm runs over the expert axis, the expert is fc2(SiLU(fc1(x))).
+ *  [S4] same page, "Chunk Sparsification Loss": chunks are consecutive, aligned,
+ *       ceil(S/L) of them, the last one possibly partial.
+ *  [S5] paper card (sota2), Abstract: a router integrating ReLU and RMSNorm.
+ *
+ * Readings where the pages are silent (each is also listed in the design notes):
+ *  - Experts carry no biases and dropout is the identity (inference).
+ *  - The gate is the post-RMSNorm score s[t,e]; an expert is active for a token
+ *    exactly when s[t,e] != 0 (compared in fp32, the precision scores are stored in;
+ *    -0 counts as inactive).
+ *  - ReLU maps every logit that is not > 0 (NaN included) to 0.
+ *  - The union list is in ascending expert id; list entries past the count are -1.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* Number of threads the parallel loops below use (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+/*
+ * Router, per token t, following [S1] "Architecture Overview", [S3] and [S5]:
+ *   l[t,e] = sum_j x[t,j] * W_r[e,j]            (+ bias[e] when bias != NULL)
+ *   r[t,e] = l[t,e] if l[t,e] > 0 else 0          (ReLU)
+ *   s[t,e] = r[t,e] / sqrt(mean_e r[t,e]^2 + eps) * gain[e]   (RMSNorm over experts)
+ * x: [T, d_h], w_r: [E, d_h] (nn.Linear layout), gain/bias: [E] or NULL (ones/zeros).
+ * Outputs logits, scores: [T, E] double.
+ */
+void oracle_router(const float *x, const float *w_r, const float *gain, const float *bias,
+                   double eps, int64_t T, int64_t d_h, int64_t E,
+                   double *logits, double *scores)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        const float *xt = x + t * d_h;
+        double *lt = logits + t * E;
+        double *st = scores + t * E;
+
+        for (int64_t e = 0; e < E; ++e) {
+            const float *we = w_r + e * d_h;
+            double acc = 0.0;
+            for (int64_t j = 0; j < d_h; ++j)
+                acc += (double)xt[j] * (double)we[j];
+            if (bias)
+                acc += (double)bias[e];
+            lt[e] = acc;
+        }
+
+        double sumsq = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            double r = lt[e] > 0.0 ? lt[e] : 0.0;
+            st[e] = r;
+            sumsq += r * r;
+        }
+        double mean_sq = sumsq / (double)E;
+        double denom = sqrt(mean_sq + eps);
+        for (int64_t e = 0; e < E; ++e) {
+            double g = gain ? (double)gain[e] : 1.0;
+            st[e] = st[e] / denom * g;
+        }
+    }
+}
+
+/*
+ * Chunk union, following [S2] and [S4]: chunk c holds tokens
+ * [c*n, min(c*n + n, T)); expert e is in the union U_c when some token of the chunk
+ * has scores[t,e] != 0. Outputs, for C = ceil(T/n) chunks and W = ceil(E/64) words:
+ *   masks  [C][W]  bit (e % 64) of word (e / 64) set when e is in U_c
+ *   lists  [C][E]  the members of U_c in ascending order, then -1
+ *   counts [C]     |U_c|
+ */
+void oracle_chunk_union(const float *scores, int64_t T, int64_t E, int64_t n,
+                        uint64_t *masks, int32_t *lists, int32_t *counts)
+{
+    int64_t C = (T + n - 1) / n;
+    int64_t W = (E + 63) / 64;
+    for (int64_t c = 0; c < C; ++c) {
+        uint64_t *mc = masks + c * W;
+        int32_t *lc = lists + c * E;
+        int64_t t_end = c * n + n < T ? c * n + n : T;
+
+        for (int64_t w = 0; w < W; ++w)
+            mc[w] = 0;
+        for (int64_t t = c * n; t < t_end; ++t)
+            for (int64_t e = 0; e < E; ++e)
+                if (scores[t * E + e] != 0.0f)
+                    mc[e / 64] |= (uint64_t)1 << (e % 64);
+
+        int32_t count = 0;
+        for (int64_t e = 0; e < E; ++e)
+            if (mc[e / 64] & ((uint64_t)1 << (e % 64)))
+                lc[count++] = (int32_t)e;
+        counts[c] = count;
+        for (int64_t i = count; i < E; ++i)
+            lc[i] = -1;
+    }
+}
+
+/*
+ * One expert applied to one token and added into y with weight s, following [S1]
+ * "Architecture Overview" and [S3]: Expert_e(x) = W2_e * swish(W1_e * x), with
+ * swish(a) = a / (1 + exp(-a)) (SiLU, beta = 1).
+ * w1e: [d_e, d_h] (fc1 weight), w2e: [d_h, d_e] (fc2 weight), h: scratch [d_e].
+ */
+static void add_expert_output(const float *xt, const float *w1e, const float *w2e,
+                              double s, int64_t d_h, int64_t d_e, double *h, double *yt)
+{
+    for (int64_t k = 0; k < d_e; ++k) {
+        double a = 0.0;
+        for (int64_t j = 0; j < d_h; ++j)
+            a += (double)w1e[k * d_h + j] * (double)xt[j];
+        h[k] = a / (1.0 + exp(-a));
+    }
+    for (int64_t j = 0; j < d_h; ++j) {
+        double z = 0.0;
+        for (int64_t k = 0; k < d_e; ++k)
+            z += (double)w2e[j * d_e + k] * h[k];
+        yt[j] += s * z;
+    }
+}
+
+/*
+ * Union-then-mask chunk FFN, following [S2]: every expert of the chunk's union is
+ * evaluated for every token of the chunk and its output is weighted by that token's
+ * score, which is 0 for tokens where the expert is inactive ("masking after the
+ * computation"). Experts outside the union are never read.
+ *   y[t,:] = sum_{e in U_c(t), ascending} s[t,e] * Expert_e(x[t,:])
+ * x: [T, d_h]; scores: [T, E]; w1: [E, d_e, d_h]; w2: [E, d_h, d_e]; y: [T, d_h].
+ * h_scratch: [nthreads][d_e] doubles, lists/counts: [C][E] and [C] scratch.
+ */
+void oracle_chunk_ffn(const float *x, const float *scores, const float *w1,
+                      const float *w2, int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                      int64_t n, double *y, uint64_t *masks, int32_t *lists,
+                      int32_t *counts, double *h_scratch)
+{
+    oracle_chunk_union(scores, T, E, n, masks, lists, counts);
+
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+#ifdef _OPENMP
+        double *h = h_scratch + (int64_t)omp_get_thread_num() * d_e;
+#else
+        double *h = h_scratch;
+#endif
+        int64_t c = t / n;
+        double *yt = y + t * d_h;
+        for (int64_t j = 0; j < d_h; ++j)
+            yt[j] = 0.0;
+        for (int32_t i = 0; i < counts[c]; ++i) {
+            int64_t e = lists[c * E + i];
+            add_expert_output(x + t * d_h, w1 + e * d_e * d_h, w2 + e * d_h * d_e,
+                              (double)scores[t * E + e], d_h, d_e, h, yt);
+        }
+    }
+}
+
+/*
+ * Per-token brute force: the same sum restricted to the experts active for the
+ * token itself (scores[t,e] != 0), ascending. By the definition of the layer this is
+ * the result the union-then-mask form must reproduce.
+ */
+void oracle_token_ffn(const float *x, const float *scores, const float *w1,
+                      const float *w2, int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                      double *y, double *h_scratch)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+#ifdef _OPENMP
+        double *h = h_scratch + (int64_t)omp_get_thread_num() * d_e;
+#else
+        double *h = h_scratch;
+#endif
+        double *yt = y + t * d_h;
+        for (int64_t j = 0; j < d_h; ++j)
+            yt[j] = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            float s = scores[t * E + e];
+            if (s != 0.0f)
+                add_expert_output(x + t * d_h, w1 + e * d_e * d_h, w2 + e * d_h * d_e,
+                                  (double)s, d_h, d_e, h, yt);
+        }
+    }
+}

@@ -1,0 +1,100 @@
+"""Checks of the seeded input generators and of the sparsity meter."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from chunk_level_activation_amd import inputs
+
+
+def test_bf16_rounding_matches_torch():
+    rng = np.random.default_rng(0)
+    a = rng.standard_normal(1 << 16).astype(np.float32) * 10
+    edge = np.array([0.0, -0.0, 1.0, -1.0, 1.00390625, 1.0078125 * (1 + 2 ** -9),
+                     3.4e38, -3.4e38, 1e-40, np.inf, -np.inf], np.float32)
+    # exact ties between two bf16 values: round to even
+    ties = (np.arange(1, 200, dtype=np.uint32) << 16 | 0x8000).view(np.float32)
+    a = np.concatenate([a, edge, ties])
+    mine = inputs.f32_to_bf16_bits(a)
+    ref = torch.from_numpy(a).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(mine, ref)
+    back = inputs.bf16_bits_to_f32(mine)
+    assert np.array_equal(back, torch.from_numpy(a).to(torch.bfloat16).float().numpy())
+
+
+@pytest.mark.parametrize("tls,cls,q_ref,p_ref,u32_ref", [
+    (0.8, 0.7, 0.018895, 0.075580, 0.5571),
+    (0.5, 0.3, 0.070376, 0.070376, 0.9479),
+    (0.9, 0.85, 0.008132, 0.073190, 0.3013),
+])
+def test_markov_closed_form(tls, cls, q_ref, p_ref, u32_ref):
+    q, p = inputs.markov_params(tls, cls, 8)
+    assert abs(q - q_ref) < 5e-6 and abs(p - p_ref) < 5e-6
+    # stationary law and chunk law restated from the chain itself
+    assert abs(p / (p + q) - tls) < 1e-12
+    assert abs(tls * (1 - q) ** 7 - cls) < 1e-12
+    assert abs(inputs.expected_union_fraction(tls, cls, 8, 32) - u32_ref) < 5e-5
+
+
+def test_markov_infeasible_rejected():
+    with pytest.raises(ValueError):
+        inputs.markov_params(0.5, 0.7, 8)
+
+
+@pytest.mark.parametrize("tls,cls", [(0.8, 0.7), (0.5, 0.3), (0.9, 0.85)])
+def test_markov_masks_hit_targets(tls, cls):
+    """Generated masks (64 experts x 2^17 tokens) hit TLS and 8-token CLS."""
+    rng = np.random.default_rng(123)
+    act = inputs.markov_active(rng, 1 << 17, 64, tls, cls, 8)
+    assert abs(oracle.tls(act) - tls) < 0.005
+    assert abs(oracle.cls(act, 8) - cls) < 0.005
+    u32 = oracle.union_fraction(act, 32).mean()
+    assert abs(u32 - inputs.expected_union_fraction(tls, cls, 8, 32)) < 0.005
+
+
+def test_meter_closed_forms():
+    act = np.zeros((16, 4), bool)
+    assert oracle.tls(act) == 1.0 and oracle.cls(act, 8) == 1.0
+    act[:, 0] = True                                  # one expert always on
+    assert oracle.tls(act) == 0.75 and oracle.cls(act, 8) == 0.75
+    act = np.zeros((16, 4), bool)
+    act[np.arange(16), np.arange(16) % 4] = True      # round robin: 1 per token
+    assert oracle.tls(act) == 0.75
+    assert oracle.cls(act, 8) == 0.0                  # every chunk touches all 4
+    assert oracle.cls(act, 2) == 0.5
+    # partial last chunk counts as a chunk
+    assert np.allclose(oracle.union_fraction(act[:10], 8), [1.0, 0.5])
+
+
+def test_meter_union_matches_oracle_union():
+    rng = np.random.default_rng(5)
+    act = inputs.markov_active(rng, 200, 64, 0.8, 0.7, 8)
+    s = inputs.scores_for_mask(rng, act)
+    _, _, counts = oracle.chunk_union(s, 32)
+    assert np.allclose(oracle.union_fraction(act, 32), counts / 64)
+
+
+def test_scores_are_zero_exactly_where_inactive():
+    rng = np.random.default_rng(1)
+    act = rng.random((50, 20)) < 0.3
+    s = inputs.scores_for_mask(rng, act)
+    assert s.dtype == np.float32
+    assert np.array_equal(s != 0, act)
+    assert s[act].min() >= np.float32(0.1)
+
+
+def test_workloads_shapes_and_seeding():
+    a = inputs.make_workload("decode", seed=3)
+    b = inputs.make_workload("decode", seed=3)
+    assert np.array_equal(a.x, b.x) and np.array_equal(a.scores, b.scores)
+    assert a.x.shape == (32, 2048) and a.w1.shape == (64, 128, 2048)
+    assert a.w2.shape == (64, 2048, 128) and a.scores.shape == (32, 64)
+    assert np.array_equal(inputs.round_bf16(a.w1[:2]), a.w1[:2])   # bf16-exact values
+    t = inputs.make_workload("tiny", seed=0)
+    assert t.dtype == "f32" and t.scores is None and t.w_r.shape == (16, 256)
+
+
+def test_e2e_router_shift_gives_80_percent_zeros():
+    inp = inputs.make_workload("e2e", seed=0, T=1024)
+    l, _ = oracle.router(inp.x, inp.w_r, bias=inp.bias)
+    assert abs((l <= 0).mean() - 0.8) < 0.01
