@@ -1,0 +1,168 @@
+"""MI355X (gfx950) BlockFFN layer forward: Python binding of libblockffn.so.
+
+The functions here carry the names of the C ABI in include/blockffn.h and only
+marshal arguments: they check tensor placement/dtype/contiguity, allocate outputs
+with torch when the caller gives none, and pass raw device pointers and torch's
+current HIP stream. Every step of the layer runs in the library's HIP kernels; there
+is no fallback. If the library is missing the calls raise.
+
+Layer (BlockFFN, arXiv 2507.08771; skill page "BlockFFN: Sparse Mixture-of-Experts
+Optimized for End-Device Deployment", "Core Concept" and "Architecture Overview"):
+    scores = RMSNorm_E(ReLU(x W_r^T)) * g
+    y_t    = sum_{e in U_c(t)} scores[t,e] * W2_e swish(W1_e x_t)
+with U_c the union of experts active in the n-token chunk c holding t.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "BLOCKFFN_F32", "BLOCKFFN_BF16", "BlockFFNError", "FP32_EPS", "library_path",
+    "blockffn_router", "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
+    "blockffn_last_error", "blockffn_version", "load_library",
+]
+
+BLOCKFFN_F32 = 0
+BLOCKFFN_BF16 = 1
+# torch.nn.RMSNorm's default eps for fp32 (torch.finfo(torch.float32).eps).
+FP32_EPS = 1.1920928955078125e-07
+
+STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libblockffn.so")
+_lib = None
+
+
+class BlockFFNError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"blockffn status {STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load_library():
+    """Load libblockffn.so (built in-tree by build_lib.py); raise if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(library_path):
+        raise ImportError(
+            f"{library_path} is missing: build it with "
+            "`python -m chunk_level_activation_amd.build_lib` (or __graft_entry__.build())")
+    lib = ctypes.CDLL(library_path)
+    P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+    lib.blockffn_router.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P]
+    lib.blockffn_router.restype = I
+    lib.blockffn_chunk_ffn_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.blockffn_chunk_ffn_workspace_bytes.restype = ctypes.c_size_t
+    lib.blockffn_chunk_ffn.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, P,
+                                       ctypes.c_size_t, P, P, P, P]
+    lib.blockffn_chunk_ffn.restype = I
+    lib.blockffn_last_error.argtypes = []
+    lib.blockffn_last_error.restype = ctypes.c_char_p
+    lib.blockffn_version.argtypes = []
+    lib.blockffn_version.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def blockffn_last_error() -> str:
+    return load_library().blockffn_last_error().decode()
+
+
+def blockffn_version() -> str:
+    return load_library().blockffn_version().decode()
+
+
+def _check(status: int):
+    if status != 0:
+        raise BlockFFNError(status, blockffn_last_error())
+
+
+def _dtype_code(t) -> int:
+    import torch
+    if t.dtype == torch.float32:
+        return BLOCKFFN_F32
+    if t.dtype == torch.bfloat16:
+        return BLOCKFFN_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}: float32 or bfloat16")
+
+
+def _dev(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return s.cuda_stream
+
+
+def blockffn_router(x, w_r, gain=None, bias=None, eps: float = FP32_EPS, *, scores=None,
+                    logits=None, stream=None):
+    """scores [T, E] fp32 = RMSNorm_E(ReLU(x W_r^T + bias)) * gain. x [T, d_h] and
+    w_r [E, d_h] are both float32 or both bfloat16; gain/bias are [E] float32."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    E = w_r.shape[0]
+    if tuple(w_r.shape) != (E, d_h) or w_r.dtype != x.dtype:
+        raise ValueError("w_r must be [E, d_h] with the dtype of x")
+    if scores is None:
+        scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
+            _dev(bias, "bias", torch.float32), float(eps), T, d_h, E, _dtype_code(x),
+            _dev(scores, "scores", torch.float32), _dev(logits, "logits", torch.float32),
+            _stream(stream)]
+    _check(lib.blockffn_router(*args))
+    return scores
+
+
+def blockffn_chunk_ffn_workspace_bytes(T: int, d_h: int, E: int, d_e: int, n: int,
+                                       dtype: int) -> int:
+    nbytes = load_library().blockffn_chunk_ffn_workspace_bytes(T, d_h, E, d_e, n, dtype)
+    if nbytes == 0:
+        raise BlockFFNError(1, blockffn_last_error())
+    return int(nbytes)
+
+
+def blockffn_chunk_ffn(x, scores, w1, w2, n: int, *, y=None, workspace=None,
+                       union_masks=None, expert_lists=None, union_counts=None,
+                       stream=None):
+    """y [T, d_h] = chunk-union expert FFN of x masked by scores (see blockffn.h).
+    x [T, d_h], w1 [E, d_e, d_h], w2 [E, d_h, d_e] share one dtype; scores [T, E] fp32.
+    Optional outputs: union_masks [C, ceil(E/64)] int64 (uint64 bits), expert_lists
+    [C, E] int32, union_counts [C] int32, C = ceil(T/n)."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    E, d_e, _ = w1.shape
+    if tuple(w1.shape) != (E, d_e, d_h) or tuple(w2.shape) != (E, d_h, d_e):
+        raise ValueError("w1 must be [E, d_e, d_h] and w2 [E, d_h, d_e]")
+    if tuple(scores.shape) != (T, E):
+        raise ValueError("scores must be [T, E]")
+    if w1.dtype != x.dtype or w2.dtype != x.dtype:
+        raise TypeError("x, w1 and w2 must share a dtype")
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    nbytes = blockffn_chunk_ffn_workspace_bytes(T, d_h, E, d_e, n, code)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+    args = [_dev(x, "x"), _dev(scores, "scores", torch.float32), _dev(w1, "w1"),
+            _dev(w2, "w2"), T, d_h, E, d_e, n, code, _dev(y, "y", x.dtype),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _dev(union_masks, "union_masks", torch.int64),
+            _dev(expert_lists, "expert_lists", torch.int32),
+            _dev(union_counts, "union_counts", torch.int32), _stream(stream)]
+    _check(lib.blockffn_chunk_ffn(*args))
+    return y

@@ -1,0 +1,176 @@
+// C ABI of the BlockFFN layer forward: argument validation, workspace layout and
+// kernel launches. The declarations and their contracts are in include/blockffn.h.
+//
+// Nothing here touches the device before every argument has been checked, so an
+// invalid call returns an error and enqueues nothing; this also lets the checks run
+// on a machine without a GPU.
+#include <string>
+
+#include "../../include/blockffn.h"
+#include "plan.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+blockffn_status_t fail(blockffn_status_t code, const std::string &msg)
+{
+    g_last_error = msg;
+    return code;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+blockffn_status_t check_dtype(int dtype)
+{
+    if (dtype != BLOCKFFN_F32 && dtype != BLOCKFFN_BF16)
+        return fail(BLOCKFFN_EINVAL, "dtype must be BLOCKFFN_F32 (0) or BLOCKFFN_BF16 (1), got " +
+                                         std::to_string(dtype));
+    return BLOCKFFN_OK;
+}
+
+// Sizes shared by both calls.
+blockffn_status_t check_sizes(int64_t T, int64_t d_h, int64_t E, int dtype)
+{
+    if (T <= 0 || d_h <= 0 || E <= 0)
+        return fail(BLOCKFFN_EINVAL, "T, d_h and E must be positive (T=" + std::to_string(T) +
+                                         ", d_h=" + std::to_string(d_h) +
+                                         ", E=" + std::to_string(E) + ")");
+    if (E > 256)
+        return fail(BLOCKFFN_EUNSUPPORTED,
+                    "E=" + std::to_string(E) + " experts: at most 256 are supported");
+    if (T > (int64_t)1 << 30 || d_h > (int64_t)1 << 20)
+        return fail(BLOCKFFN_EUNSUPPORTED, "T or d_h too large");
+    if (dtype == BLOCKFFN_BF16 && d_h % 32 != 0)
+        return fail(BLOCKFFN_EUNSUPPORTED,
+                    "bf16 needs d_h % 32 == 0, got d_h=" + std::to_string(d_h));
+    return BLOCKFFN_OK;
+}
+
+blockffn_status_t check_ffn_sizes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                  int64_t n, int dtype)
+{
+    blockffn_status_t st = check_dtype(dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if ((st = check_sizes(T, d_h, E, dtype)) != BLOCKFFN_OK)
+        return st;
+    if (d_e <= 0 || n <= 0)
+        return fail(BLOCKFFN_EINVAL, "d_e and n must be positive (d_e=" + std::to_string(d_e) +
+                                         ", n=" + std::to_string(n) + ")");
+    if (d_e > 65536)
+        return fail(BLOCKFFN_EUNSUPPORTED, "d_e too large");
+    if (dtype == BLOCKFFN_BF16 && d_e % 16 != 0)
+        return fail(BLOCKFFN_EUNSUPPORTED,
+                    "bf16 needs d_e % 16 == 0, got d_e=" + std::to_string(d_e));
+    // Grid sizes of the widest launch must fit a 32-bit grid dimension.
+    const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
+    if (p.CT * p.E * (d_e / 16 + 1) >= ((int64_t)1 << 31) ||
+        p.CT * (p.JT + 8) * p.G >= ((int64_t)1 << 31))
+        return fail(BLOCKFFN_EUNSUPPORTED, "problem too large for one launch");
+    return BLOCKFFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *blockffn_last_error(void) { return g_last_error.c_str(); }
+
+const char *blockffn_version(void) { return "blockffn-gfx950 0.1.0"; }
+
+blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *gain,
+                                  const float *bias, float eps, int64_t T, int64_t d_h,
+                                  int64_t E, int dtype, float *scores, float *logits,
+                                  void *stream)
+{
+    blockffn_status_t st = check_dtype(dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if (!x || !w_r || !scores)
+        return fail(BLOCKFFN_EINVAL, "x, w_r and scores must not be NULL");
+    if ((st = check_sizes(T, d_h, E, dtype)) != BLOCKFFN_OK)
+        return st;
+    if (!(eps >= 0.0f))
+        return fail(BLOCKFFN_EINVAL, "eps must be >= 0");
+    const size_t ea = dtype == BLOCKFFN_BF16 ? 16 : 4;
+    if (!aligned(x, ea) || !aligned(w_r, ea))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x and w_r must be " + std::to_string(ea) +
+                                               "-byte aligned");
+    if (!aligned(scores, 4) || (logits && !aligned(logits, 4)) || (gain && !aligned(gain, 4)) ||
+        (bias && !aligned(bias, 4)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "float arrays must be 4-byte aligned");
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err;
+    if (dtype == BLOCKFFN_BF16)
+        err = blockffn::launch_router_bf16(static_cast<const uint16_t *>(x),
+                                           static_cast<const uint16_t *>(w_r), gain, bias, eps,
+                                           T, d_h, E, scores, logits, s);
+    else
+        err = blockffn::launch_router_f32(static_cast<const float *>(x),
+                                          static_cast<const float *>(w_r), gain, bias, eps, T,
+                                          d_h, E, scores, logits, s);
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("router launch failed: ") + hipGetErrorString(err));
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
+size_t blockffn_chunk_ffn_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                          int64_t n, int dtype)
+{
+    if (check_ffn_sizes(T, d_h, E, d_e, n, dtype) != BLOCKFFN_OK)
+        return 0;
+    return blockffn::make_plan(T, d_h, E, d_e, n, dtype).total_bytes;
+}
+
+blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const void *w1,
+                                     const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                     int64_t d_e, int64_t n, int dtype, void *y,
+                                     void *workspace, size_t workspace_bytes,
+                                     uint64_t *union_masks_out, int32_t *expert_lists_out,
+                                     int32_t *union_counts_out, void *stream)
+{
+    if (!x || !scores || !w1 || !w2 || !y || !workspace)
+        return fail(BLOCKFFN_EINVAL, "x, scores, w1, w2, y and workspace must not be NULL");
+    blockffn_status_t st = check_ffn_sizes(T, d_h, E, d_e, n, dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    const size_t ea = dtype == BLOCKFFN_BF16 ? 16 : 4;
+    if (!aligned(x, ea) || !aligned(w1, ea) || !aligned(w2, ea) || !aligned(y, ea))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x, w1, w2 and y must be " + std::to_string(ea) +
+                                               "-byte aligned");
+    if (!aligned(scores, 4) || !aligned(workspace, 256) ||
+        (union_masks_out && !aligned(union_masks_out, 8)) ||
+        (expert_lists_out && !aligned(expert_lists_out, 4)) ||
+        (union_counts_out && !aligned(union_counts_out, 4)))
+        return fail(BLOCKFFN_EUNSUPPORTED,
+                    "scores/lists/counts need 4-byte, masks 8-byte, workspace 256-byte alignment");
+    const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
+    if (workspace_bytes < p.total_bytes)
+        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                             " bytes, needs " + std::to_string(p.total_bytes));
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t err = blockffn::launch_union(p, scores, workspace, union_masks_out,
+                                            expert_lists_out, union_counts_out, s);
+    if (err == hipSuccess) {
+        if (dtype == BLOCKFFN_BF16)
+            err = blockffn::launch_ffn_bf16(p, static_cast<const uint16_t *>(x), scores,
+                                            static_cast<const uint16_t *>(w1),
+                                            static_cast<const uint16_t *>(w2),
+                                            static_cast<uint16_t *>(y), workspace, s);
+        else
+            err = blockffn::launch_ffn_f32(p, static_cast<const float *>(x), scores,
+                                           static_cast<const float *>(w1),
+                                           static_cast<const float *>(w2),
+                                           static_cast<float *>(y), workspace, s);
+    }
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("chunk FFN launch failed: ") + hipGetErrorString(err));
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
+}  // extern "C"

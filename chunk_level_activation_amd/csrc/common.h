@@ -1,0 +1,63 @@
+// Device-side helpers shared by the gfx950 kernels of the BlockFFN layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace blockffn {
+
+// Operand and accumulator vectors of the bf16 matrix-core (MFMA) instructions.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;     // CDNA wavefront width
+constexpr int kTileM = 32;    // token rows per tile: one n = 32 chunk
+
+// 16-byte load of eight bf16 values.
+__device__ __forceinline__ bf16x8 load_bf16x8(const uint16_t *p)
+{
+    u32x4 v = *reinterpret_cast<const u32x4 *>(p);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+// Same, but bypassing reuse in the caches: for weights that are streamed once.
+__device__ __forceinline__ bf16x8 load_bf16x8_stream(const uint16_t *p)
+{
+    u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ bf16x8 zero_bf16x8()
+{
+    return __builtin_bit_cast(bf16x8, u32x4{0u, 0u, 0u, 0u});
+}
+
+// fp32 -> bf16 bits, round to nearest, ties to even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t f32_to_bf16(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (uint16_t)((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b)
+{
+    return __uint_as_float((uint32_t)b << 16);
+}
+
+// Swish / SiLU with beta = 1: a * sigmoid(a) = a / (1 + e^-a).
+__device__ __forceinline__ float swish_fast(float a)
+{
+    return a / (1.0f + __expf(-a));
+}
+
+__device__ __forceinline__ float swish_precise(float a)
+{
+    return a / (1.0f + expf(-a));
+}
+
+}  // namespace blockffn

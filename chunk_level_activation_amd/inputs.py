@@ -1,6 +1,7 @@
 """Seeded synthetic inputs for the BlockFFN layer forward.
 
-This module is shared by the tests, the benchmark and the oracle's callers. It holds
+This module is shared by the tests and the benchmark; it is the only code the test
+reference and the GPU path have in common. It holds
 none of the layer's arithmetic. It only draws numbers:
 
 * Gaussian activations and weights (``np.random.default_rng(seed)``), rounded to bf16

@@ -1,0 +1,129 @@
+/*
+ * blockffn.h: C ABI of the MI355X (gfx950) BlockFFN layer forward.
+ *
+ * The layer (BlockFFN, arXiv 2507.08771; skill page "BlockFFN: Sparse
+ * Mixture-of-Experts Optimized for End-Device Deployment", sections "Core Concept"
+ * and "Architecture Overview"; paper-card Abstract) has two parts:
+ *
+ *   router      s[t,:] = RMSNorm_E( ReLU( W_r x_t ) ) * g          (no router bias)
+ *   chunk FFN   y_t = sum over e in U_c(t) of s[t,e] * W2_e swish(W1_e x_t)
+ *
+ * where U_c is the union of the experts active (s != 0) in any token of the
+ * n-token chunk c that holds t. Experts of the union that are inactive for a token
+ * are computed and then masked by that token's zero score; experts outside the
+ * union are never read.
+ *
+ * Conventions shared by every call:
+ *  - All array pointers are DEVICE pointers (hipMalloc / torch CUDA memory) owned by
+ *    the caller. The library allocates, frees and retains nothing.
+ *  - Arrays are dense, row-major, C-contiguous. Weights use the nn.Linear layout
+ *    [out_features, in_features], stacked over experts.
+ *  - `dtype` selects the element type of x, W_r, W1, W2 and y: BLOCKFFN_F32 (float)
+ *    or BLOCKFFN_BF16 (bfloat16 bits, products accumulated in fp32). Scores, gain,
+ *    bias and logits are always float.
+ *  - `stream` is a hipStream_t (NULL = the default stream). Calls enqueue their
+ *    kernels and return; BLOCKFFN_OK means "validated and enqueued". Faults inside a
+ *    kernel surface at the caller's next synchronisation.
+ *  - Every argument is validated on the host before anything is enqueued; an
+ *    invalid call writes nothing and returns a non-zero status, and
+ *    blockffn_last_error() returns a message for the calling thread.
+ *  - Supported sizes: 1 <= E <= 256; T, d_h, d_e, n >= 1. bf16 additionally needs
+ *    d_h % 32 == 0, d_e % 16 == 0 and 16-byte aligned x, W_r, W1, W2, y; every
+ *    pointer needs the alignment of its element type; the workspace 256 bytes.
+ */
+#ifndef BLOCKFFN_H
+#define BLOCKFFN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    BLOCKFFN_OK = 0,
+    BLOCKFFN_EINVAL = 1,        /* NULL required pointer, size <= 0, unknown dtype   */
+    BLOCKFFN_EUNSUPPORTED = 2,  /* valid but outside the supported sizes/alignment   */
+    BLOCKFFN_EWORKSPACE = 3,    /* workspace smaller than the query call returned    */
+    BLOCKFFN_EHIP = 4           /* the HIP runtime reported an error at launch       */
+} blockffn_status_t;
+
+typedef enum { BLOCKFFN_F32 = 0, BLOCKFFN_BF16 = 1 } blockffn_dtype_t;
+
+/*
+ * Router (skill page, "Architecture Overview" and "Router Architecture Setup";
+ * paper-card Abstract: a router integrating ReLU and RMSNorm):
+ *   l[t,e] = sum_j x[t,j] W_r[e,j] (+ bias[e])
+ *   s[t,e] = max(l[t,e], 0) / sqrt(mean_e max(l[t,e],0)^2 + eps) * gain[e]
+ * The pages' router has no bias; `bias` is an optional per-expert logit shift for
+ * callers that need one (NULL = none).
+ *
+ *   x       [T, d_h]  dtype         tokens
+ *   w_r     [E, d_h]  dtype         router weight (nn.Linear(d_h, E) layout)
+ *   gain    [E] float or NULL (=1)  RMSNorm weight
+ *   bias    [E] float or NULL (=0)
+ *   eps     RMSNorm epsilon (torch's default for fp32 is 1.1920929e-07)
+ *   scores  [T, E] float, written   post-RMSNorm scores (exactly 0 when inactive)
+ *   logits  [T, E] float or NULL    pre-ReLU logits, written when given
+ * ReLU maps every logit that is not > 0 (NaN included) to 0. A row with no positive
+ * logit gets all-zero scores.
+ */
+blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *gain,
+                                  const float *bias, float eps, int64_t T, int64_t d_h,
+                                  int64_t E, int dtype, float *scores, float *logits,
+                                  void *stream);
+
+/*
+ * Bytes of device workspace blockffn_chunk_ffn needs for these sizes (0 when the
+ * sizes are invalid; see blockffn_last_error()).
+ */
+size_t blockffn_chunk_ffn_workspace_bytes(int64_t T, int64_t d_h, int64_t E,
+                                          int64_t d_e, int64_t n, int dtype);
+
+/*
+ * Chunked expert FFN (skill page, "Core Concept": compute only the union of experts
+ * activated across n tokens and mask unneeded activations after the computation;
+ * "Architecture Overview": non-gated Swish experts, n = 32 tokens in the pages'
+ * kernel). Chunk c holds tokens [c*n, min(c*n + n, T)); the last chunk may be
+ * partial (skill page, "Chunk Sparsification Loss": ceil(T/n) aligned chunks).
+ *
+ *   x        [T, d_h]       dtype   tokens
+ *   scores   [T, E]         float   router scores; expert e is active for token t
+ *                                   exactly when scores[t,e] != 0 (-0 is inactive)
+ *   w1       [E, d_e, d_h]  dtype   fc1 weights (nn.Linear(d_h, d_e) per expert)
+ *   w2       [E, d_h, d_e]  dtype   fc2 weights (nn.Linear(d_e, d_h) per expert)
+ *   n        chunk length in tokens (n >= T means one chunk)
+ *   y        [T, d_h]       dtype   OVERWRITTEN with
+ *                   y[t,:] = sum_{e in U_c(t)} s[t,e] * W2_e swish(W1_e x[t,:])
+ *                   (swish(a) = a / (1 + exp(-a))). bf16: fp32 accumulation, the
+ *                   score-scaled hidden activations are rounded to bf16 before the
+ *                   second product and y is rounded to bf16 (nearest even).
+ *   workspace, workspace_bytes: device scratch of at least
+ *                   blockffn_chunk_ffn_workspace_bytes(...) bytes; its contents need
+ *                   no initialisation and are unspecified afterwards. Calls that may
+ *                   run concurrently need separate workspaces.
+ *   union_masks_out   [C][ceil(E/64)] uint64 or NULL: bit e%64 of word e/64 set when
+ *                   e is in U_c (C = ceil(T/n))
+ *   expert_lists_out  [C][E] int32 or NULL: U_c in ascending expert id, then -1
+ *   union_counts_out  [C] int32 or NULL: |U_c|
+ * The optional outputs receive exactly the unions the FFN kernels used.
+ */
+blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const void *w1,
+                                     const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                     int64_t d_e, int64_t n, int dtype, void *y,
+                                     void *workspace, size_t workspace_bytes,
+                                     uint64_t *union_masks_out, int32_t *expert_lists_out,
+                                     int32_t *union_counts_out, void *stream);
+
+/* Message describing the calling thread's last non-OK status ("" if none). */
+const char *blockffn_last_error(void);
+
+/* Library version string. */
+const char *blockffn_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BLOCKFFN_H */

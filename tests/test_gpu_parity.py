@@ -1,0 +1,332 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Bars: union masks, expert lists and counts bit-exact; y within
+max|dy| / max|y_ref| <= 1e-2 for bf16 inputs and <= 1e-5 for fp32; router masks
+equal wherever the oracle's pre-ReLU logit has |l| >= 1e-3.
+"""
+import numpy as np
+import pytest
+import torch
+
+import chunk_level_activation_amd as bf
+import oracle
+from chunk_level_activation_amd import inputs
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, dev, host, rel_err, sample_rows, tol, wdtype
+
+pytestmark = pytest.mark.gpu
+
+
+def run_ffn(inp, scores=None, workspace=None, n=None):
+    """GPU chunk FFN for a workload; returns (y, masks, lists, counts) on the host."""
+    n = inp.n if n is None else n
+    s = inp.scores if scores is None else scores
+    T, E = s.shape
+    C = -(-T // n)
+    masks = torch.empty((C, -(-E // 64)), dtype=torch.int64, device=DEV)
+    lists = torch.empty((C, E), dtype=torch.int32, device=DEV)
+    counts = torch.empty((C,), dtype=torch.int32, device=DEV)
+    dt = wdtype(inp)
+    y = bf.blockffn_chunk_ffn(dev(inp.x, dt), dev(s), dev(inp.w1, dt), dev(inp.w2, dt), n,
+                              workspace=workspace, union_masks=masks, expert_lists=lists,
+                              union_counts=counts)
+    torch.cuda.synchronize()
+    return (host(y), masks.cpu().numpy().view(np.uint64), lists.cpu().numpy(),
+            counts.cpu().numpy())
+
+
+def check_union(scores, n, masks, lists, counts):
+    m_ref, l_ref, c_ref = oracle.chunk_union(scores, n)
+    assert np.array_equal(counts, c_ref)
+    assert np.array_equal(masks, m_ref)
+    assert np.array_equal(lists, l_ref)
+
+
+# ------------------------------------------------------------------ union
+
+@pytest.mark.parametrize("T,E,n,kind", [
+    (32, 64, 32, "markov"), (2048, 64, 32, "markov"), (512, 128, 32, "markov"),
+    (70, 80, 8, "markov"), (1, 16, 32, "markov"), (100, 256, 32, "markov"),
+    (33, 64, 32, "hand"), (96, 200, 32, "hand"), (64, 1, 8, "markov"),
+])
+def test_union_bit_exact(T, E, n, kind):
+    rng = np.random.default_rng(T + E)
+    if kind == "markov":
+        act = inputs.markov_active(rng, T, E, 0.8, 0.7, 8)
+    else:
+        act = rng.random((T, E)) < 0.02
+        act[:min(n, T)] = False                      # empty first chunk
+        if T > 2 * n:
+            act[n:2 * n] = True                      # full second chunk
+    s = inputs.scores_for_mask(rng, act)
+    s[act == 0] = np.where(rng.random(int((~act).sum())) < 0.5, 0.0, -0.0)
+    x = inputs.gaussian(rng, (T, 32), 1.0, True)
+    w1, w2 = inputs.expert_weights(rng, E, 16, 32, True)
+    inp = inputs.LayerInputs("union", "bf16", T, 32, E, 16, n, x, w1, w2, scores=s)
+    _, masks, lists, counts = run_ffn(inp)
+    check_union(s, n, masks, lists, counts)
+
+
+# ------------------------------------------------------------------ chunk FFN, bf16
+
+@pytest.fixture(scope="module")
+def decode_draws():
+    return [inputs.make_workload("decode", seed=s) for s in range(3)]
+
+
+@pytest.mark.parametrize("i", range(3))
+def test_decode_chunk_full(decode_draws, i):
+    """d_h=2048, E=64, d_e=128, one 32-token chunk, Markov 80% TLS / 70% CLS_8."""
+    inp = decode_draws[i]
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, inp.n, masks, lists, counts)
+    y_ref = oracle.chunk_ffn(inp.x, inp.scores, inp.w1, inp.w2, inp.n)
+    assert rel_err(y, y_ref) <= TOL_BF16
+    assert 16 < counts[0] < 60     # a sparse but non-trivial union
+
+
+def test_prefill_sampled():
+    """T=2048 = 64 chunks: unions in full, y on sampled rows."""
+    inp = inputs.make_workload("prefill", seed=5)
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, inp.n, masks, lists, counts)
+    rows = sample_rows(inp.T, inp.n, 96)
+    y_ref = oracle.token_ffn(inp.x[rows], inp.scores[rows], inp.w1, inp.w2)
+    assert rel_err(y[rows], y_ref) <= TOL_BF16
+
+
+@pytest.mark.parametrize("tls,cls,dense", [(0.5, 0.3, False), (0.8, 0.7, False),
+                                           (0.9, 0.85, False), (0.8, 0.7, True)])
+def test_large_layer_sweep_sampled(tls, cls, dense):
+    """d_h=4096, E=128 (two mask words), T=512: the sparsity sweep and all-active."""
+    inp = inputs.make_workload("large", seed=7, tls=tls, cls=cls, dense=dense)
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, inp.n, masks, lists, counts)
+    if dense:
+        assert np.all(counts == 128)
+    rows = sample_rows(inp.T, inp.n, 16 if dense else 64)
+    y_ref = oracle.token_ffn(inp.x[rows], inp.scores[rows], inp.w1, inp.w2)
+    assert rel_err(y[rows], y_ref) <= TOL_BF16
+
+
+# ------------------------------------------------------------------ edge cases
+
+def small(dtype, T, n, E=16, d_h=64, d_e=32, tls=0.8, cls=0.6, seed=0):
+    return inputs.make_workload("decode", seed=seed, T=T, n=n, E=E, d_h=d_h, d_e=d_e,
+                                dtype=dtype, tls=tls, cls=cls)
+
+
+EDGE = [
+    # (label, T, n, E, d_h, d_e)
+    ("one token", 1, 32, 16, 64, 32),
+    ("ragged tail of one token", 33, 32, 16, 64, 32),
+    ("n=1", 40, 1, 16, 64, 32),
+    ("n=48 spans two tiles", 100, 48, 16, 64, 32),
+    ("n larger than T", 40, 64, 16, 64, 32),
+    ("n=8", 64, 8, 16, 256, 64),
+    ("one expert", 64, 32, 1, 64, 32),
+    ("E=80 partial mask word", 96, 32, 80, 64, 32),
+    ("E=256 four mask words", 64, 32, 256, 64, 16),
+    ("minimum bf16 sizes", 32, 32, 4, 32, 16),
+    ("many chunks", 1000, 32, 16, 64, 32),
+]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("label,T,n,E,d_h,d_e", EDGE, ids=[e[0] for e in EDGE])
+def test_edge_cases(dtype, label, T, n, E, d_h, d_e):
+    inp = small(dtype, T, n, E=E, d_h=d_h, d_e=d_e, tls=0.8, cls=0.6)
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, n, masks, lists, counts)
+    y_ref = oracle.chunk_ffn(inp.x, inp.scores, inp.w1, inp.w2, n)
+    assert rel_err(y, y_ref) <= tol(inp), label
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_all_zero_scores_give_zero(dtype):
+    inp = small(dtype, 70, 32)
+    s = np.zeros_like(inp.scores)
+    s[5, 3] = -0.0
+    y, masks, lists, counts = run_ffn(inp, scores=s)
+    assert np.all(counts == 0) and np.all(masks == 0) and np.all(lists == -1)
+    assert np.all(y == 0)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_single_active_entry(dtype):
+    inp = small(dtype, 64, 32)
+    s = np.zeros_like(inp.scores)
+    s[40, 7] = 1.25
+    y, _, lists, counts = run_ffn(inp, scores=s)
+    assert counts.tolist() == [0, 1] and lists[1, 0] == 7
+    assert np.all(y[np.arange(64) != 40] == 0)
+    y_ref = oracle.chunk_ffn(inp.x, s, inp.w1, inp.w2, 32)
+    assert rel_err(y, y_ref) <= tol(inp)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_experts_outside_union_are_never_read(dtype):
+    """NaN weights on experts outside every union leave y finite and unchanged."""
+    inp = small(dtype, 64, 32, E=32, tls=0.9, cls=0.85, seed=3)
+    m_ref, _, _ = oracle.chunk_union(inp.scores, 32)
+    used = np.zeros(32, bool)
+    for c in range(m_ref.shape[0]):
+        used |= [(int(m_ref[c, 0]) >> e) & 1 == 1 for e in range(32)]
+    assert not used.all()
+    y, *_ = run_ffn(inp)
+    inp.w1 = inp.w1.copy()
+    inp.w2 = inp.w2.copy()
+    inp.w1[~used] = np.nan
+    inp.w2[~used] = np.nan
+    yn, *_ = run_ffn(inp)
+    assert np.all(np.isfinite(yn))
+    assert np.array_equal(y, yn)
+
+
+def test_deterministic_and_workspace_needs_no_init():
+    """Two calls agree bitwise (the split-sum path included), and a workspace full of
+    garbage, or left over from a call of another shape, gives the same result."""
+    inp = inputs.make_workload("decode", seed=11)
+    nbytes = bf.blockffn_chunk_ffn_workspace_bytes(2048, 2048, 64, 128, 32, bf.BLOCKFFN_BF16)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    y1, *_ = run_ffn(inp, workspace=ws)
+    y2, *_ = run_ffn(inp, workspace=ws)
+    assert np.array_equal(y1, y2)
+    big = inputs.make_workload("prefill", seed=12, T=256)
+    run_ffn(big, workspace=ws)
+    y3, *_ = run_ffn(inp, workspace=ws)
+    assert np.array_equal(y1, y3)
+
+
+def test_score_scaling_by_two_is_exact():
+    """y(2s) == 2 y(s) bitwise: powers of two commute with every rounding step."""
+    inp = inputs.make_workload("decode", seed=13)
+    y1, *_ = run_ffn(inp)
+    y2, *_ = run_ffn(inp, scores=inp.scores * np.float32(2.0))
+    assert np.array_equal(y2, 2 * y1)
+
+
+def test_chunk_length_changes_only_unions():
+    """y does not depend on n beyond rounding; the unions do."""
+    inp = inputs.make_workload("prefill", seed=14, T=256)
+    y32, *_ = run_ffn(inp, n=32)
+    y8, m8, l8, c8 = run_ffn(inp, n=8)
+    check_union(inp.scores, 8, m8, l8, c8)
+    assert rel_err(y8, y32) <= TOL_BF16
+
+
+def test_small_workspace_rejected():
+    inp = small("bf16", 64, 32)
+    ws = torch.empty(64, dtype=torch.uint8, device=DEV)
+    with pytest.raises(bf.BlockFFNError) as ei:
+        run_ffn(inp, workspace=ws)
+    assert ei.value.status == 3
+
+
+# ------------------------------------------------------------------ router
+
+def run_router(inp, use_gain=True, use_bias=True, logits=True):
+    dt = wdtype(inp)
+    T, E = inp.T, inp.w_r.shape[0]
+    lg = torch.empty((T, E), dtype=torch.float32, device=DEV) if logits else None
+    s = bf.blockffn_router(dev(inp.x, dt), dev(inp.w_r, dt),
+                           dev(inp.gain) if (use_gain and inp.gain is not None) else None,
+                           dev(inp.bias) if (use_bias and inp.bias is not None) else None,
+                           logits=lg)
+    torch.cuda.synchronize()
+    return s.cpu().numpy(), (lg.cpu().numpy() if logits else None)
+
+
+def check_router(inp, s, lg, use_gain=True, use_bias=True, score_tol=1e-4):
+    gain = inp.gain if use_gain else None
+    bias = inp.bias if use_bias else None
+    l_ref, s_ref = oracle.router(inp.x, inp.w_r, gain=gain, bias=bias)
+    # forward error bound of an fp32 sum of d_h products (bf16 x bf16 products are
+    # exact in fp32; fp32 products add one rounding each): (d_h + 2) u sum|x_j w_j|
+    u = 2.0 ** -24
+    absdot = np.abs(inp.x.astype(np.float64)) @ np.abs(inp.w_r.astype(np.float64)).T
+    if bias is not None:
+        absdot += np.abs(bias)
+    bound = (inp.d_h + 2) * u * absdot
+    if lg is not None:
+        assert np.all(np.abs(lg - l_ref) <= bound)
+    decided = np.abs(l_ref) >= 1e-3
+    assert np.array_equal((s != 0)[decided], (l_ref > 0)[decided])
+    assert rel_err(s, s_ref) <= score_tol
+
+
+def test_router_e2e_full():
+    """T=4096, d_h=2048, E=64, bf16, logit shift for ~80% zeros after ReLU."""
+    inp = inputs.make_workload("e2e", seed=0)
+    s, lg = run_router(inp)
+    check_router(inp, s, lg)
+    assert abs((s == 0).mean() - 0.8) < 0.02
+
+
+def test_router_tiny_f32():
+    inp = inputs.make_workload("tiny", seed=0)
+    s, lg = run_router(inp)
+    check_router(inp, s, lg, score_tol=TOL_F32)
+
+
+ROUTER_EDGE = [
+    # (label, dtype, T, d_h, E, gain, bias)
+    ("one expert", "bf16", 64, 256, 1, True, False),
+    ("E=40", "bf16", 96, 512, 40, True, True),
+    ("E=256", "bf16", 64, 256, 256, True, True),
+    ("ragged T", "bf16", 33, 256, 64, False, False),
+    ("one token", "bf16", 1, 256, 16, True, False),
+    ("f32 E=40", "f32", 50, 100, 40, True, True),
+    ("f32 E=256", "f32", 20, 64, 256, False, True),
+]
+
+
+@pytest.mark.parametrize("label,dtype,T,d_h,E,g,b", ROUTER_EDGE, ids=[r[0] for r in ROUTER_EDGE])
+def test_router_edge_cases(label, dtype, T, d_h, E, g, b):
+    rng = np.random.default_rng(T * 7 + E)
+    bfl = dtype == "bf16"
+    x = inputs.gaussian(rng, (T, d_h), 1.0, bfl)
+    w_r = inputs.gaussian(rng, (E, d_h), 1.0 / np.sqrt(d_h), bfl)
+    inp = inputs.LayerInputs("router", dtype, T, d_h, E, 16, 32, x, None, None, w_r=w_r)
+    inp.gain = (rng.random(E) + 0.5).astype(np.float32) if g else None
+    inp.bias = inputs.router_shift(w_r, 0.6) if b else None
+    s, lg = run_router(inp, use_gain=g, use_bias=b, logits=(T % 2 == 0))
+    check_router(inp, s, lg, use_gain=g, use_bias=b,
+                 score_tol=1e-4 if bfl else TOL_F32)
+
+
+def test_router_all_negative_row():
+    x = np.ones((4, 64), np.float32)
+    w_r = -np.ones((8, 64), np.float32) / 64
+    inp = inputs.LayerInputs("router", "bf16", 4, 64, 8, 16, 32, x, None, None, w_r=w_r)
+    s, _ = run_router(inp, use_gain=False, use_bias=False)
+    assert np.all(s == 0)
+
+
+# ------------------------------------------------------------------ end to end
+
+def test_end_to_end_router_then_ffn_sampled():
+    """Router on the GPU feeds the GPU chunk FFN; compared on sampled rows with the
+    oracle's router feeding the oracle's FFN."""
+    inp = inputs.make_workload("e2e", seed=1)
+    dt = torch.bfloat16
+    x = dev(inp.x, dt)
+    s = bf.blockffn_router(x, dev(inp.w_r, dt), dev(inp.gain), dev(inp.bias))
+    y = bf.blockffn_chunk_ffn(x, s, dev(inp.w1, dt), dev(inp.w2, dt), inp.n)
+    torch.cuda.synchronize()
+    _, s_ref = oracle.router(inp.x, inp.w_r, gain=inp.gain, bias=inp.bias)
+    rows = sample_rows(inp.T, inp.n, 64)
+    y_ref = oracle.token_ffn(inp.x[rows], s_ref[rows].astype(np.float32), inp.w1, inp.w2)
+    assert rel_err(host(y)[rows], y_ref) <= TOL_BF16
+
+
+def test_tiny_fp32_end_to_end():
+    """The tiny fp32 workload: router from x, ~50% active, n=8."""
+    inp = inputs.make_workload("tiny", seed=2)
+    x = dev(inp.x)
+    s = bf.blockffn_router(x, dev(inp.w_r), dev(inp.gain))
+    y = bf.blockffn_chunk_ffn(x, s, dev(inp.w1), dev(inp.w2), inp.n)
+    torch.cuda.synchronize()
+    _, s_ref = oracle.router(inp.x, inp.w_r, gain=inp.gain)
+    y_ref = oracle.chunk_ffn(inp.x, s_ref.astype(np.float32), inp.w1, inp.w2, inp.n)
+    assert rel_err(host(y), y_ref) <= TOL_F32
+    assert 0.3 < (host(s) == 0).mean() < 0.7
