@@ -20,6 +20,7 @@ import os
 __all__ = [
     "BLOCKFFN_F32", "BLOCKFFN_BF16", "BlockFFNError", "FP32_EPS", "library_path",
     "blockffn_router", "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
+    "blockffn_chunk_ffn_workspace",
     "blockffn_last_error", "blockffn_version", "load_library",
 ]
 
@@ -135,6 +136,15 @@ def blockffn_chunk_ffn_workspace_bytes(T: int, d_h: int, E: int, d_e: int, n: in
     return int(nbytes)
 
 
+def blockffn_chunk_ffn_workspace(T: int, d_h: int, E: int, d_e: int, n: int, dtype: int,
+                                 device="cuda"):
+    """A zero-filled workspace of the size the C ABI asks for (see blockffn.h): it
+    must start zeroed and is returned to that state by every call."""
+    import torch
+    nbytes = blockffn_chunk_ffn_workspace_bytes(T, d_h, E, d_e, n, dtype)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def blockffn_chunk_ffn(x, scores, w1, w2, n: int, *, y=None, workspace=None,
                        union_masks=None, expert_lists=None, union_counts=None,
                        stream=None):
@@ -157,7 +167,7 @@ def blockffn_chunk_ffn(x, scores, w1, w2, n: int, *, y=None, workspace=None,
         y = torch.empty_like(x)
     nbytes = blockffn_chunk_ffn_workspace_bytes(T, d_h, E, d_e, n, code)
     if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=x.device)
+        workspace = torch.zeros(nbytes, dtype=torch.uint8, device=x.device)
     args = [_dev(x, "x"), _dev(scores, "scores", torch.float32), _dev(w1, "w1"),
             _dev(w2, "w2"), T, d_h, E, d_e, n, code, _dev(y, "y", x.dtype),
             _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),

@@ -4,6 +4,7 @@
 // Nothing here touches the device before every argument has been checked, so an
 // invalid call returns an error and enqueues nothing; this also lets the checks run
 // on a machine without a GPU.
+#include <mutex>
 #include <string>
 
 #include "../../include/blockffn.h"
@@ -12,6 +13,52 @@
 namespace {
 
 thread_local std::string g_last_error;
+
+// Per-device facts the one-launch bf16 schedule depends on, found on first use.
+struct DeviceInfo {
+    bool probed = false;
+    int xcds = 0;          // XCDs, when round-robin workgroup placement was verified
+    int wg_per_xcd = 0;    // resident one-launch workgroups per XCD
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_device_mutex;
+DeviceInfo g_devices[kMaxDevices];
+
+// The one-launch schedule's grid on the current device: fills *xcds and *wg_per_xcd
+// and returns true when it may be used. The first call probes workgroup placement;
+// it is skipped (and retried later) while the stream is being captured into a
+// graph, because the probe synchronises.
+bool chunk1_grid(hipStream_t stream, int *xcds, int *wg_per_xcd)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+        return false;
+    std::lock_guard<std::mutex> lock(g_device_mutex);
+    DeviceInfo &d = g_devices[dev];
+    if (!d.probed) {
+        hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+        if (hipStreamIsCapturing(stream, &cs) != hipSuccess ||
+            cs != hipStreamCaptureStatusNone)
+            return false;
+        int nxcd = 0, cus = 0;
+        bool round_robin = false;
+        if (hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess &&
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
+                hipSuccess &&
+            nxcd > 1 && nxcd <= blockffn::kMaxGroups && cus % nxcd == 0 &&
+            blockffn::probe_xcd_placement(nxcd, &round_robin) == hipSuccess && round_robin) {
+            const int per_cu = blockffn::chunk1_blocks_per_cu();
+            if (per_cu >= 1) {
+                d.xcds = nxcd;
+                d.wg_per_xcd = (per_cu >= 2 ? 2 : 1) * (cus / nxcd);
+            }
+        }
+        d.probed = true;
+    }
+    *xcds = d.xcds;
+    *wg_per_xcd = d.wg_per_xcd;
+    return d.xcds > 0;
+}
 
 blockffn_status_t fail(blockffn_status_t code, const std::string &msg)
 {
@@ -65,8 +112,8 @@ blockffn_status_t check_ffn_sizes(int64_t T, int64_t d_h, int64_t E, int64_t d_e
                     "bf16 needs d_e % 16 == 0, got d_e=" + std::to_string(d_e));
     // Grid sizes of the widest launch must fit a 32-bit grid dimension.
     const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
-    if (p.CT * p.E * (d_e / 16 + 1) >= ((int64_t)1 << 31) ||
-        p.CT * (p.JT + 8) * p.G >= ((int64_t)1 << 31))
+    if (p.CT * p.E * (d_e / 16 + 1) * 2 >= ((int64_t)1 << 31) ||
+        p.CT * p.JT >= ((int64_t)1 << 31))
         return fail(BLOCKFFN_EUNSUPPORTED, "problem too large for one launch");
     return BLOCKFFN_OK;
 }
@@ -147,21 +194,32 @@ blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const v
         (union_counts_out && !aligned(union_counts_out, 4)))
         return fail(BLOCKFFN_EUNSUPPORTED,
                     "scores/lists/counts need 4-byte, masks 8-byte, workspace 256-byte alignment");
-    const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
-    if (workspace_bytes < p.total_bytes)
-        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                             " bytes, needs " + std::to_string(p.total_bytes));
-
     hipStream_t s = static_cast<hipStream_t>(stream);
-    hipError_t err = blockffn::launch_union(p, scores, workspace, union_masks_out,
-                                            expert_lists_out, union_counts_out, s);
-    if (err == hipSuccess) {
-        if (dtype == BLOCKFFN_BF16)
-            err = blockffn::launch_ffn_bf16(p, static_cast<const uint16_t *>(x), scores,
-                                            static_cast<const uint16_t *>(w1),
-                                            static_cast<const uint16_t *>(w2),
-                                            static_cast<uint16_t *>(y), workspace, s);
-        else
+    const size_t needed = blockffn::make_plan(T, d_h, E, d_e, n, dtype).total_bytes;
+    if (workspace_bytes < needed)
+        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                             " bytes, needs " + std::to_string(needed));
+    const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
+
+    hipError_t err;
+    int xcds = 0, wg_per_xcd = 0;
+    if (dtype == BLOCKFFN_BF16 && p.chunk1 && chunk1_grid(s, &xcds, &wg_per_xcd)) {
+        // one launch: union, up- and down-projection of a single chunk tile
+        err = blockffn::launch_ffn_bf16_chunk1(
+            p, xcds, wg_per_xcd, static_cast<const uint16_t *>(x), scores,
+            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w2),
+            static_cast<uint16_t *>(y), workspace, union_masks_out, expert_lists_out,
+            union_counts_out, s);
+    } else if (dtype == BLOCKFFN_BF16) {
+        err = blockffn::launch_ffn_bf16(p, static_cast<const uint16_t *>(x), scores,
+                                        static_cast<const uint16_t *>(w1),
+                                        static_cast<const uint16_t *>(w2),
+                                        static_cast<uint16_t *>(y), workspace, union_masks_out,
+                                        expert_lists_out, union_counts_out, s);
+    } else {
+        err = blockffn::launch_union(p, scores, workspace, union_masks_out, expert_lists_out,
+                                     union_counts_out, s);
+        if (err == hipSuccess)
             err = blockffn::launch_ffn_f32(p, static_cast<const float *>(x), scores,
                                            static_cast<const float *>(w1),
                                            static_cast<const float *>(w2),

@@ -7,6 +7,19 @@
 
 namespace blockffn {
 
+// The workspace starts with a control block of fixed size. The one-launch bf16
+// kernel keeps its arrival counters there; every call returns the counters it used
+// to zero, so the block is all-zero between calls whatever sizes the calls have, and
+// a workspace zero-filled once stays valid. Scratch data always lies after the block.
+constexpr size_t kControlBytes = 64 * 1024;
+constexpr int64_t kControlWords = kControlBytes / sizeof(uint32_t);
+constexpr int64_t kMaxGroups = 16;   // XCDs the one-launch kernel may spread groups over
+
+// One-launch bf16 schedule for a single chunk tile (defined in ffn_bf16_chunk.hip).
+bool chunk1_supported(int64_t CT, int64_t d_h, int64_t d_e);
+size_t chunk1_partial_bytes(int64_t d_h, int64_t E, int64_t d_e);
+int chunk1_blocks_per_cu();
+
 // Problem sizes plus everything derived from them that the kernels and the
 // workspace layout need. Built once per call by make_plan().
 struct FfnPlan {
@@ -16,9 +29,11 @@ struct FfnPlan {
     int64_t MPC;          // 32-token tiles per chunk, ceil(n / 32) (n capped at T)
     int64_t CT;           // chunk tiles, C * MPC
     int64_t W;            // 64-bit mask words per chunk, ceil(E / 64)
-    int64_t JT;           // 32-column tiles of d_h in the down-projection
-    int64_t G;            // expert groups the down-projection splits a union into
-    size_t off_ctrl, off_masks, off_lists, off_counts, off_hidden, off_partials;
+    int64_t JT;           // 32-column tiles of d_h in the two-launch down-projection
+    bool chunk1;          // sizes admit the one-launch single-tile bf16 schedule
+    // scratch after the control block (byte offsets)
+    size_t off_masks, off_lists, off_counts;   // fp32 path union
+    size_t off_hidden, off_partials;
     size_t total_bytes;
 };
 
@@ -35,23 +50,17 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     p.CT = p.C * p.MPC;
     p.W = (E + 63) / 64;
     p.JT = (d_h + 31) / 32;
-    // Split each union over G expert groups when there are too few (tile, column
-    // tile) pairs to give every compute unit work; partial sums are then combined
-    // in a fixed order by the last group to finish.
-    int64_t tiles = p.CT * p.JT;
-    p.G = 1;
-    while (p.G < 8 && tiles * p.G * 2 <= 256)
-        p.G *= 2;
+    p.chunk1 = dtype == 1 && chunk1_supported(p.CT, d_h, d_e) &&
+               E * (d_e / 64 + 1) + kMaxGroups + d_h / 64 <= kControlWords;
     const size_t helem = dtype == 1 ? 2 : 4;   // hidden activations: bf16 or fp32
-    size_t off = 0;
-    p.off_ctrl = off;     off = align_up(off + sizeof(uint32_t) * p.CT * p.JT, 256);
+    size_t off = kControlBytes;
     p.off_masks = off;    off = align_up(off + sizeof(uint64_t) * p.C * p.W, 256);
     p.off_lists = off;    off = align_up(off + sizeof(int32_t) * p.C * E, 256);
     p.off_counts = off;   off = align_up(off + sizeof(int32_t) * p.C, 256);
     p.off_hidden = off;   off = align_up(off + helem * p.CT * E * 32 * d_e, 256);
     p.off_partials = off;
-    if (p.G > 1)
-        off = align_up(off + sizeof(float) * p.CT * p.JT * p.G * 32 * 32, 256);
+    if (p.chunk1)
+        off = align_up(off + chunk1_partial_bytes(d_h, E, d_e), 256);
     p.total_bytes = off;
     return p;
 }
@@ -62,13 +71,23 @@ hipError_t launch_union(const FfnPlan &p, const float *scores, void *ws,
                         hipStream_t stream);
 hipError_t launch_ffn_bf16(const FfnPlan &p, const uint16_t *x, const float *scores,
                            const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *ws,
+                           uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,
                            hipStream_t stream);
+// One launch for a single chunk tile, `xcds` expert groups of `wg_per_xcd`
+// workgroups each (requires round-robin placement and that many resident workgroups).
+hipError_t launch_ffn_bf16_chunk1(const FfnPlan &p, int xcds, int wg_per_xcd,
+                                  const uint16_t *x, const float *scores, const uint16_t *w1,
+                                  const uint16_t *w2, uint16_t *y, void *ws,
+                                  uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,
+                                  hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnPlan &p, const float *x, const float *scores,
                           const float *w1, const float *w2, float *y, void *ws,
                           hipStream_t stream);
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const float *gain,
                               const float *bias, float eps, int64_t T, int64_t d_h,
                               int64_t E, float *scores, float *logits, hipStream_t stream);
+// Checks that workgroup b of a launch runs on XCD b % nxcd (round-robin dispatch).
+hipError_t probe_xcd_placement(int nxcd, bool *round_robin);
 hipError_t launch_router_f32(const float *x, const float *w_r, const float *gain,
                              const float *bias, float eps, int64_t T, int64_t d_h,
                              int64_t E, float *scores, float *logits, hipStream_t stream);

@@ -13,20 +13,25 @@
 
 namespace blockffn {
 
-// bf16: 32 tokens x all experts per workgroup, ET tiles of 32 experts. The 32x32x16
-// bf16 MFMA takes A = x rows (32 tokens x 16 k) and B = W_r rows transposed (16 k x
-// 32 experts); the four waves interleave over the k steps and are summed in wave
-// order through LDS.
+// bf16: 32 tokens x all experts per workgroup, ET tiles of 32 experts, 8 waves. The
+// 32x32x16 bf16 MFMA takes A = x rows (32 tokens x 16 k) and B = W_r rows
+// transposed (16 k x 32 experts). The waves take k steps round robin, each issuing
+// the loads of KB steps together; the wave sums are added in wave order in LDS.
+constexpr int kRouterThreads = 512;
+constexpr int kRouterWaves = kRouterThreads / kWave;
+
 template <int ET>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kRouterThreads)
 router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w_r,
                    const float *__restrict__ gain, const float *__restrict__ bias,
                    float eps, int64_t T, int d_h, int E, float *__restrict__ scores,
                    float *__restrict__ logits)
 {
+    constexpr int KB = ET >= 8 ? 2 : (ET >= 4 ? 4 : 8);
     const int64_t t0 = (int64_t)blockIdx.x * kTileM;
-    const int wave = threadIdx.x / kWave;
-    const int lane = threadIdx.x % kWave;
+    const int tid = threadIdx.x;
+    const int wave = tid / kWave;
+    const int lane = tid % kWave;
     const int row = lane % 32;
     const int kg = lane / 32;
     const bool vt = t0 + row < T;
@@ -44,18 +49,29 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
             acc[et][i] = 0.0f;
     }
     const int KS = d_h / 16;
-#pragma unroll 2
-    for (int ks = wave; ks < KS; ks += 4) {
-        const bf16x8 a = vt ? load_bf16x8(xr + ks * 16) : zero_bf16x8();
+    for (int kb = wave; kb < KS; kb += kRouterWaves * KB) {
+        bf16x8 av[KB], bv[KB][ET];
 #pragma unroll
-        for (int et = 0; et < ET; ++et) {
-            const bf16x8 b = ve[et] ? load_bf16x8(wr[et] + ks * 16) : zero_bf16x8();
-            acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[et], 0, 0, 0);
+        for (int i = 0; i < KB; ++i) {
+            const int ks = kb + i * kRouterWaves;
+            const bool ok = ks < KS;
+            av[i] = ok && vt ? load_bf16x8(xr + ks * 16) : zero_bf16x8();
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+                bv[i][et] = ok && ve[et] ? load_bf16x8(wr[et] + ks * 16) : zero_bf16x8();
         }
+#pragma unroll
+        for (int i = 0; i < KB; ++i)
+#pragma unroll
+            for (int et = 0; et < ET; ++et)
+                acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[i][et], acc[et], 0,
+                                                                  0, 0);
     }
 
+    // 32x32 accumulator layout: element i is row (i/4)*8 + (lane/32)*4 + i%4 (token)
+    // of column lane%32 (expert).
     __shared__ float lg[kTileM][ET * 32 + 1];
-    for (int w = 0; w < 4; ++w) {
+    for (int w = 0; w < kRouterWaves; ++w) {
         if (wave == w) {
 #pragma unroll
             for (int et = 0; et < ET; ++et)
@@ -68,11 +84,11 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
         __syncthreads();
     }
 
-    // Epilogue: 8 threads per token.
-    const int tt = threadIdx.x / 8, sub = threadIdx.x % 8;
+    // Epilogue: 16 threads per token.
+    const int tt = tid / 16, sub = tid % 16;
     const int64_t t = t0 + tt;
     float sumsq = 0.0f;
-    for (int e = sub; e < E; e += 8) {
+    for (int e = sub; e < E; e += 16) {
         const float l = bias ? lg[tt][e] + bias[e] : lg[tt][e];
         lg[tt][e] = l;
         const float r = l > 0.0f ? l : 0.0f;
@@ -81,9 +97,10 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     sumsq += __shfl_xor(sumsq, 1);
     sumsq += __shfl_xor(sumsq, 2);
     sumsq += __shfl_xor(sumsq, 4);
+    sumsq += __shfl_xor(sumsq, 8);
     const float inv = 1.0f / sqrtf(sumsq / (float)E + eps);
     if (t < T) {
-        for (int e = sub; e < E; e += 8) {
+        for (int e = sub; e < E; e += 16) {
             const float l = lg[tt][e];
             const float r = l > 0.0f ? l : 0.0f;
             scores[t * E + e] = r * inv * (gain ? gain[e] : 1.0f);
@@ -132,7 +149,7 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const floa
                               const float *bias, float eps, int64_t T, int64_t d_h,
                               int64_t E, float *scores, float *logits, hipStream_t stream)
 {
-    const dim3 grid((unsigned)((T + kTileM - 1) / kTileM)), block(256);
+    const dim3 grid((unsigned)((T + kTileM - 1) / kTileM)), block(kRouterThreads);
     const int ET = (int)((E + 31) / 32);
     if (ET <= 1)
         hipLaunchKernelGGL(router_bf16_kernel<1>, grid, block, 0, stream, x, w_r, gain, bias,

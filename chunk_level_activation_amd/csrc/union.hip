@@ -7,10 +7,12 @@
 // last one possibly partial ("Chunk Sparsification Loss").
 //
 // One wavefront per chunk, lane = expert within a 64-expert word: each lane ORs its
-// expert's activity over the chunk's tokens (a coalesced 256-byte row read per
-// token), a wave ballot turns the 64 flags into the mask word, and the position of
-// every member in the list is the popcount of the mask bits below its lane plus the
-// members of earlier words, so the list comes out in ascending expert id.
+// expert's activity over the chunk's tokens (a coalesced row read per token, 16
+// tokens in flight at a time), a wave ballot turns the 64 flags into the mask word,
+// and the position of every member in the list is the popcount of the mask bits
+// below its lane plus the members of earlier words, so the list comes out in
+// ascending expert id. (The bf16 kernels compute the same union inside each
+// workgroup instead; this kernel serves the fp32 path.)
 #include "common.h"
 #include "plan.h"
 
@@ -19,10 +21,10 @@ namespace blockffn {
 __global__ void __launch_bounds__(kWave)
 union_kernel(const float *__restrict__ scores, int64_t T, int E, int64_t n, int W,
              uint64_t *__restrict__ masks, int32_t *__restrict__ lists,
-             int32_t *__restrict__ counts, uint32_t *__restrict__ ctrl, int ctrl_per_chunk,
-             uint64_t *__restrict__ masks_out, int32_t *__restrict__ lists_out,
-             int32_t *__restrict__ counts_out)
+             int32_t *__restrict__ counts, uint64_t *__restrict__ masks_out,
+             int32_t *__restrict__ lists_out, int32_t *__restrict__ counts_out)
 {
+    constexpr int kBatch = 16;    // tokens whose score loads are in flight together
     const int64_t c = blockIdx.x;
     const int lane = threadIdx.x;
     const int64_t t0 = c * n;
@@ -31,9 +33,17 @@ union_kernel(const float *__restrict__ scores, int64_t T, int E, int64_t n, int 
     for (int w = 0; w < W; ++w) {
         const int e = w * kWave + lane;
         bool active = false;
-        if (e < E)
-            for (int64_t t = t0; t < t1; ++t)
-                active |= scores[t * E + e] != 0.0f;
+        if (e < E) {
+            for (int64_t tb = t0; tb < t1; tb += kBatch) {
+                float v[kBatch];
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    v[i] = tb + i < t1 ? scores[(tb + i) * E + e] : 0.0f;
+#pragma unroll
+                for (int i = 0; i < kBatch; ++i)
+                    active |= v[i] != 0.0f;
+            }
+        }
         const uint64_t word = __ballot(active);
         if (active) {
             const int pos = members + __popcll(word & ((1ull << lane) - 1ull));
@@ -58,9 +68,6 @@ union_kernel(const float *__restrict__ scores, int64_t T, int E, int64_t n, int 
         if (counts_out)
             counts_out[c] = members;
     }
-    // Arrival counters of this chunk's tiles for the down-projection's split sum.
-    for (int i = lane; i < ctrl_per_chunk; i += kWave)
-        ctrl[c * ctrl_per_chunk + i] = 0u;
 }
 
 hipError_t launch_union(const FfnPlan &p, const float *scores, void *ws,
@@ -72,9 +79,8 @@ hipError_t launch_union(const FfnPlan &p, const float *scores, void *ws,
                        p.T, (int)p.E, p.n, (int)p.W,
                        reinterpret_cast<uint64_t *>(base + p.off_masks),
                        reinterpret_cast<int32_t *>(base + p.off_lists),
-                       reinterpret_cast<int32_t *>(base + p.off_counts),
-                       reinterpret_cast<uint32_t *>(base + p.off_ctrl),
-                       (int)(p.MPC * p.JT), masks_out, lists_out, counts_out);
+                       reinterpret_cast<int32_t *>(base + p.off_counts), masks_out,
+                       lists_out, counts_out);
     return hipGetLastError();
 }
 

@@ -100,9 +100,15 @@ size_t blockffn_chunk_ffn_workspace_bytes(int64_t T, int64_t d_h, int64_t E,
  *                   score-scaled hidden activations are rounded to bf16 before the
  *                   second product and y is rounded to bf16 (nearest even).
  *   workspace, workspace_bytes: device scratch of at least
- *                   blockffn_chunk_ffn_workspace_bytes(...) bytes; its contents need
- *                   no initialisation and are unspecified afterwards. Calls that may
- *                   run concurrently need separate workspaces.
+ *                   blockffn_chunk_ffn_workspace_bytes(...) bytes, ZERO-FILLED before
+ *                   its first use (e.g. hipMemset or torch.zeros). It holds arrival
+ *                   counters that every call returns to zero, so a zeroed workspace
+ *                   stays valid across calls of any sizes; the rest of it is scratch.
+ *                   Calls that may run concurrently need separate workspaces. A call
+ *                   whose kernel times out waiting on its own work items (which only
+ *                   a broken device or a workspace that was not zeroed can cause)
+ *                   writes NaN to the affected rows of y; zero the workspace again
+ *                   before reusing it.
  *   union_masks_out   [C][ceil(E/64)] uint64 or NULL: bit e%64 of word e/64 set when
  *                   e is in U_c (C = ceil(T/n))
  *   expert_lists_out  [C][E] int32 or NULL: U_c in ascending expert id, then -1

@@ -182,19 +182,31 @@ def test_experts_outside_union_are_never_read(dtype):
     assert np.array_equal(y, yn)
 
 
-def test_deterministic_and_workspace_needs_no_init():
-    """Two calls agree bitwise (the split-sum path included), and a workspace full of
-    garbage, or left over from a call of another shape, gives the same result."""
+def test_deterministic_and_workspace_reuse():
+    """Calls agree bitwise (the split-sum path included), and one zeroed workspace
+    stays valid across many calls of different shapes: every call returns its
+    arrival counters to zero."""
     inp = inputs.make_workload("decode", seed=11)
-    nbytes = bf.blockffn_chunk_ffn_workspace_bytes(2048, 2048, 64, 128, 32, bf.BLOCKFFN_BF16)
-    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device=DEV)
+    shapes = [(32, 32), (256, 32), (77, 48)]
+    nbytes = max(bf.blockffn_chunk_ffn_workspace_bytes(T, 2048, 64, 128, n, bf.BLOCKFFN_BF16)
+                 for T, n in shapes)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device=DEV)
     y1, *_ = run_ffn(inp, workspace=ws)
     y2, *_ = run_ffn(inp, workspace=ws)
     assert np.array_equal(y1, y2)
     big = inputs.make_workload("prefill", seed=12, T=256)
-    run_ffn(big, workspace=ws)
+    yb1, *_ = run_ffn(big, workspace=ws)
+    odd = inputs.make_workload("decode", seed=13, T=77, n=48)
+    yo, *_ = run_ffn(odd, workspace=ws)
     y3, *_ = run_ffn(inp, workspace=ws)
     assert np.array_equal(y1, y3)
+    yb2, *_ = run_ffn(big, workspace=ws)
+    assert np.array_equal(yb1, yb2)
+    y_ref = oracle.chunk_ffn(odd.x, odd.scores, odd.w1, odd.w2, 48)
+    assert rel_err(yo, y_ref) <= TOL_BF16
+    fresh = bf.blockffn_chunk_ffn_workspace(2048, 2048, 64, 128, 32, bf.BLOCKFFN_BF16, DEV)
+    y4, *_ = run_ffn(inp, workspace=fresh)
+    assert np.array_equal(y1, y4)
 
 
 def test_score_scaling_by_two_is_exact():
@@ -330,3 +342,36 @@ def test_tiny_fp32_end_to_end():
     y_ref = oracle.chunk_ffn(inp.x, s_ref.astype(np.float32), inp.w1, inp.w2, inp.n)
     assert rel_err(host(y), y_ref) <= TOL_F32
     assert 0.3 < (host(s) == 0).mean() < 0.7
+
+
+# ------------------------------------------------------------------ graph capture
+
+def test_graph_replays_match_eager():
+    """The calls captured in a HIP graph (as the benchmark runs them) give the eager
+    results on every replay, with eager work and synchronisations in between."""
+    draws = [inputs.make_workload("decode", seed=20 + i) for i in range(3)]
+    dt = torch.bfloat16
+    w1 = dev(draws[0].w1, dt)
+    w2 = dev(draws[0].w2, dt)
+    xs = [dev(d.x, dt) for d in draws]
+    ss = [dev(d.scores) for d in draws]
+    ws = bf.blockffn_chunk_ffn_workspace(32, 2048, 64, 128, 32, bf.BLOCKFFN_BF16, DEV)
+    ys = [torch.empty((32, 2048), dtype=dt, device=DEV) for _ in draws]
+    eager = []
+    for x, s in zip(xs, ss):
+        eager.append(host(bf.blockffn_chunk_ffn(x, s, w1, w2, 32, workspace=ws)))
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for x, s, y in zip(xs, ss, ys):
+            bf.blockffn_chunk_ffn(x, s, w1, w2, 32, y=y, workspace=ws)
+    for rep in range(4):
+        for y in ys:
+            y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        for y, ref in zip(ys, eager):
+            assert np.array_equal(host(y), ref), f"replay {rep}"
+        # eager work on the same workspace between replays
+        bf.blockffn_chunk_ffn(xs[rep % 3], ss[(rep + 1) % 3], w1, w2, 32, workspace=ws)
+        torch.cuda.synchronize()
