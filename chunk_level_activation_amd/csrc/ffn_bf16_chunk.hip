@@ -18,10 +18,10 @@
 //     union's slots are split into X contiguous groups, group g on XCD g, so all
 //     exchanges of a group stay in that XCD's L2.
 //   * Every workgroup computes the union itself from the 32 x E scores.
-//   * Up items: (slot, 64 hidden units, 512-wide slice of d_h). The x slice (32 x 512)
-//     is staged once in LDS; eight waves (2 row halves x 4 k quarters) stream the W1
-//     block, partial sums meet in LDS, and the item's 32 x 64 fp32 partial goes to the
-//     XCD's L2. The last of the d_h/512 slices to arrive adds them in slice order,
+//   * Up items: (slot, 128 hidden units, 512-wide slice of d_h). The x slice (32 x
+//     512) is staged once in LDS; eight waves (4 row quarters x 2 k halves) stream the
+//     W1 block, partial sums meet in LDS, and the item's 32 x 128 fp32 partial goes to
+//     the XCD's L2. The last of the d_h/512 slices to arrive adds them in slice order,
 //     applies Swish and the score, and writes the bf16 hidden tile.
 //   * Down items: (64 output columns, expert group). W2 for the group's slots is
 //     loaded first (it depends only on the union), then the item waits for the
@@ -30,7 +30,8 @@
 //   * The X group tiles of an output tile are on different XCDs: they go to memory
 //     with device-scope stores, and the last of the X to arrive (an atomic counter)
 //     adds them in group order and writes y.
-// The lower half of each XCD's workgroups run up items, the upper half down items.
+// The lower workgroups of each XCD run up items, the upper ones down items (the split
+// follows the group's size: one workgroup per up item where possible).
 // A down workgroup waits only on up workgroups of its own XCD with smaller indices,
 // which the in-order dispatcher has placed first, so every wait ends (it is bounded
 // anyway: on time-out the outputs of the tile become NaN). The cross-XCD sum and the
@@ -46,7 +47,7 @@ namespace {
 
 constexpr int kThreads = 512;
 constexpr int kKSlice = 512;        // d_h elements per up item
-constexpr int kUpRows = 64;         // hidden units per up item
+constexpr int kUpRows = 128;        // hidden units per up item
 constexpr int kDnCols = 64;         // output columns per down item
 constexpr int kXPitch = kKSlice + 8;   // LDS row pitch (bf16) of the staged x slice
 constexpr uint32_t kSpinLimit = 1u << 22;
@@ -59,7 +60,7 @@ struct Chunk1Args {
     const uint16_t *w2;
     uint16_t *y;
     uint16_t *hidden;       // [E][32][d_e] bf16
-    float *up_part;         // [E][RT][KP][32][64] fp32 partial pre-activations
+    float *up_part;         // [E][RT][KP][32][128] fp32 partial pre-activations
     float *dn_part;         // [JT][X][32][64] fp32 group tiles
     uint32_t *up_arrive;    // [E][RT] k slices stored per up tile
     uint32_t *up_done;      // [E]     finished hidden tiles per slot
@@ -71,7 +72,7 @@ struct Chunk1Args {
     int T, d_h, E, d_e;
     int X;                  // XCDs = expert groups
     int WPX;                // workgroups per XCD
-    int RT, KP, JT;         // d_e / 64, d_h / 512, d_h / 64
+    int RT, KP, JT;         // d_e / 128, d_h / 512, d_h / 64
 };
 
 // Buffer-resource accesses: a 128-bit descriptor in scalar registers plus a 32-bit
@@ -134,7 +135,7 @@ struct Shared {
     int list[256];
     int flag;
     float s_col[kTileM];
-    float red[4][2][kTileM][33];              // [k part][half][row][col]
+    float red[4][2][kTileM][33];              // up: [row quarter][k half]; down: [part][half]
     uint16_t xs[kTileM * kXPitch];            // staged x slice (up items)
 };
 
@@ -181,16 +182,16 @@ __device__ void up_item(const Chunk1Args &a, const Rsrc &r, Shared &sh, int slot
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int e = sh.list[slot];
     const int k0 = kq * kKSlice;
-    // wave -> (row half rh, k part kp): rows rt*64 + rh*32 .. +32, k k0 + kp*128 .. +128
-    const int rh = wave & 1, kp = wave >> 1;
+    // wave -> (row quarter rq, k half kh): rows rt*128 + rq*32 .. +32, k k0 + kh*256 .. +256
+    const int rq = wave & 3, kh = wave >> 2;
     const int col = lane & 31, kg = lane >> 5;
     const uint32_t w1_off = (uint32_t)e * ((uint32_t)a.d_e * (uint32_t)a.d_h * 2u) +
-                            (uint32_t)(rt * kUpRows + rh * 32 + col) * ((uint32_t)a.d_h * 2u) +
-                            (uint32_t)(k0 + kp * 128 + kg * 8) * 2u;
+                            (uint32_t)(rt * kUpRows + rq * 32 + col) * ((uint32_t)a.d_h * 2u) +
+                            (uint32_t)(k0 + kh * 256 + kg * 8) * 2u;
     // W1 first: the weight stream is the long pole, x comes from L2
-    bf16x8 bw[8];
+    bf16x8 bw[16];
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks)
+    for (int ks = 0; ks < 16; ++ks)
         bw[ks] = bload<kNT>(r.w1, w1_off + ks * 32);
     // stage x[:, k0:k0+512] in LDS (rows past T read as zero): 4 loads per thread
     constexpr int kXLoads = kTileM * (kKSlice / 8) / kThreads;
@@ -216,31 +217,30 @@ __device__ void up_item(const Chunk1Args &a, const Rsrc &r, Shared &sh, int slot
     for (int i = 0; i < 16; ++i)
         acc[i] = 0.0f;
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < 16; ++ks) {
         const bf16x8 ax =
-            *reinterpret_cast<const bf16x8 *>(&sh.xs[col * kXPitch + kp * 128 + ks * 16 + kg * 8]);
+            *reinterpret_cast<const bf16x8 *>(&sh.xs[col * kXPitch + kh * 256 + ks * 16 + kg * 8]);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ax, bw[ks], acc, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
-        sh.red[kp][rh][acc_row(i, lane)][col] = acc[i];
+        sh.red[rq][kh][acc_row(i, lane)][col] = acc[i];
     __syncthreads();
-    // 32 tokens x 64 units; thread -> (token tt, units u0 .. u0 + 3)
-    const int tt = tid >> 4, u0 = (tid & 15) * 4;
-    float4 p;
-    {
-        float q4[4];
+    // 32 tokens x 128 units; thread -> (token tt, units u0 .. u0 + 7), u0 within one quarter
+    const int tt = tid >> 4, u0 = (tid & 15) * 8;
+    float pv[8];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int u = u0 + q, h = u >> 5, uc = u & 31;
-            q4[q] = ((sh.red[0][h][tt][uc] + sh.red[1][h][tt][uc]) + sh.red[2][h][tt][uc]) +
-                    sh.red[3][h][tt][uc];
-        }
-        p = make_float4(q4[0], q4[1], q4[2], q4[3]);
+    for (int q = 0; q < 8; ++q) {
+        const int u = u0 + q, quarter = u >> 5, uc = u & 31;
+        pv[q] = sh.red[quarter][0][tt][uc] + sh.red[quarter][1][tt][uc];
     }
-    const uint32_t tile_off = (uint32_t)(((slot * a.RT + rt) * a.KP) * (kTileM * kUpRows) * 4);
+    const uint32_t tile_bytes = kTileM * kUpRows * 4;
+    const uint32_t tile_off = (uint32_t)((slot * a.RT + rt) * a.KP) * tile_bytes;
     const uint32_t elem_off = (uint32_t)((tt * kUpRows + u0) * 4);
-    bstore_f4<kSC0>(r.upp, tile_off + kq * (kTileM * kUpRows * 4) + elem_off, p);
+    bstore_f4<kSC0>(r.upp, tile_off + kq * tile_bytes + elem_off,
+                    make_float4(pv[0], pv[1], pv[2], pv[3]));
+    bstore_f4<kSC0>(r.upp, tile_off + kq * tile_bytes + elem_off + 16,
+                    make_float4(pv[4], pv[5], pv[6], pv[7]));
     drain_memory();
     __syncthreads();
     if (tid == 0) {
@@ -253,21 +253,28 @@ __device__ void up_item(const Chunk1Args &a, const Rsrc &r, Shared &sh, int slot
     if (!sh.flag)
         return;
     // Last slice of the tile: add the KP partials in slice order, Swish, score, bf16.
-    float sum[4] = {0.f, 0.f, 0.f, 0.f};
+    float sum[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int q = 0; q < a.KP; ++q) {
-        const float4 v = bload_f4<kSC0>(r.upp, tile_off + q * (kTileM * kUpRows * 4) + elem_off);
-        sum[0] += v.x;
-        sum[1] += v.y;
-        sum[2] += v.z;
-        sum[3] += v.w;
+        const float4 v0 = bload_f4<kSC0>(r.upp, tile_off + q * tile_bytes + elem_off);
+        const float4 v1 = bload_f4<kSC0>(r.upp, tile_off + q * tile_bytes + elem_off + 16);
+        sum[0] += v0.x;
+        sum[1] += v0.y;
+        sum[2] += v0.z;
+        sum[3] += v0.w;
+        sum[4] += v1.x;
+        sum[5] += v1.y;
+        sum[6] += v1.z;
+        sum[7] += v1.w;
     }
     const float sc = sh.s_col[tt];
-    uint64_t packed = 0;
+    uint32_t h[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
-        packed |= (uint64_t)f32_to_bf16(swish_fast(sum[q]) * sc) << (16 * q);
-    bstore_u64<kSC0>(r.hid, (uint32_t)(((slot * kTileM + tt) * a.d_e + rt * kUpRows + u0) * 2),
-                     packed);
+        h[q] = (uint32_t)f32_to_bf16(swish_fast(sum[2 * q]) * sc) |
+               ((uint32_t)f32_to_bf16(swish_fast(sum[2 * q + 1]) * sc) << 16);
+    __builtin_amdgcn_raw_buffer_store_b128(
+        u32x4{h[0], h[1], h[2], h[3]}, r.hid,
+        (int)(((slot * kTileM + tt) * a.d_e + rt * kUpRows + u0) * 2), 0, kSC0);
     drain_memory();
     __syncthreads();
     if (tid == 0)
@@ -447,10 +454,14 @@ ffn_bf16_chunk1_kernel(Chunk1Args a)
     const int s0 = (int)((int64_t)g * cnt / a.X), s1 = (int)((int64_t)(g + 1) * cnt / a.X);
     const int sg = s1 - s0;
     const int U = sg * a.RT * a.KP;           // up items of this group
-    const int half = a.WPX / 2;
-    if (k < half) {
-        // up workgroups: items k, k + half, ...
-        for (int u = k; u < U; u += half) {
+    // Role split of this XCD's workgroups, decided per group from the union: up items
+    // finish with a k-slice sum and a hidden-tile handoff, so a second round of them is
+    // dear; give them one workgroup each where possible and let the down workgroups
+    // (at least a quarter of the XCD) loop over the column tiles instead.
+    const int n_up = U < a.WPX - a.WPX / 4 ? U : a.WPX - a.WPX / 4;
+    if (k < n_up) {
+        // up workgroups: items k, k + n_up, ...
+        for (int u = k; u < U; u += n_up) {
             const int slot = s0 + u / (a.RT * a.KP);
             const int rt = (u / a.KP) % a.RT;
             const int kq = u % a.KP;
@@ -470,7 +481,7 @@ ffn_bf16_chunk1_kernel(Chunk1Args a)
         d.w2_expert_bytes = (uint32_t)a.d_h * (uint32_t)a.d_e * 2u;
         d.hid_slot_bytes = (uint32_t)kTileM * (uint32_t)a.d_e * 2u;
         d.hid_row_off = (uint32_t)(lane & 31) * (uint32_t)a.d_e * 2u;
-        for (int dn = k - half; dn < a.JT; dn += half) {
+        for (int dn = k - n_up; dn < a.JT; dn += a.WPX - n_up) {
             d.jt = dn;
             d.w2_row_off = (uint32_t)(dn * kDnCols + d.ch * 32 + (lane & 31)) * (uint32_t)a.d_e * 2u;
             down_issue_w2(a, r, sh, d, 0);
@@ -484,7 +495,8 @@ ffn_bf16_chunk1_kernel(Chunk1Args a)
 
 bool chunk1_supported(int64_t CT, int64_t d_h, int64_t d_e)
 {
-    return CT == 1 && d_h % kKSlice == 0 && d_e % kUpRows == 0;
+    return CT == 1 && d_h % kKSlice == 0 && d_e % kUpRows == 0 &&
+           (uint64_t)d_h * (uint64_t)d_e * 2u * 256u < 0x7fffffffull;
 }
 
 // Occupancy of the chunk kernel (workgroups per CU), 0 on error.
