@@ -51,6 +51,9 @@ def parse_args(argv=None):
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the all-experts-active comparison run")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="run one device-to-device copy of this many MiB first (a plain "
+                         "kernel of known traffic, for scaling hardware byte counters)")
     return ap.parse_args(argv)
 
 
@@ -104,6 +107,12 @@ def main(argv=None):
     from chunk_level_activation_amd import inputs
 
     torch.cuda.set_device(0)
+    if args.calibrate_copy_mib > 0:
+        src = torch.ones(args.calibrate_copy_mib * 2 ** 18, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     cfg, copies, draws = make_inputs(args, torch, np, inputs)
     T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
     C = -(-T // n)
@@ -112,6 +121,7 @@ def main(argv=None):
     router_out = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in draws]
     y = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
     ws = bf.blockffn_chunk_ffn_workspace(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16, dev)
+    router_ws = bf.blockffn_router_workspace(T, d_h, E, bf.BLOCKFFN_BF16, dev)
     counts = [torch.zeros(C, dtype=torch.int32, device=dev) for _ in draws]
     nc, nd = len(copies), len(draws)
     # One captured graph holds S consecutive steps, S a multiple of both rotation
@@ -131,7 +141,8 @@ def main(argv=None):
     def step(i):
         w = copies[i % nc]
         d = draws[i % nd]
-        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=router_out[i % nd])
+        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=router_out[i % nd],
+                           workspace=router_ws)
         ffn(i)
 
     def capture(body):

@@ -19,7 +19,8 @@ import os
 
 __all__ = [
     "BLOCKFFN_F32", "BLOCKFFN_BF16", "BlockFFNError", "FP32_EPS", "library_path",
-    "blockffn_router", "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
+    "blockffn_router", "blockffn_router_workspace_bytes", "blockffn_router_workspace",
+    "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
     "blockffn_chunk_ffn_workspace",
     "blockffn_last_error", "blockffn_version", "load_library",
 ]
@@ -53,8 +54,11 @@ def load_library():
             "`python -m chunk_level_activation_amd.build_lib` (or __graft_entry__.build())")
     lib = ctypes.CDLL(library_path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.blockffn_router.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P]
+    lib.blockffn_router.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P,
+                                    ctypes.c_size_t, P]
     lib.blockffn_router.restype = I
+    lib.blockffn_router_workspace_bytes.argtypes = [I64, I64, I64, I]
+    lib.blockffn_router_workspace_bytes.restype = ctypes.c_size_t
     lib.blockffn_chunk_ffn_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
     lib.blockffn_chunk_ffn_workspace_bytes.restype = ctypes.c_size_t
     lib.blockffn_chunk_ffn.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, P,
@@ -108,10 +112,27 @@ def _stream(stream):
     return s.cuda_stream
 
 
+def blockffn_router_workspace_bytes(T: int, d_h: int, E: int, dtype: int) -> int:
+    nbytes = load_library().blockffn_router_workspace_bytes(T, d_h, E, dtype)
+    if nbytes == 0:
+        raise BlockFFNError(1, blockffn_last_error())
+    return int(nbytes)
+
+
+def blockffn_router_workspace(T: int, d_h: int, E: int, dtype: int, device="cuda"):
+    """A zero-filled router workspace (see blockffn.h): it must start zeroed and is
+    returned to that state by every call."""
+    import torch
+    nbytes = blockffn_router_workspace_bytes(T, d_h, E, dtype)
+    return torch.zeros(nbytes, dtype=torch.uint8, device=device)
+
+
 def blockffn_router(x, w_r, gain=None, bias=None, eps: float = FP32_EPS, *, scores=None,
-                    logits=None, stream=None):
+                    logits=None, workspace=None, stream=None):
     """scores [T, E] fp32 = RMSNorm_E(ReLU(x W_r^T + bias)) * gain. x [T, d_h] and
-    w_r [E, d_h] are both float32 or both bfloat16; gain/bias are [E] float32."""
+    w_r [E, d_h] are both float32 or both bfloat16; gain/bias are [E] float32.
+    `workspace` (from blockffn_router_workspace) lets few-token calls split the d_h
+    sum over several workgroups; without one the call runs unsplit."""
     import torch
     lib = load_library()
     T, d_h = x.shape
@@ -120,10 +141,11 @@ def blockffn_router(x, w_r, gain=None, bias=None, eps: float = FP32_EPS, *, scor
         raise ValueError("w_r must be [E, d_h] with the dtype of x")
     if scores is None:
         scores = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
             _dev(bias, "bias", torch.float32), float(eps), T, d_h, E, _dtype_code(x),
             _dev(scores, "scores", torch.float32), _dev(logits, "logits", torch.float32),
-            _stream(stream)]
+            _dev(workspace, "workspace"), ws_bytes, _stream(stream)]
     _check(lib.blockffn_router(*args))
     return scores
 

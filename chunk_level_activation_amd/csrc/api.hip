@@ -14,32 +14,32 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Per-device facts the one-launch bf16 schedule depends on, found on first use.
+// Per-device facts some schedules depend on, found on first use.
 struct DeviceInfo {
     bool probed = false;
     int xcds = 0;          // XCDs, when round-robin workgroup placement was verified
-    int wg_per_xcd = 0;    // resident one-launch workgroups per XCD
+    int cus = 0;           // compute units
 };
 constexpr int kMaxDevices = 64;
 std::mutex g_device_mutex;
 DeviceInfo g_devices[kMaxDevices];
 
-// The one-launch schedule's grid on the current device: fills *xcds and *wg_per_xcd
-// and returns true when it may be used. The first call probes workgroup placement;
-// it is skipped (and retried later) while the stream is being captured into a
-// graph, because the probe synchronises.
-bool chunk1_grid(hipStream_t stream, int *xcds, int *wg_per_xcd)
+// Number of XCDs X of the current device if workgroup b of a launch is verified to
+// run on XCD b % X, else 0. The first call probes; the probe synchronises, so it is
+// skipped (and retried on a later call) while the stream is being captured into a
+// graph, and the call answers 0 meanwhile.
+const DeviceInfo *device_info(hipStream_t stream)
 {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
-        return false;
+        return nullptr;
     std::lock_guard<std::mutex> lock(g_device_mutex);
     DeviceInfo &d = g_devices[dev];
     if (!d.probed) {
         hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
         if (hipStreamIsCapturing(stream, &cs) != hipSuccess ||
             cs != hipStreamCaptureStatusNone)
-            return false;
+            return nullptr;
         int nxcd = 0, cus = 0;
         bool round_robin = false;
         if (hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess &&
@@ -47,17 +47,34 @@ bool chunk1_grid(hipStream_t stream, int *xcds, int *wg_per_xcd)
                 hipSuccess &&
             nxcd > 1 && nxcd <= blockffn::kMaxGroups && cus % nxcd == 0 &&
             blockffn::probe_xcd_placement(nxcd, &round_robin) == hipSuccess && round_robin) {
-            const int per_cu = blockffn::chunk1_blocks_per_cu();
-            if (per_cu >= 1) {
-                d.xcds = nxcd;
-                d.wg_per_xcd = (per_cu >= 2 ? 2 : 1) * (cus / nxcd);
-            }
+            d.xcds = nxcd;
+            d.cus = cus;
         }
         d.probed = true;
     }
-    *xcds = d.xcds;
-    *wg_per_xcd = d.wg_per_xcd;
-    return d.xcds > 0;
+    return &d;
+}
+
+int placement_xcds(hipStream_t stream)
+{
+    const DeviceInfo *d = device_info(stream);
+    return d ? d->xcds : 0;
+}
+
+// The one-launch schedule's grid on the current device: fills *xcds and *wg_per_xcd
+// and returns true when it may be used (verified placement, enough resident
+// workgroups).
+bool chunk1_grid(hipStream_t stream, int *xcds, int *wg_per_xcd)
+{
+    const DeviceInfo *d = device_info(stream);
+    if (!d || d->xcds <= 1)
+        return false;
+    const int per_cu = blockffn::chunk1_blocks_per_cu();
+    if (per_cu < 1)
+        return false;
+    *xcds = d->xcds;
+    *wg_per_xcd = (per_cu >= 2 ? 2 : 1) * (d->cus / d->xcds);
+    return true;
 }
 
 blockffn_status_t fail(blockffn_status_t code, const std::string &msg)
@@ -126,10 +143,18 @@ const char *blockffn_last_error(void) { return g_last_error.c_str(); }
 
 const char *blockffn_version(void) { return "blockffn-gfx950 0.1.0"; }
 
+size_t blockffn_router_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int dtype)
+{
+    if (check_dtype(dtype) != BLOCKFFN_OK || check_sizes(T, d_h, E, dtype) != BLOCKFFN_OK)
+        return 0;
+    const size_t need = dtype == BLOCKFFN_BF16 ? blockffn::router_workspace_bytes(T, d_h, E) : 0;
+    return need > 256 ? need : 256;
+}
+
 blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *gain,
                                   const float *bias, float eps, int64_t T, int64_t d_h,
                                   int64_t E, int dtype, float *scores, float *logits,
-                                  void *stream)
+                                  void *workspace, size_t workspace_bytes, void *stream)
 {
     blockffn_status_t st = check_dtype(dtype);
     if (st != BLOCKFFN_OK)
@@ -147,13 +172,22 @@ blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *g
     if (!aligned(scores, 4) || (logits && !aligned(logits, 4)) || (gain && !aligned(gain, 4)) ||
         (bias && !aligned(bias, 4)))
         return fail(BLOCKFFN_EUNSUPPORTED, "float arrays must be 4-byte aligned");
+    if (workspace) {
+        if (!aligned(workspace, 256))
+            return fail(BLOCKFFN_EUNSUPPORTED, "workspace needs 256-byte alignment");
+        const size_t need = blockffn_router_workspace_bytes(T, d_h, E, dtype);
+        if (workspace_bytes < need)
+            return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                                 " bytes, needs " + std::to_string(need));
+    }
 
     hipStream_t s = static_cast<hipStream_t>(stream);
     hipError_t err;
     if (dtype == BLOCKFFN_BF16)
         err = blockffn::launch_router_bf16(static_cast<const uint16_t *>(x),
                                            static_cast<const uint16_t *>(w_r), gain, bias, eps,
-                                           T, d_h, E, scores, logits, s);
+                                           T, d_h, E, scores, logits, workspace,
+                                           workspace ? placement_xcds(s) : 0, s);
     else
         err = blockffn::launch_router_f32(static_cast<const float *>(x),
                                           static_cast<const float *>(w_r), gain, bias, eps, T,

@@ -40,6 +40,7 @@
 // control block.
 #include "common.h"
 #include "plan.h"
+#include "sync.h"
 
 namespace blockffn {
 
@@ -74,57 +75,6 @@ struct Chunk1Args {
     int WPX;                // workgroups per XCD
     int RT, KP, JT;         // d_e / 128, d_h / 512, d_h / 64
 };
-
-// Buffer-resource accesses: a 128-bit descriptor in scalar registers plus a 32-bit
-// byte offset per lane (fewer vector registers than 64-bit pointers, and loads past
-// the range return zero instead of faulting). Cache policy bits: nt = streamed once,
-// sc0 = bypass L1 (meet in the XCD's L2), sc1 = device-coherent.
-constexpr int kNT = 2, kSC0 = 1, kSC1 = 16;
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint64_t bytes)
-{
-    const int n = bytes < 0x7fffffffull ? (int)bytes : 0x7fffffff;
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, n, 0x00020000);
-}
-template <int AUX>
-__device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
-}
-template <int AUX>
-__device__ __forceinline__ float4 bload_f4(__amdgpu_buffer_rsrc_t r, uint32_t off)
-{
-    return __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
-}
-template <int AUX>
-__device__ __forceinline__ void bstore_f4(__amdgpu_buffer_rsrc_t r, uint32_t off, float4 v)
-{
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, AUX);
-}
-template <int AUX>
-__device__ __forceinline__ void bstore_u64(__amdgpu_buffer_rsrc_t r, uint32_t off, uint64_t v)
-{
-    __builtin_amdgcn_raw_buffer_store_b64(
-        __builtin_bit_cast(unsigned int __attribute__((ext_vector_type(2))), v), r, (int)off, 0, AUX);
-}
-
-__device__ __forceinline__ uint32_t ld_counter(const uint32_t *p)
-{
-    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t add_counter(uint32_t *p, uint32_t v)
-{
-    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_counter(uint32_t *p, uint32_t v)
-{
-    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void drain_memory()
-{
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
 
 // 32x32 accumulator layout: element i of a lane is row (i/4)*8 + (lane/32)*4 + i%4 of
 // column lane%32.

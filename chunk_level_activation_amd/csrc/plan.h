@@ -83,9 +83,18 @@ hipError_t launch_ffn_bf16_chunk1(const FfnPlan &p, int xcds, int wg_per_xcd,
 hipError_t launch_ffn_f32(const FfnPlan &p, const float *x, const float *scores,
                           const float *w1, const float *w2, float *y, void *ws,
                           hipStream_t stream);
+// Router: the bf16 kernel splits the d_h sum over workgroups when it has a workspace
+// (ws != NULL, at least router_workspace_bytes, zero-filled once; its counters return
+// to zero after every call). router_workspace_bytes is 0 when no split pays. xcds > 1
+// states that workgroup b runs on XCD b % xcds (verified on this device); the splits
+// of a tile then share an XCD. xcds <= 1: no placement assumption.
+constexpr size_t kRouterControlBytes = 64 * 1024;   // arrival counters, one per token tile
+int router_splits(int64_t T, int64_t d_h);
+size_t router_workspace_bytes(int64_t T, int64_t d_h, int64_t E);
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const float *gain,
                               const float *bias, float eps, int64_t T, int64_t d_h,
-                              int64_t E, float *scores, float *logits, hipStream_t stream);
+                              int64_t E, float *scores, float *logits, void *ws, int xcds,
+                              hipStream_t stream);
 // Checks that workgroup b of a launch runs on XCD b % nxcd (round-robin dispatch).
 hipError_t probe_xcd_placement(int nxcd, bool *round_robin);
 hipError_t launch_router_f32(const float *x, const float *w_r, const float *gain,

@@ -8,78 +8,164 @@
 //     s[t,e] = max(l,0) / sqrt(mean_e max(l,0)^2 + eps) * gain[e]
 // A workgroup owns all E logits of its 32 tokens, so the RMSNorm row reduction is
 // done in LDS right after the product, with no second pass over memory.
+//
+// Few tokens (decode) leave most of the chip idle with one workgroup per 32 tokens,
+// so the d_h sum is split over S workgroups per token tile: each stores its 32 x E
+// partial logits in the workspace, and the last of the S to arrive (an atomic
+// counter) adds the S partials in split order, so the result does not depend on
+// which workgroup finishes last, and applies ReLU and RMSNorm.
 #include "common.h"
 #include "plan.h"
+#include "sync.h"
 
 namespace blockffn {
 
 // bf16: 32 tokens x all experts per workgroup, ET tiles of 32 experts, 8 waves. The
 // 32x32x16 bf16 MFMA takes A = x rows (32 tokens x 16 k) and B = W_r rows
-// transposed (16 k x 32 experts). The waves take k steps round robin, each issuing
-// the loads of KB steps together; the wave sums are added in wave order in LDS.
+// transposed (16 k x 32 experts). Wave w owns expert tile w % ET and every
+// (8/ET)-th k step of the workgroup's range, issuing the loads of KB steps together;
+// the 8/ET k parts of a tile meet in LDS after one barrier and are added in part
+// order.
 constexpr int kRouterThreads = 512;
 constexpr int kRouterWaves = kRouterThreads / kWave;
+constexpr int64_t kRouterTargetBlocks = 128;   // split the d_h sum until about this many
+constexpr int kRouterMaxSplits = 8;
 
-template <int ET>
+// LOCAL: the S splits of a tile run on one XCD (the caller verified round-robin
+// placement and laid the grid out so), and their partials meet in that XCD's L2;
+// otherwise they meet in memory.
+template <int ET, bool LOCAL>
 __global__ void __launch_bounds__(kRouterThreads)
 router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w_r,
                    const float *__restrict__ gain, const float *__restrict__ bias,
-                   float eps, int64_t T, int d_h, int E, float *__restrict__ scores,
-                   float *__restrict__ logits)
+                   float eps, int64_t T, int d_h, int E, int S, int X,
+                   float *__restrict__ scores, float *__restrict__ logits,
+                   float *__restrict__ part, uint32_t *__restrict__ arrive)
 {
-    constexpr int KB = ET >= 8 ? 2 : (ET >= 4 ? 4 : 8);
-    const int64_t t0 = (int64_t)blockIdx.x * kTileM;
+    constexpr int KPARTS = kRouterWaves / ET;
+    constexpr int KB = 8;
+    constexpr int kPitch = ET * 32 + 1;
+    __shared__ float red[KPARTS][kTileM][kPitch];
+    __shared__ float sgain[ET * 32], sbias[ET * 32];
+    __shared__ int last;
+
+    // workgroup -> (tile, split)
+    int64_t tile;
+    int split;
+    if (LOCAL) {
+        // workgroup b runs on XCD b % X; tile t lives on XCD t % X, so its splits are
+        // the workgroups (m*S + s)*X + t % X with m = t / X
+        const int xcd = blockIdx.x % X;
+        const int k = blockIdx.x / X;
+        tile = (int64_t)(k / S) * X + xcd;
+        split = k % S;
+        if (tile * kTileM >= T)
+            return;
+    } else {
+        tile = blockIdx.x / S;
+        split = blockIdx.x % S;
+    }
+    const int64_t t0 = tile * kTileM;
     const int tid = threadIdx.x;
     const int wave = tid / kWave;
     const int lane = tid % kWave;
     const int row = lane % 32;
     const int kg = lane / 32;
-    const bool vt = t0 + row < T;
-    const uint16_t *xr = x + (vt ? t0 + row : 0) * d_h + kg * 8;
-    const uint16_t *wr[ET];
-    bool ve[ET];
-    f32x16 acc[ET];
-#pragma unroll
-    for (int et = 0; et < ET; ++et) {
-        const int e = et * 32 + row;
-        ve[et] = e < E;
-        wr[et] = w_r + (int64_t)(ve[et] ? e : 0) * d_h + kg * 8;
-#pragma unroll
-        for (int i = 0; i < 16; ++i)
-            acc[et][i] = 0.0f;
+    const int et = wave % ET, kp = wave / ET;
+    if (tid < E) {
+        sgain[tid] = gain ? gain[tid] : 1.0f;
+        sbias[tid] = bias ? bias[tid] : 0.0f;
     }
+    const bool vt = t0 + row < T;
+    const int e_row = et * 32 + row;
+    const bool ve = e_row < E;
+    const uint16_t *xr = x + (vt ? t0 + row : 0) * d_h + kg * 8;
+    const uint16_t *wr = w_r + (int64_t)(ve ? e_row : 0) * d_h + kg * 8;
+    f32x16 acc;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        acc[i] = 0.0f;
+    // this split's range of 16-wide k steps
     const int KS = d_h / 16;
-    for (int kb = wave; kb < KS; kb += kRouterWaves * KB) {
-        bf16x8 av[KB], bv[KB][ET];
+    const int ks0 = (int)((int64_t)KS * split / S), ks1 = (int)((int64_t)KS * (split + 1) / S);
+    for (int kb = ks0 + kp; kb < ks1; kb += KPARTS * KB) {
+        bf16x8 av[KB], bv[KB];
 #pragma unroll
         for (int i = 0; i < KB; ++i) {
-            const int ks = kb + i * kRouterWaves;
-            const bool ok = ks < KS;
+            const int ks = kb + i * KPARTS;
+            const bool ok = ks < ks1;
             av[i] = ok && vt ? load_bf16x8(xr + ks * 16) : zero_bf16x8();
-#pragma unroll
-            for (int et = 0; et < ET; ++et)
-                bv[i][et] = ok && ve[et] ? load_bf16x8(wr[et] + ks * 16) : zero_bf16x8();
+            bv[i] = ok && ve ? load_bf16x8(wr + ks * 16) : zero_bf16x8();
         }
 #pragma unroll
         for (int i = 0; i < KB; ++i)
-#pragma unroll
-            for (int et = 0; et < ET; ++et)
-                acc[et] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[i][et], acc[et], 0,
-                                                                  0, 0);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[i], acc, 0, 0, 0);
     }
 
     // 32x32 accumulator layout: element i is row (i/4)*8 + (lane/32)*4 + i%4 (token)
     // of column lane%32 (expert).
-    __shared__ float lg[kTileM][ET * 32 + 1];
-    for (int w = 0; w < kRouterWaves; ++w) {
-        if (wave == w) {
 #pragma unroll
-            for (int et = 0; et < ET; ++et)
+    for (int i = 0; i < 16; ++i)
+        red[kp][(i / 4) * 8 + kg * 4 + (i % 4)][et * 32 + row] = acc[i];
+    __syncthreads();
+    // k parts in order -> red[0]
+    for (int v = tid; v < kTileM * E; v += kRouterThreads) {
+        const int tt = v / E, e = v % E;
+        float sum = red[0][tt][e];
 #pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    float &dst = lg[(i / 4) * 8 + kg * 4 + (i % 4)][et * 32 + row];
-                    dst = w == 0 ? acc[et][i] : dst + acc[et][i];
+        for (int q = 1; q < KPARTS; ++q)
+            sum += red[q][tt][e];
+        red[0][tt][e] = sum;
+    }
+    __syncthreads();
+    float(*lg)[kPitch] = red[0];
+
+    if (S > 1) {
+        // partial logits of this split -> workspace, then count the arrival. Four
+        // floats per access.
+        constexpr int kPol = LOCAL ? kSC0 : kSC1;
+        const int tile_floats = kTileM * E;
+        const __amdgpu_buffer_rsrc_t rp =
+            make_rsrc(part + (uint64_t)tile * S * tile_floats, (uint64_t)S * tile_floats * 4);
+        for (int v = tid * 4; v < tile_floats; v += kRouterThreads * 4) {
+            float4 o;
+            o.x = lg[v / E][v % E];
+            o.y = lg[(v + 1) / E][(v + 1) % E];
+            o.z = lg[(v + 2) / E][(v + 2) % E];
+            o.w = lg[(v + 3) / E][(v + 3) % E];
+            bstore_f4<kPol>(rp, (uint32_t)((split * tile_floats + v) * 4), o);
+        }
+        drain_memory();
+        __syncthreads();
+        if (tid == 0) {
+            const uint32_t prev = add_counter(&arrive[tile], 1u);
+            last = prev == (uint32_t)(S - 1);
+            if (last)
+                st_counter(&arrive[tile], 0u);
+        }
+        __syncthreads();
+        if (!last)
+            return;
+        // the last split adds all S partials in split order; all loads in flight first
+        for (int v = tid * 4; v < tile_floats; v += kRouterThreads * 4) {
+            float4 pv[kRouterMaxSplits];
+#pragma unroll
+            for (int q = 0; q < kRouterMaxSplits; ++q)
+                if (q < S)
+                    pv[q] = bload_f4<kPol>(rp, (uint32_t)((q * tile_floats + v) * 4));
+            float4 sum = pv[0];
+#pragma unroll
+            for (int q = 1; q < kRouterMaxSplits; ++q)
+                if (q < S) {
+                    sum.x += pv[q].x;
+                    sum.y += pv[q].y;
+                    sum.z += pv[q].z;
+                    sum.w += pv[q].w;
                 }
+            lg[v / E][v % E] = sum.x;
+            lg[(v + 1) / E][(v + 1) % E] = sum.y;
+            lg[(v + 2) / E][(v + 2) % E] = sum.z;
+            lg[(v + 3) / E][(v + 3) % E] = sum.w;
         }
         __syncthreads();
     }
@@ -89,7 +175,7 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     const int64_t t = t0 + tt;
     float sumsq = 0.0f;
     for (int e = sub; e < E; e += 16) {
-        const float l = bias ? lg[tt][e] + bias[e] : lg[tt][e];
+        const float l = bias ? lg[tt][e] + sbias[e] : lg[tt][e];
         lg[tt][e] = l;
         const float r = l > 0.0f ? l : 0.0f;
         sumsq = fmaf(r, r, sumsq);
@@ -103,7 +189,7 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
         for (int e = sub; e < E; e += 16) {
             const float l = lg[tt][e];
             const float r = l > 0.0f ? l : 0.0f;
-            scores[t * E + e] = r * inv * (gain ? gain[e] : 1.0f);
+            scores[t * E + e] = r * inv * sgain[e];
             if (logits)
                 logits[t * E + e] = l;
         }
@@ -145,24 +231,62 @@ router_f32_kernel(const float *__restrict__ x, const float *__restrict__ w_r,
     }
 }
 
+int router_splits(int64_t T, int64_t d_h)
+{
+    const int64_t tiles = (T + kTileM - 1) / kTileM;
+    // at least two 16-wide k steps per wave of a split
+    const int64_t smax = d_h / (16 * 2 * kRouterWaves);
+    int64_t s = (kRouterTargetBlocks + tiles - 1) / tiles;
+    if (s > smax)
+        s = smax;
+    if (s > kRouterMaxSplits)
+        s = kRouterMaxSplits;
+    return s < 2 ? 1 : (int)s;
+}
+
+size_t router_workspace_bytes(int64_t T, int64_t d_h, int64_t E)
+{
+    const int S = router_splits(T, d_h);
+    if (S == 1)
+        return 0;
+    const int64_t tiles = (T + kTileM - 1) / kTileM;
+    return kRouterControlBytes + (size_t)tiles * S * kTileM * E * sizeof(float);
+}
+
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const float *gain,
                               const float *bias, float eps, int64_t T, int64_t d_h,
-                              int64_t E, float *scores, float *logits, hipStream_t stream)
+                              int64_t E, float *scores, float *logits, void *ws, int xcds,
+                              hipStream_t stream)
 {
-    const dim3 grid((unsigned)((T + kTileM - 1) / kTileM)), block(kRouterThreads);
+    const int64_t tiles = (T + kTileM - 1) / kTileM;
+    const int S = ws ? router_splits(T, d_h) : 1;
+    uint32_t *arrive = static_cast<uint32_t *>(ws);
+    float *part = ws ? reinterpret_cast<float *>(static_cast<char *>(ws) + kRouterControlBytes)
+                     : nullptr;
+    const bool local = S > 1 && xcds > 1;
+    const int X = local ? xcds : 1;
+    const int64_t blocks = local ? (tiles + X - 1) / X * S * X : tiles * S;
+    const dim3 grid((unsigned)blocks), block(kRouterThreads);
     const int ET = (int)((E + 31) / 32);
-    if (ET <= 1)
-        hipLaunchKernelGGL(router_bf16_kernel<1>, grid, block, 0, stream, x, w_r, gain, bias,
-                           eps, T, (int)d_h, (int)E, scores, logits);
-    else if (ET <= 2)
-        hipLaunchKernelGGL(router_bf16_kernel<2>, grid, block, 0, stream, x, w_r, gain, bias,
-                           eps, T, (int)d_h, (int)E, scores, logits);
-    else if (ET <= 4)
-        hipLaunchKernelGGL(router_bf16_kernel<4>, grid, block, 0, stream, x, w_r, gain, bias,
-                           eps, T, (int)d_h, (int)E, scores, logits);
-    else
-        hipLaunchKernelGGL(router_bf16_kernel<8>, grid, block, 0, stream, x, w_r, gain, bias,
-                           eps, T, (int)d_h, (int)E, scores, logits);
+#define ROUTER_LAUNCH(N, L)                                                                 \
+    hipLaunchKernelGGL((router_bf16_kernel<N, L>), grid, block, 0, stream, x, w_r, gain,    \
+                       bias, eps, T, (int)d_h, (int)E, S, X, scores, logits, part, arrive)
+#define ROUTER_LAUNCH_ET(L)   \
+    if (ET <= 1)              \
+        ROUTER_LAUNCH(1, L);  \
+    else if (ET <= 2)         \
+        ROUTER_LAUNCH(2, L);  \
+    else if (ET <= 4)         \
+        ROUTER_LAUNCH(4, L);  \
+    else                      \
+        ROUTER_LAUNCH(8, L);
+    if (local) {
+        ROUTER_LAUNCH_ET(true)
+    } else {
+        ROUTER_LAUNCH_ET(false)
+    }
+#undef ROUTER_LAUNCH_ET
+#undef ROUTER_LAUNCH
     return hipGetLastError();
 }
 

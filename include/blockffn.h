@@ -66,13 +66,26 @@ typedef enum { BLOCKFFN_F32 = 0, BLOCKFFN_BF16 = 1 } blockffn_dtype_t;
  *   eps     RMSNorm epsilon (torch's default for fp32 is 1.1920929e-07)
  *   scores  [T, E] float, written   post-RMSNorm scores (exactly 0 when inactive)
  *   logits  [T, E] float or NULL    pre-ReLU logits, written when given
+ *   workspace, workspace_bytes      optional device scratch (NULL, 0 = none). With a
+ *           workspace of at least blockffn_router_workspace_bytes(...) bytes,
+ *           ZERO-FILLED before its first use, a bf16 call with few tokens splits the
+ *           d_h sum over several workgroups (fixed summation order, so results do
+ *           not depend on timing). The workspace holds arrival counters that every
+ *           call returns to zero; calls that may run concurrently need separate
+ *           workspaces. Without one the call uses one workgroup per 32 tokens.
  * ReLU maps every logit that is not > 0 (NaN included) to 0. A row with no positive
  * logit gets all-zero scores.
  */
 blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *gain,
                                   const float *bias, float eps, int64_t T, int64_t d_h,
                                   int64_t E, int dtype, float *scores, float *logits,
-                                  void *stream);
+                                  void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Bytes of router workspace for these sizes (>= 256; 0 when the sizes are invalid,
+ * see blockffn_last_error()).
+ */
+size_t blockffn_router_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int dtype);
 
 /*
  * Bytes of device workspace blockffn_chunk_ffn needs for these sizes (0 when the

@@ -55,9 +55,9 @@ def ffn(lib, x=FAKE, scores=FAKE, w1=FAKE, w2=FAKE, T=32, d_h=2048, E=64, d_e=12
 
 
 def router(lib, x=FAKE, w_r=FAKE, gain=None, bias=None, eps=1e-6, T=32, d_h=2048, E=64,
-           dtype=1, scores=FAKE, logits=None):
+           dtype=1, scores=FAKE, logits=None, ws=None, ws_bytes=0):
     return lib.blockffn_router(x, w_r, gain, bias, eps, T, d_h, E, dtype, scores, logits,
-                               None)
+                               ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -84,10 +84,22 @@ def test_fp32_accepts_unaligned_sizes_but_checks_workspace(lib):
     (dict(x=None), 1), (dict(w_r=None), 1), (dict(scores=None), 1), (dict(T=0), 1),
     (dict(dtype=-1), 1), (dict(eps=-1.0), 1), (dict(eps=float("nan")), 1),
     (dict(E=300), 2), (dict(d_h=100), 2), (dict(x=FAKE_ODD), 2),
-    (dict(scores=FAKE_ODD), 2),
+    (dict(scores=FAKE_ODD), 2), (dict(ws=FAKE + 4, ws_bytes=1 << 30), 2),
+    (dict(ws=FAKE, ws_bytes=0), 3), (dict(ws=FAKE, ws_bytes=255), 3),
 ])
 def test_router_rejects(lib, kw, status):
     assert router(lib, **kw) == status
+
+
+def test_router_workspace_query(lib):
+    f = lib.blockffn_router_workspace_bytes
+    # decode: the d_h sum is split, partial logits of every split need room
+    assert f(32, 2048, 64, 1) >= 8 * 32 * 64 * 4
+    # many tokens or fp32: no split, the minimum size
+    assert f(1 << 16, 2048, 64, 1) == 256
+    assert f(32, 2048, 64, 0) == 256
+    assert f(0, 2048, 64, 1) == 0
+    assert f(32, 2048, 999, 1) == 0
 
 
 def test_workspace_query(lib):

@@ -236,14 +236,19 @@ def test_small_workspace_rejected():
 
 # ------------------------------------------------------------------ router
 
-def run_router(inp, use_gain=True, use_bias=True, logits=True):
+def router_ws(inp):
+    code = bf.BLOCKFFN_BF16 if inp.dtype == "bf16" else bf.BLOCKFFN_F32
+    return bf.blockffn_router_workspace(inp.T, inp.d_h, inp.w_r.shape[0], code, DEV)
+
+
+def run_router(inp, use_gain=True, use_bias=True, logits=True, workspace=None):
     dt = wdtype(inp)
     T, E = inp.T, inp.w_r.shape[0]
     lg = torch.empty((T, E), dtype=torch.float32, device=DEV) if logits else None
     s = bf.blockffn_router(dev(inp.x, dt), dev(inp.w_r, dt),
                            dev(inp.gain) if (use_gain and inp.gain is not None) else None,
                            dev(inp.bias) if (use_bias and inp.bias is not None) else None,
-                           logits=lg)
+                           logits=lg, workspace=workspace)
     torch.cuda.synchronize()
     return s.cpu().numpy(), (lg.cpu().numpy() if logits else None)
 
@@ -272,6 +277,24 @@ def test_router_e2e_full():
     s, lg = run_router(inp)
     check_router(inp, s, lg)
     assert abs((s == 0).mean() - 0.8) < 0.02
+    s2, lg2 = run_router(inp, workspace=router_ws(inp))
+    check_router(inp, s2, lg2)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("T", [1, 32, 100, 2048])
+def test_router_split_sum(T):
+    """Few tokens: the d_h sum is split over workgroups (with a workspace); the
+    result matches the oracle and, bit for bit, a second call on the same
+    workspace (the counters returned to zero, the split order is fixed)."""
+    inp = inputs.make_workload("e2e", seed=11, T=T)
+    ws = router_ws(inp)
+    s, lg = run_router(inp, workspace=ws)
+    check_router(inp, s, lg)
+    ctrl = ws[:4096].cpu().numpy()
+    assert not ctrl.any()
+    s2, lg2 = run_router(inp, workspace=ws)
+    assert np.array_equal(s, s2) and np.array_equal(lg, lg2)
 
 
 def test_router_tiny_f32():
