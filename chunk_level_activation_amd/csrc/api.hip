@@ -77,6 +77,20 @@ bool chunk1_grid(hipStream_t stream, int *xcds, int *wg_per_xcd)
     return true;
 }
 
+// The decode schedule's grid: xcds groups of `members` workgroups (one per CU).
+bool decode_grid(hipStream_t stream, const blockffn::FfnPlan &p, int *xcds, int *members)
+{
+    const DeviceInfo *d = device_info(stream);
+    if (!d || d->xcds <= 1 || blockffn::decode_blocks_per_cu() < 1)
+        return false;
+    const int m = d->cus / d->xcds;
+    if (!blockffn::decode_supported(p.CT, p.d_h, p.E, p.d_e, d->xcds, m))
+        return false;
+    *xcds = d->xcds;
+    *members = m;
+    return true;
+}
+
 blockffn_status_t fail(blockffn_status_t code, const std::string &msg)
 {
     g_last_error = msg;
@@ -236,8 +250,15 @@ blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const v
     const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
 
     hipError_t err;
-    int xcds = 0, wg_per_xcd = 0;
-    if (dtype == BLOCKFFN_BF16 && p.chunk1 && chunk1_grid(s, &xcds, &wg_per_xcd)) {
+    int xcds = 0, wg_per_xcd = 0, members = 0;
+    if (p.decode && decode_grid(s, p, &xcds, &members)) {
+        // one launch, one workgroup per CU: union, up- and down-projection
+        err = blockffn::launch_ffn_bf16_decode(
+            p, xcds, members, static_cast<const uint16_t *>(x), scores,
+            static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w2),
+            static_cast<uint16_t *>(y), workspace, union_masks_out, expert_lists_out,
+            union_counts_out, s);
+    } else if (dtype == BLOCKFFN_BF16 && p.chunk1 && chunk1_grid(s, &xcds, &wg_per_xcd)) {
         // one launch: union, up- and down-projection of a single chunk tile
         err = blockffn::launch_ffn_bf16_chunk1(
             p, xcds, wg_per_xcd, static_cast<const uint16_t *>(x), scores,

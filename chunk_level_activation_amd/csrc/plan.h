@@ -20,6 +20,20 @@ bool chunk1_supported(int64_t CT, int64_t d_h, int64_t d_e);
 size_t chunk1_partial_bytes(int64_t d_h, int64_t E, int64_t d_e);
 int chunk1_blocks_per_cu();
 
+// One-launch bf16 decode schedule, one workgroup per CU (ffn_bf16_decode.hip).
+// decode_shape(): sizes that may use it on some device (the workspace is sized for
+// it); decode_supported(): sizes usable with `xcds` groups of `members` workgroups.
+// Its counters start at this word of the control block.
+constexpr int64_t kDecodeControlWord = kControlWords / 2;
+inline bool decode_shape(int dtype, int64_t CT, int64_t d_h, int64_t d_e)
+{
+    return dtype == 1 && CT == 1 && d_h % 128 == 0 && d_h <= 2048 && d_e % 64 == 0 &&
+           d_e <= 128;
+}
+bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds, int members);
+size_t decode_scratch_bytes(int64_t d_h, int64_t d_e);
+int decode_blocks_per_cu();
+
 // Problem sizes plus everything derived from them that the kernels and the
 // workspace layout need. Built once per call by make_plan().
 struct FfnPlan {
@@ -31,6 +45,7 @@ struct FfnPlan {
     int64_t W;            // 64-bit mask words per chunk, ceil(E / 64)
     int64_t JT;           // 32-column tiles of d_h in the two-launch down-projection
     bool chunk1;          // sizes admit the one-launch single-tile bf16 schedule
+    bool decode;          // sizes may admit the one-workgroup-per-CU decode schedule
     // scratch after the control block (byte offsets)
     size_t off_masks, off_lists, off_counts;   // fp32 path union
     size_t off_hidden, off_partials;
@@ -52,6 +67,7 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     p.JT = (d_h + 31) / 32;
     p.chunk1 = dtype == 1 && chunk1_supported(p.CT, d_h, d_e) &&
                E * (d_e / 64 + 1) + kMaxGroups + d_h / 64 <= kControlWords;
+    p.decode = decode_shape(dtype, p.CT, d_h, d_e);
     const size_t helem = dtype == 1 ? 2 : 4;   // hidden activations: bf16 or fp32
     size_t off = kControlBytes;
     p.off_masks = off;    off = align_up(off + sizeof(uint64_t) * p.C * p.W, 256);
@@ -59,8 +75,12 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     p.off_counts = off;   off = align_up(off + sizeof(int32_t) * p.C, 256);
     p.off_hidden = off;   off = align_up(off + helem * p.CT * E * 32 * d_e, 256);
     p.off_partials = off;
+    size_t partials = 0;
     if (p.chunk1)
-        off = align_up(off + chunk1_partial_bytes(d_h, E, d_e), 256);
+        partials = chunk1_partial_bytes(d_h, E, d_e);
+    if (p.decode && decode_scratch_bytes(d_h, d_e) > partials)
+        partials = decode_scratch_bytes(d_h, d_e);
+    off = align_up(off + partials, 256);
     p.total_bytes = off;
     return p;
 }
@@ -80,6 +100,13 @@ hipError_t launch_ffn_bf16_chunk1(const FfnPlan &p, int xcds, int wg_per_xcd,
                                   const uint16_t *w2, uint16_t *y, void *ws,
                                   uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,
                                   hipStream_t stream);
+// One launch for a single chunk tile of at most 32 tokens: `xcds` groups of `members`
+// workgroups, one per CU, group g on XCD g (requires round-robin placement and every
+// workgroup resident at once).
+hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const uint16_t *x,
+                                  const float *scores, const uint16_t *w1, const uint16_t *w2,
+                                  uint16_t *y, void *ws, uint64_t *masks_out,
+                                  int32_t *lists_out, int32_t *counts_out, hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnPlan &p, const float *x, const float *scores,
                           const float *w1, const float *w2, float *y, void *ws,
                           hipStream_t stream);

@@ -69,6 +69,16 @@ __device__ __forceinline__ void st_counter(uint32_t *p, uint32_t v)
 {
     __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// Flags shared only by workgroups of one XCD: the producer stores with sc0 (the value
+// lands in the XCD's L2) and consumers read with a device-scope load (sc1), which is
+// answered from that L2 in about 0.3 us. A plain or sc0 load may instead be served by
+// a stale L1 copy of the line indefinitely, and a device-scope (write-through) store
+// takes several times longer to become visible (measured on MI355X).
+__device__ __forceinline__ void xcd_flag_store(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v)
+{
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, kSC0);
+}
+
 // Wait until every memory access this wave issued has completed.
 __device__ __forceinline__ void drain_memory()
 {

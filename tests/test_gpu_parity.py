@@ -108,6 +108,74 @@ def test_large_layer_sweep_sampled(tls, cls, dense):
     assert rel_err(y[rows], y_ref) <= TOL_BF16
 
 
+# ------------------------------------------------------------------ decode schedule
+
+DECODE = [
+    # (label, T, E, d_h, d_e, tls, cls, dense): single chunks of <= 32 tokens
+    ("T=32 E=64", 32, 64, 2048, 128, 0.8, 0.7, False),
+    ("one token", 1, 64, 2048, 128, 0.8, 0.7, False),
+    ("T=5", 5, 64, 2048, 128, 0.8, 0.7, False),
+    ("T=31", 31, 64, 2048, 128, 0.8, 0.7, False),
+    ("all experts active", 32, 64, 2048, 128, 0.8, 0.7, True),
+    ("d_e=64", 32, 64, 2048, 64, 0.8, 0.7, False),
+    ("d_h=1024", 32, 64, 1024, 128, 0.8, 0.7, False),
+    ("d_h=128", 32, 64, 128, 128, 0.8, 0.7, False),
+    ("E=8", 32, 8, 2048, 128, 0.5, 0.3, False),
+    ("E=1", 32, 1, 2048, 128, 0.5, 0.3, False),
+    ("E=40", 32, 40, 2048, 128, 0.8, 0.7, False),
+    # sizes outside the one-workgroup-per-CU schedule (other single-chunk paths)
+    ("d_h=4096", 32, 64, 4096, 128, 0.8, 0.7, False),
+    ("E=128", 32, 128, 2048, 128, 0.8, 0.7, False),
+    ("d_e=256", 32, 32, 2048, 256, 0.8, 0.7, False),
+]
+
+
+@pytest.mark.parametrize("label,T,E,d_h,d_e,tls,cls,dense", DECODE,
+                         ids=[d[0] for d in DECODE])
+def test_decode_shapes(label, T, E, d_h, d_e, tls, cls, dense):
+    inp = inputs.make_workload("decode", seed=21, T=T, E=E, d_h=d_h, d_e=d_e, tls=tls,
+                               cls=cls, dense=dense)
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, inp.n, masks, lists, counts)
+    y_ref = oracle.chunk_ffn(inp.x, inp.scores, inp.w1, inp.w2, inp.n)
+    assert rel_err(y, y_ref) <= TOL_BF16, label
+
+
+def test_decode_all_zero_scores_give_zero():
+    inp = inputs.make_workload("decode", seed=22)
+    s = np.zeros_like(inp.scores)
+    s[3, 9] = -0.0
+    y, masks, lists, counts = run_ffn(inp, scores=s)
+    assert counts.tolist() == [0] and np.all(masks == 0) and np.all(lists == -1)
+    assert np.all(y == 0)
+
+
+def test_decode_single_active_entry():
+    inp = inputs.make_workload("decode", seed=23)
+    s = np.zeros_like(inp.scores)
+    s[17, 42] = 0.75
+    y, _, lists, counts = run_ffn(inp, scores=s)
+    assert counts.tolist() == [1] and lists[0, 0] == 42
+    assert np.all(y[np.arange(32) != 17] == 0)
+    y_ref = oracle.chunk_ffn(inp.x, s, inp.w1, inp.w2, 32)
+    assert rel_err(y, y_ref) <= TOL_BF16
+
+
+def test_decode_experts_outside_union_are_never_read():
+    inp = inputs.make_workload("decode", seed=24, tls=0.9, cls=0.85)
+    _, _, c_ref = oracle.chunk_union(inp.scores, 32)
+    used = np.any(inp.scores != 0, axis=0)
+    assert 0 < c_ref[0] < 64
+    y, *_ = run_ffn(inp)
+    inp.w1 = inp.w1.copy()
+    inp.w2 = inp.w2.copy()
+    inp.w1[~used] = np.nan
+    inp.w2[~used] = np.nan
+    yn, *_ = run_ffn(inp)
+    assert np.all(np.isfinite(yn))
+    assert np.array_equal(y, yn)
+
+
 # ------------------------------------------------------------------ edge cases
 
 def small(dtype, T, n, E=16, d_h=64, d_e=32, tls=0.8, cls=0.6, seed=0):
