@@ -265,6 +265,12 @@ blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const v
             static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w2),
             static_cast<uint16_t *>(y), workspace, union_masks_out, expert_lists_out,
             union_counts_out, s);
+    } else if (p.grouped) {
+        // several chunk tiles: each union expert's weights read once per launch
+        err = blockffn::launch_ffn_bf16_grouped(
+            p, static_cast<const uint16_t *>(x), scores, static_cast<const uint16_t *>(w1),
+            static_cast<const uint16_t *>(w2), static_cast<uint16_t *>(y), workspace,
+            union_masks_out, expert_lists_out, union_counts_out, s);
     } else if (dtype == BLOCKFFN_BF16) {
         err = blockffn::launch_ffn_bf16(p, static_cast<const uint16_t *>(x), scores,
                                         static_cast<const uint16_t *>(w1),

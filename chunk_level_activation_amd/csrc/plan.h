@@ -34,6 +34,11 @@ bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds,
 size_t decode_scratch_bytes(int64_t d_h, int64_t d_e);
 int decode_blocks_per_cu();
 
+// Expert-grouped multi-chunk bf16 schedule (ffn_bf16_grouped.hip): sizes it takes and
+// the bytes of its per-expert tile lists.
+bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_e);
+size_t grouped_tile_bytes(int64_t CT, int64_t E);
+
 // Problem sizes plus everything derived from them that the kernels and the
 // workspace layout need. Built once per call by make_plan().
 struct FfnPlan {
@@ -46,9 +51,10 @@ struct FfnPlan {
     int64_t JT;           // 32-column tiles of d_h in the two-launch down-projection
     bool chunk1;          // sizes admit the one-launch single-tile bf16 schedule
     bool decode;          // sizes may admit the one-workgroup-per-CU decode schedule
+    bool grouped;         // sizes admit the expert-grouped multi-chunk schedule
     // scratch after the control block (byte offsets)
     size_t off_masks, off_lists, off_counts;   // fp32 path union
-    size_t off_hidden, off_partials;
+    size_t off_hidden, off_partials, off_tiles;
     size_t total_bytes;
 };
 
@@ -68,6 +74,7 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     p.chunk1 = dtype == 1 && chunk1_supported(p.CT, d_h, d_e) &&
                E * (d_e / 64 + 1) + kMaxGroups + d_h / 64 <= kControlWords;
     p.decode = decode_shape(dtype, p.CT, d_h, d_e);
+    p.grouped = dtype == 1 && grouped_supported(T, p.CT, d_h, E, d_e);
     const size_t helem = dtype == 1 ? 2 : 4;   // hidden activations: bf16 or fp32
     size_t off = kControlBytes;
     p.off_masks = off;    off = align_up(off + sizeof(uint64_t) * p.C * p.W, 256);
@@ -81,6 +88,9 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     if (p.decode && decode_scratch_bytes(d_h, d_e) > partials)
         partials = decode_scratch_bytes(d_h, d_e);
     off = align_up(off + partials, 256);
+    p.off_tiles = off;
+    if (p.grouped)
+        off = align_up(off + grouped_tile_bytes(p.CT, E), 256);
     p.total_bytes = off;
     return p;
 }
@@ -107,6 +117,12 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
                                   const float *scores, const uint16_t *w1, const uint16_t *w2,
                                   uint16_t *y, void *ws, uint64_t *masks_out,
                                   int32_t *lists_out, int32_t *counts_out, hipStream_t stream);
+// Four launches: union, per-expert tile lists, expert-grouped up-projection,
+// tile-pair x column-tile down-projection.
+hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const float *scores,
+                                   const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *ws,
+                                   uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,
+                                   hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnPlan &p, const float *x, const float *scores,
                           const float *w1, const float *w2, float *y, void *ws,
                           hipStream_t stream);

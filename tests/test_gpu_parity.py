@@ -176,6 +176,57 @@ def test_decode_experts_outside_union_are_never_read():
     assert np.array_equal(y, yn)
 
 
+# ------------------------------------------------------------------ multi-chunk schedule
+
+GROUPED = [
+    # (label, T, n, E, d_h, d_e, dense): several chunk tiles, full check against the oracle
+    ("T=256 n=32", 256, 32, 64, 2048, 128, False),
+    ("T=100 n=48 partial tiles", 100, 48, 64, 2048, 128, False),
+    ("n=64 two tiles per chunk", 256, 64, 64, 2048, 128, False),
+    ("n=128", 256, 128, 64, 1024, 128, False),
+    ("n=8", 128, 8, 64, 1024, 128, False),
+    ("d_e=256", 96, 32, 40, 1024, 256, False),
+    ("E=40", 160, 32, 40, 2048, 128, False),
+    ("E=128", 96, 32, 128, 512, 128, False),
+    ("d_h=256", 64, 32, 16, 256, 128, False),
+    ("all experts active", 64, 32, 64, 1024, 128, True),
+]
+
+
+@pytest.mark.parametrize("label,T,n,E,d_h,d_e,dense", GROUPED, ids=[g[0] for g in GROUPED])
+def test_multichunk_shapes(label, T, n, E, d_h, d_e, dense):
+    inp = inputs.make_workload("prefill", seed=31, T=T, n=n, E=E, d_h=d_h, d_e=d_e,
+                               dense=dense)
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, n, masks, lists, counts)
+    y_ref = oracle.chunk_ffn(inp.x, inp.scores, inp.w1, inp.w2, n)
+    assert rel_err(y, y_ref) <= TOL_BF16, label
+
+
+def test_multichunk_zero_single_and_outside_union():
+    """All-zero scores give y = 0; one active entry touches only its token; NaN weights
+    on experts outside every union are never read."""
+    inp = inputs.make_workload("prefill", seed=32, T=192, d_h=1024, tls=0.9, cls=0.85)
+    s = np.zeros_like(inp.scores)
+    s[7, 3] = -0.0
+    y, _, lists, counts = run_ffn(inp, scores=s)
+    assert np.all(counts == 0) and np.all(lists == -1) and np.all(y == 0)
+    s[100, 11] = 2.5
+    y, _, lists, counts = run_ffn(inp, scores=s)
+    assert counts.tolist() == [0, 0, 0, 1, 0, 0] and lists[3, 0] == 11
+    assert np.all(y[np.arange(192) != 100] == 0)
+    assert rel_err(y, oracle.chunk_ffn(inp.x, s, inp.w1, inp.w2, 32)) <= TOL_BF16
+    used = np.any(inp.scores != 0, axis=0)
+    assert not used.all()
+    y, *_ = run_ffn(inp)
+    inp.w1 = inp.w1.copy()
+    inp.w2 = inp.w2.copy()
+    inp.w1[~used] = np.nan
+    inp.w2[~used] = np.nan
+    yn, *_ = run_ffn(inp)
+    assert np.all(np.isfinite(yn)) and np.array_equal(y, yn)
+
+
 # ------------------------------------------------------------------ edge cases
 
 def small(dtype, T, n, E=16, d_h=64, d_e=32, tls=0.8, cls=0.6, seed=0):
