@@ -41,6 +41,9 @@ constexpr int kDnTiles = 2;               // chunk tiles per down workgroup
 constexpr int kDnRows = kDnTiles * kTileM;    // 64
 constexpr int kDnCols = 256;              // output columns per down workgroup
 constexpr int kMaxWords = 4;
+constexpr int kDepth = 4;                 // down: k steps whose loads are in flight ahead of use
+// A buffer offset beyond every range used here: the load returns zero, no memory access.
+constexpr uint32_t kOutOfRange = 0x80000000u;
 
 struct GroupedArgs {
     const uint16_t *x;
@@ -270,46 +273,57 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
         for (int v = 0; v < 16; ++v)
             acc[j][v] = 0.0f;
 
-    auto load_step = [&](int s, bf16x8 &ra, bf16x8 (&rb)[4]) {
-        const int e = list[s / DK];
-        const int k0 = (s % DK) * kKStep;
-        const bool use = a_tile >= 0 && ((m_tile[a_tile_i][e >> 6] >> (e & 63)) & 1ull);
-        ra = use ? bload<0>(rhid, (uint32_t)(((((int64_t)a_tile * a.E + e) * kTileM + a_r) * a.d_e +
-                                               k0 + acol) *
-                                              2))
-                 : zero_bf16x8();
+    // kDepth k steps in flight: every load is issued (a tile whose chunk does not use
+    // the expert, and steps past the end, read beyond the buffer and get zero)
+    bf16x8 ra[kDepth], rb[kDepth][4];
+    auto issue = [&](int st, int d) {
+        // branch-free: the list entry is read even past the end (masked to a valid
+        // expert index) and the offsets are replaced afterwards
+        const bool ok = st < steps;
+        const int li = st / DK;
+        const int e = list[li < 255 ? li : 255] & 255;
+        const int k0 = (st - li * DK) * kKStep;
+        const bool use = ok && a_tile >= 0 && ((m_tile[a_tile_i][e >> 6] >> (e & 63)) & 1ull);
+        const uint32_t aoffs =
+            (uint32_t)((((a_tile * a.E + e) * kTileM + a_r) * a.d_e + k0 + acol) * 2);
+        ra[d] = bload<0>(rhid, use ? aoffs : kOutOfRange);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = tid + i * kGThreads;
             const int r = q >> 3, c8 = (q & 7) * 8;
-            rb[i] = bload<kNT>(rw2, (uint32_t)((((int64_t)e * a.d_h + ct * kDnCols + r) * a.d_e + k0 +
-                                                c8) *
-                                               2));
+            const uint32_t boffs =
+                (uint32_t)(((e * a.d_h + ct * kDnCols + r) * a.d_e + k0 + c8) * 2);
+            rb[d][i] = bload<kNT>(rw2, ok ? boffs : kOutOfRange);
         }
     };
-    bf16x8 ra, rb[4];
-    if (steps > 0)
-        load_step(0, ra, rb);
-    for (int s = 0; s < steps; ++s) {
-        const int buf = s & 1;
-        *reinterpret_cast<bf16x8 *>(&As[buf][arow * kPitch + acol]) = ra;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int q = tid + i * kGThreads;
-            *reinterpret_cast<bf16x8 *>(&Bs[buf][(q >> 3) * kPitch + (q & 7) * 8]) = rb[i];
-        }
-        __syncthreads();
-        if (s + 1 < steps)
-            load_step(s + 1, ra, rb);
+    for (int d = 0; d < kDepth; ++d)
+        issue(d, d);
+    for (int s0 = 0; s0 < steps; s0 += kDepth) {
 #pragma unroll
-        for (int ks = 0; ks < kKStep / 16; ++ks) {
-            const bf16x8 fa =
-                *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * 32 + col) * kPitch + ks * 16 + kg * 8]);
+        for (int d = 0; d < kDepth; ++d) {
+            const int st = s0 + d;
+            if (st >= steps)
+                break;
+            const int buf = st & 1;
+            *reinterpret_cast<bf16x8 *>(&As[buf][arow * kPitch + acol]) = ra[d];
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
-                    &Bs[buf][(wn * 64 + j * 32 + col) * kPitch + ks * 16 + kg * 8]);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
+            for (int i = 0; i < 4; ++i) {
+                const int q = tid + i * kGThreads;
+                *reinterpret_cast<bf16x8 *>(&Bs[buf][(q >> 3) * kPitch + (q & 7) * 8]) = rb[d][i];
+            }
+            __syncthreads();
+            issue(st + kDepth, d);
+#pragma unroll
+            for (int ks = 0; ks < kKStep / 16; ++ks) {
+                const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
+                    &As[buf][(wm * 32 + col) * kPitch + ks * 16 + kg * 8]);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
+                        &Bs[buf][(wn * 64 + j * 32 + col) * kPitch + ks * 16 + kg * 8]);
+                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
+                }
             }
         }
     }
