@@ -1,4 +1,5 @@
-"""CPU oracle for the BlockFFN layer forward (router + chunk-union expert FFN).
+"""CPU oracle for the BlockFFN layer forward (router + chunk-union expert FFN), its
+residual + LayerNorm epilogue and the two sparsity training losses with gradients.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg use this package; the GPU library never imports, links or calls it,
@@ -11,7 +12,9 @@ Pages followed (BlockFFN, arXiv 2507.08771):
     Deployment": "Core Concept" (union of active experts over n tokens, masking after
     the computation), "Architecture Overview" (ReLU + RMSNorm router, non-gated Swish
     experts), "Router Architecture Setup" (no router bias, RMSNorm over experts),
-    "Chunk Sparsification Loss" (aligned chunks, ceil(S/L) of them).
+    "Chunk Sparsification Loss" (aligned chunks, ceil(S/L) of them), "Activation
+    Locality Loss" (BCE of adjacent sharpened patterns), "Full BlockFFN Layer with
+    Combined Losses" (LayerNorm of expert output plus residual).
   * paper card, Abstract: TLS and 8-token CLS as the sparsity measures.
 """
 from __future__ import annotations
@@ -75,6 +78,19 @@ def _bind(lib):
     lib.oracle_chunk_ffn.restype = None
     lib.oracle_token_ffn.argtypes = [P, P, P, P, I64, I64, I64, I64, P, P]
     lib.oracle_token_ffn.restype = None
+    D = ctypes.c_double
+    lib.oracle_router_probs.argtypes = [P, I64, D, P]
+    lib.oracle_router_probs.restype = None
+    lib.oracle_add_layernorm.argtypes = [P, P, P, P, D, I64, I64, P]
+    lib.oracle_add_layernorm.restype = None
+    lib.oracle_locality_loss.argtypes = [P, I64, I64, I64, D]
+    lib.oracle_locality_loss.restype = D
+    lib.oracle_chunk_sparsification_loss.argtypes = [P, I64, I64, I64, I64]
+    lib.oracle_chunk_sparsification_loss.restype = D
+    lib.oracle_locality_loss_grad.argtypes = [P, I64, I64, I64, D, P]
+    lib.oracle_locality_loss_grad.restype = None
+    lib.oracle_chunk_sparsification_loss_grad.argtypes = [P, I64, I64, I64, I64, P]
+    lib.oracle_chunk_sparsification_loss_grad.restype = None
     _lib = lib
     return lib
 
@@ -156,6 +172,62 @@ def token_ffn(x, scores, w1, w2) -> np.ndarray:
     lib.oracle_token_ffn(_ptr(x), _ptr(scores), _ptr(w1), _ptr(w2), T, d_h, E, d_e,
                          _ptr(y), _ptr(h))
     return y
+
+
+# Layer epilogue and the training losses (skill page: "Router Architecture Setup",
+# "Full BlockFFN Layer with Combined Losses", "Activation Locality Loss", "Chunk
+# Sparsification Loss"). Probabilities are [B, S, E] (a [S, E] array is one batch).
+
+def router_probs(scores, sharpness: float = 1.0) -> np.ndarray:
+    """float64 sigmoid(sharpness * scores), same shape."""
+    s = np.ascontiguousarray(scores, dtype=np.float64)
+    out = np.empty_like(s)
+    _load().oracle_router_probs(_ptr(s), s.size, float(sharpness), _ptr(out))
+    return out
+
+
+def add_layernorm(y, x, gamma=None, beta=None, eps: float = 1e-5) -> np.ndarray:
+    """float64 LayerNorm(y + x) over the last axis; y, x [T, d]; gamma/beta [d]."""
+    y, x = _f32(y), _f32(x)
+    T, d = x.shape
+    assert y.shape == (T, d)
+    gamma = None if gamma is None else _f32(gamma)
+    beta = None if beta is None else _f32(beta)
+    out = np.empty((T, d), np.float64)
+    _load().oracle_add_layernorm(_ptr(y), _ptr(x), _ptr(gamma), _ptr(beta), float(eps),
+                                 T, d, _ptr(out))
+    return out
+
+
+def _bse(p):
+    p = _f32(p)
+    if p.ndim == 2:
+        p = p[None]
+    return p, p.shape
+
+
+def locality_loss(p, alpha: float = 2.0) -> float:
+    p, (B, S, E) = _bse(p)
+    return float(_load().oracle_locality_loss(_ptr(p), B, S, E, float(alpha)))
+
+
+def chunk_sparsification_loss(p, L: int = 8) -> float:
+    p, (B, S, E) = _bse(p)
+    return float(_load().oracle_chunk_sparsification_loss(_ptr(p), B, S, E, int(L)))
+
+
+def locality_loss_grad(p, alpha: float = 2.0) -> np.ndarray:
+    p, (B, S, E) = _bse(p)
+    g = np.empty((B, S, E), np.float64)
+    _load().oracle_locality_loss_grad(_ptr(p), B, S, E, float(alpha), _ptr(g))
+    return g
+
+
+def chunk_sparsification_loss_grad(p, L: int = 8) -> np.ndarray:
+    p, (B, S, E) = _bse(p)
+    g = np.empty((B, S, E), np.float64)
+    _load().oracle_chunk_sparsification_loss_grad(_ptr(p), B, S, E, int(L), _ptr(g))
+    return g
 
 
 # --------------------------------------------------------------------------------

@@ -24,6 +24,11 @@
  *  [S4] same page, "Chunk Sparsification Loss": chunks are consecutive, aligned,
  *       ceil(S/L) of them, the last one possibly partial.
  *  [S5] paper card (sota2), Abstract: a router integrating ReLU and RMSNorm.
+ *  [S6] skill page, "Full BlockFFN Layer with Combined Losses": the layer output is
+ *       a LayerNorm over d_h of (expert output + x); the router also returns
+ *       probabilities sigmoid(sharpness * score) ("Router Architecture Setup").
+ *  [S7] skill page, "Activation Locality Loss": binary cross entropy between the
+ *       sigmoid-sharpened activation patterns of adjacent tokens.
  *
  * Readings where the pages are silent (each is also listed in the design notes):
  *  - Experts carry no biases and dropout is the identity (inference).
@@ -213,4 +218,150 @@ void oracle_token_ffn(const float *x, const float *scores, const float *w1,
                                   (double)s, d_h, d_e, h, yt);
         }
     }
+}
+
+/*
+ * Router probabilities, [S6] / [S3]: p = sigmoid(sharpness * s), elementwise over n
+ * scores (the pages' default sharpness is 1).
+ */
+void oracle_router_probs(const double *scores, int64_t n, double sharpness, double *probs)
+{
+    for (int64_t i = 0; i < n; ++i)
+        probs[i] = 1.0 / (1.0 + exp(-sharpness * scores[i]));
+}
+
+/*
+ * Residual + LayerNorm, [S6]: out[t,:] = LayerNorm(y[t,:] + x[t,:]) over the d axis,
+ *   v = y + x,  mean = (1/d) sum_j v_j,  var = (1/d) sum_j (v_j - mean)^2  (biased),
+ *   out_j = (v_j - mean) / sqrt(var + eps) * gamma_j + beta_j
+ * (nn.LayerNorm's definition; gamma/beta NULL mean ones/zeros).
+ */
+void oracle_add_layernorm(const float *y, const float *x, const float *gamma,
+                          const float *beta, double eps, int64_t T, int64_t d, double *out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        double mean = 0.0;
+        for (int64_t j = 0; j < d; ++j)
+            mean += (double)y[t * d + j] + (double)x[t * d + j];
+        mean /= (double)d;
+        double var = 0.0;
+        for (int64_t j = 0; j < d; ++j) {
+            double v = (double)y[t * d + j] + (double)x[t * d + j] - mean;
+            var += v * v;
+        }
+        var /= (double)d;
+        double inv = 1.0 / sqrt(var + eps);
+        for (int64_t j = 0; j < d; ++j) {
+            double v = (double)y[t * d + j] + (double)x[t * d + j] - mean;
+            out[t * d + j] = v * inv * (gamma ? (double)gamma[j] : 1.0) +
+                             (beta ? (double)beta[j] : 0.0);
+        }
+    }
+}
+
+/* Sigmoid sharpening of [S7]: sigmoid(alpha * (2p - 1)). */
+static double sharpen(double p, double alpha)
+{
+    return 1.0 / (1.0 + exp(-alpha * (2.0 * p - 1.0)));
+}
+
+#define LOSS_LOG_EPS 1e-8
+
+/*
+ * Activation locality loss, [S7], over probabilities p[B][S][E]:
+ *   q = sharpen(p);  for i = 0 .. S-2:
+ *     bce_i = mean over (b, e) of -( q[b,i,e] log(q[b,i+1,e] + 1e-8)
+ *                                    + (1 - q[b,i,e]) log(1 - q[b,i+1,e] + 1e-8) )
+ *   loss = (sum_i bce_i) / max(S - 1, 1)
+ */
+double oracle_locality_loss(const float *p, int64_t B, int64_t S, int64_t E, double alpha)
+{
+    double loss = 0.0;
+    for (int64_t i = 0; i + 1 < S; ++i) {
+        double sum = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t e = 0; e < E; ++e) {
+                double c = sharpen(p[(b * S + i) * E + e], alpha);
+                double nx = sharpen(p[(b * S + i + 1) * E + e], alpha);
+                sum += -(c * log(nx + LOSS_LOG_EPS) + (1.0 - c) * log(1.0 - nx + LOSS_LOG_EPS));
+            }
+        loss += sum / (double)(B * E);
+    }
+    return loss / (double)(S - 1 > 1 ? S - 1 : 1);
+}
+
+/*
+ * Chunk sparsification loss, [S4], over p[B][S][E] and chunks of L tokens (aligned,
+ * ceil(S/L) of them, the last possibly partial):
+ *   per chunk: mean over (b, e) of 1 - prod_{k in chunk} (1 - p[b,k,e])
+ *   loss = (sum over chunks) / ceil(S/L)
+ */
+double oracle_chunk_sparsification_loss(const float *p, int64_t B, int64_t S, int64_t E,
+                                        int64_t L)
+{
+    const int64_t nc = (S + L - 1) / L;
+    double loss = 0.0;
+    for (int64_t c = 0; c < nc; ++c) {
+        const int64_t t0 = c * L, t1 = t0 + L < S ? t0 + L : S;
+        double sum = 0.0;
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t e = 0; e < E; ++e) {
+                double none = 1.0;
+                for (int64_t k = t0; k < t1; ++k)
+                    none *= 1.0 - (double)p[(b * S + k) * E + e];
+                sum += 1.0 - none;
+            }
+        loss += sum / (double)(B * E);
+    }
+    return loss / (double)nc;
+}
+
+/*
+ * Gradient of oracle_locality_loss with respect to p (same layout), by the chain
+ * rule on its definition: with q = sharpen(p), dq/dp = 2 alpha q (1 - q), and for
+ * the pair (i, i+1) of one (b, e):
+ *   d bce_i / d q_i     = -( log(q_{i+1} + eps) - log(1 - q_{i+1} + eps) )
+ *   d bce_i / d q_{i+1} = -( q_i / (q_{i+1} + eps) - (1 - q_i) / (1 - q_{i+1} + eps) )
+ * each scaled by 1 / (B E max(S - 1, 1)).
+ */
+void oracle_locality_loss_grad(const float *p, int64_t B, int64_t S, int64_t E,
+                               double alpha, double *grad)
+{
+    const double scale = 1.0 / ((double)(B * E) * (double)(S - 1 > 1 ? S - 1 : 1));
+    for (int64_t i = 0; i < B * S * E; ++i)
+        grad[i] = 0.0;
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t i = 0; i + 1 < S; ++i)
+            for (int64_t e = 0; e < E; ++e) {
+                const int64_t a0 = (b * S + i) * E + e, a1 = (b * S + i + 1) * E + e;
+                double c = sharpen(p[a0], alpha), nx = sharpen(p[a1], alpha);
+                double dc = -(log(nx + LOSS_LOG_EPS) - log(1.0 - nx + LOSS_LOG_EPS));
+                double dn = -(c / (nx + LOSS_LOG_EPS) - (1.0 - c) / (1.0 - nx + LOSS_LOG_EPS));
+                grad[a0] += scale * dc * 2.0 * alpha * c * (1.0 - c);
+                grad[a1] += scale * dn * 2.0 * alpha * nx * (1.0 - nx);
+            }
+}
+
+/*
+ * Gradient of oracle_chunk_sparsification_loss with respect to p: the chunk term
+ * 1 - prod_k (1 - p_k) has derivative prod_{j != k} (1 - p_j) in p_k; scaled by
+ * 1 / (B E ceil(S/L)).
+ */
+void oracle_chunk_sparsification_loss_grad(const float *p, int64_t B, int64_t S, int64_t E,
+                                           int64_t L, double *grad)
+{
+    const int64_t nc = (S + L - 1) / L;
+    const double scale = 1.0 / ((double)(B * E) * (double)nc);
+    for (int64_t b = 0; b < B; ++b)
+        for (int64_t c = 0; c < nc; ++c) {
+            const int64_t t0 = c * L, t1 = t0 + L < S ? t0 + L : S;
+            for (int64_t e = 0; e < E; ++e)
+                for (int64_t k = t0; k < t1; ++k) {
+                    double others = 1.0;
+                    for (int64_t j = t0; j < t1; ++j)
+                        if (j != k)
+                            others *= 1.0 - (double)p[(b * S + j) * E + e];
+                    grad[(b * S + k) * E + e] = scale * others;
+                }
+        }
 }

@@ -9,6 +9,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_loss_pins as lpins
 import test_oracle_pins as pins
 
 # (name, text in the source, planted replacement)
@@ -45,6 +46,32 @@ MUTATIONS = [
      "                              (double)scores[t * E + e], d_h, d_e, h, yt);",
      "add_expert_output(x + t * d_h, w1 + e * d_e * d_h, w2,\n"
      "                              (double)scores[t * E + e], d_h, d_e, h, yt);"),
+    ("probs ignore sharpness", "probs[i] = 1.0 / (1.0 + exp(-sharpness * scores[i]));",
+     "probs[i] = 1.0 / (1.0 + exp(-scores[i]));"),
+    ("layernorm unbiased variance", "var /= (double)d;", "var /= (double)(d - 1);"),
+    ("layernorm eps outside sqrt", "double inv = 1.0 / sqrt(var + eps);",
+     "double inv = 1.0 / (sqrt(var) + eps);"),
+    ("layernorm beta dropped", "(beta ? (double)beta[j] : 0.0);", "0.0;"),
+    ("layernorm residual dropped",
+     "mean += (double)y[t * d + j] + (double)x[t * d + j];", "mean += (double)y[t * d + j];"),
+    ("sharpening without the 2p - 1", "return 1.0 / (1.0 + exp(-alpha * (2.0 * p - 1.0)));",
+     "return 1.0 / (1.0 + exp(-alpha * p));"),
+    ("locality bce target and input swapped",
+     "sum += -(c * log(nx + LOSS_LOG_EPS) + (1.0 - c) * log(1.0 - nx + LOSS_LOG_EPS));",
+     "sum += -(nx * log(c + LOSS_LOG_EPS) + (1.0 - nx) * log(1.0 - c + LOSS_LOG_EPS));"),
+    ("locality divided by S", "return loss / (double)(S - 1 > 1 ? S - 1 : 1);",
+     "return loss / (double)S;"),
+    ("chunk one token short", "const int64_t t0 = c * L, t1 = t0 + L < S ? t0 + L : S;\n"
+     "        double sum", "const int64_t t0 = c * L, t1 = t0 + L - 1 < S ? t0 + L - 1 : S;\n"
+     "        double sum"),
+    ("chunk count floored", "const int64_t nc = (S + L - 1) / L;\n    double loss",
+     "const int64_t nc = S / L > 0 ? S / L : 1;\n    double loss"),
+    ("locality grad without the sharpening slope",
+     "grad[a0] += scale * dc * 2.0 * alpha * c * (1.0 - c);", "grad[a0] += scale * dc;"),
+    ("locality grad next-row sign",
+     "double dn = -(c / (nx + LOSS_LOG_EPS) - (1.0 - c) / (1.0 - nx + LOSS_LOG_EPS));",
+     "double dn = (c / (nx + LOSS_LOG_EPS) - (1.0 - c) / (1.0 - nx + LOSS_LOG_EPS));"),
+    ("sparsification grad includes its own factor", "if (j != k)", "if (1)"),
 ]
 
 PIN_TESTS = [
@@ -58,6 +85,17 @@ PIN_TESTS = [
     pins.test_dense_special_case_matches_torch_layer,
     pins.test_score_homogeneity_and_additivity,
     pins.test_single_token_single_expert_closed_form,
+    lpins.test_probs_half_at_zero_and_library_sigmoid,
+    lpins.test_layernorm_worked_example,
+    lpins.test_layernorm_matches_library,
+    lpins.test_layernorm_residual_is_added_not_replaced,
+    lambda: lpins.test_locality_equals_library_bce(2.0),
+    lpins.test_locality_single_token_and_scale,
+    lpins.test_sparsification_closed_forms,
+    lambda: lpins.test_sparsification_brute_force(13, 4),
+    lambda: lpins.test_locality_grad_finite_differences(2.0),
+    lambda: lpins.test_sparsification_grad_finite_differences(9, 4),
+    lpins.test_sparsification_grad_closed_forms,
 ]
 
 
