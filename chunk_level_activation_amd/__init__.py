@@ -21,7 +21,8 @@ __all__ = [
     "BLOCKFFN_F32", "BLOCKFFN_BF16", "BlockFFNError", "FP32_EPS", "library_path",
     "blockffn_router", "blockffn_router_workspace_bytes", "blockffn_router_workspace",
     "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
-    "blockffn_chunk_ffn_workspace",
+    "blockffn_chunk_ffn_workspace", "blockffn_add_layernorm", "blockffn_sparsity_losses",
+    "blockffn_sparsity_losses_workspace_bytes", "blockffn_sparsity_losses_workspace",
     "blockffn_last_error", "blockffn_version", "load_library",
 ]
 
@@ -54,7 +55,8 @@ def load_library():
             "`python -m chunk_level_activation_amd.build_lib` (or __graft_entry__.build())")
     lib = ctypes.CDLL(library_path)
     P, I64, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
-    lib.blockffn_router.argtypes = [P, P, P, P, ctypes.c_float, I64, I64, I64, I, P, P, P,
+    F = ctypes.c_float
+    lib.blockffn_router.argtypes = [P, P, P, P, F, I64, I64, I64, I, P, P, F, P, P,
                                     ctypes.c_size_t, P]
     lib.blockffn_router.restype = I
     lib.blockffn_router_workspace_bytes.argtypes = [I64, I64, I64, I]
@@ -64,6 +66,13 @@ def load_library():
     lib.blockffn_chunk_ffn.argtypes = [P, P, P, P, I64, I64, I64, I64, I64, I, P, P,
                                        ctypes.c_size_t, P, P, P, P]
     lib.blockffn_chunk_ffn.restype = I
+    lib.blockffn_add_layernorm.argtypes = [P, P, P, P, F, I64, I64, I, P, P]
+    lib.blockffn_add_layernorm.restype = I
+    lib.blockffn_sparsity_losses_workspace_bytes.argtypes = [I64, I64, I64, I64]
+    lib.blockffn_sparsity_losses_workspace_bytes.restype = ctypes.c_size_t
+    lib.blockffn_sparsity_losses.argtypes = [P, I64, I64, I64, F, I64, F, F, P, P, P,
+                                             ctypes.c_size_t, P]
+    lib.blockffn_sparsity_losses.restype = I
     lib.blockffn_last_error.argtypes = []
     lib.blockffn_last_error.restype = ctypes.c_char_p
     lib.blockffn_version.argtypes = []
@@ -128,9 +137,11 @@ def blockffn_router_workspace(T: int, d_h: int, E: int, dtype: int, device="cuda
 
 
 def blockffn_router(x, w_r, gain=None, bias=None, eps: float = FP32_EPS, *, scores=None,
-                    logits=None, workspace=None, stream=None):
+                    logits=None, probs=None, sharpness: float = 1.0, workspace=None,
+                    stream=None):
     """scores [T, E] fp32 = RMSNorm_E(ReLU(x W_r^T + bias)) * gain. x [T, d_h] and
     w_r [E, d_h] are both float32 or both bfloat16; gain/bias are [E] float32.
+    `probs` ([T, E] fp32), when given, receives sigmoid(sharpness * scores).
     `workspace` (from blockffn_router_workspace) lets few-token calls split the d_h
     sum over several workgroups; without one the call runs unsplit."""
     import torch
@@ -145,6 +156,7 @@ def blockffn_router(x, w_r, gain=None, bias=None, eps: float = FP32_EPS, *, scor
     args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
             _dev(bias, "bias", torch.float32), float(eps), T, d_h, E, _dtype_code(x),
             _dev(scores, "scores", torch.float32), _dev(logits, "logits", torch.float32),
+            float(sharpness), _dev(probs, "probs", torch.float32),
             _dev(workspace, "workspace"), ws_bytes, _stream(stream)]
     _check(lib.blockffn_router(*args))
     return scores
@@ -198,3 +210,68 @@ def blockffn_chunk_ffn(x, scores, w1, w2, n: int, *, y=None, workspace=None,
             _dev(union_counts, "union_counts", torch.int32), _stream(stream)]
     _check(lib.blockffn_chunk_ffn(*args))
     return y
+
+
+def blockffn_add_layernorm(y, x, gamma=None, beta=None, eps: float = 1e-5, *, out=None,
+                           stream=None):
+    """out [T, d_h] = LayerNorm(y + x) * gamma + beta over d_h (see blockffn.h). y and x
+    share a dtype (float32 or bfloat16); gamma/beta are [d_h] float32. `out` may be y
+    or x (in place)."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    if tuple(y.shape) != (T, d_h) or y.dtype != x.dtype:
+        raise ValueError("y must be [T, d_h] with the dtype of x")
+    if out is None:
+        out = torch.empty_like(x)
+    args = [_dev(y, "y"), _dev(x, "x"), _dev(gamma, "gamma", torch.float32),
+            _dev(beta, "beta", torch.float32), float(eps), T, d_h, _dtype_code(x),
+            _dev(out, "out", x.dtype), _stream(stream)]
+    _check(lib.blockffn_add_layernorm(*args))
+    return out
+
+
+def blockffn_sparsity_losses_workspace_bytes(B: int, S: int, E: int, L: int) -> int:
+    nbytes = load_library().blockffn_sparsity_losses_workspace_bytes(B, S, E, L)
+    if nbytes == 0:
+        raise BlockFFNError(1, blockffn_last_error())
+    return int(nbytes)
+
+
+def blockffn_sparsity_losses_workspace(B: int, S: int, E: int, L: int, device="cuda"):
+    """A zero-filled loss workspace: it must start zeroed and every call returns it to
+    that state."""
+    import torch
+    return torch.zeros(blockffn_sparsity_losses_workspace_bytes(B, S, E, L),
+                       dtype=torch.uint8, device=device)
+
+
+def blockffn_sparsity_losses(probs, alpha: float = 2.0, L: int = 8, lambda_al: float = 1.0,
+                             lambda_cs: float = 1.0, *, losses=None, grad=None,
+                             want_grad: bool = True, workspace=None, stream=None):
+    """(losses [2] fp32 = (activation locality, chunk sparsification), grad) over
+    probabilities [B, S, E] (or [S, E]) float32; grad = lambda_al dAL/dp +
+    lambda_cs dCS/dp, same shape as probs, or None when want_grad is False and no
+    grad tensor is given."""
+    import torch
+    lib = load_library()
+    if probs.dim() == 2:
+        B, (S, E) = 1, probs.shape
+    elif probs.dim() == 3:
+        B, S, E = probs.shape
+    else:
+        raise ValueError("probs must be [B, S, E] or [S, E]")
+    if losses is None:
+        losses = torch.empty(2, dtype=torch.float32, device=probs.device)
+    if grad is None and want_grad:
+        grad = torch.empty_like(probs)
+    if grad is not None and tuple(grad.shape) != tuple(probs.shape):
+        raise ValueError("grad must have the shape of probs")
+    if workspace is None:
+        workspace = blockffn_sparsity_losses_workspace(B, S, E, L, probs.device)
+    args = [_dev(probs, "probs", torch.float32), B, S, E, float(alpha), int(L),
+            float(lambda_al), float(lambda_cs), _dev(losses, "losses", torch.float32),
+            _dev(grad, "grad", torch.float32), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    _check(lib.blockffn_sparsity_losses(*args))
+    return losses, grad

@@ -4,6 +4,7 @@
 // Nothing here touches the device before every argument has been checked, so an
 // invalid call returns an error and enqueues nothing; this also lets the checks run
 // on a machine without a GPU.
+#include <cmath>
 #include <mutex>
 #include <string>
 
@@ -149,6 +150,25 @@ blockffn_status_t check_ffn_sizes(int64_t T, int64_t d_h, int64_t E, int64_t d_e
     return BLOCKFFN_OK;
 }
 
+// [a, a + na) and [b, b + nb) share a byte.
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t pa = reinterpret_cast<uintptr_t>(a), pb = reinterpret_cast<uintptr_t>(b);
+    return pa < pb + nb && pb < pa + na;
+}
+
+blockffn_status_t check_loss_sizes(int64_t B, int64_t S, int64_t E, int64_t L)
+{
+    if (B <= 0 || S <= 0 || E <= 0 || L <= 0)
+        return fail(BLOCKFFN_EINVAL, "B, S, E and L must be positive (B=" + std::to_string(B) +
+                                         ", S=" + std::to_string(S) + ", E=" +
+                                         std::to_string(E) + ", L=" + std::to_string(L) + ")");
+    if (S > ((int64_t)1 << 30) || E > ((int64_t)1 << 20) || B > ((int64_t)1 << 30) ||
+        (double)B * (double)S * (double)E >= 2147483648.0)
+        return fail(BLOCKFFN_EUNSUPPORTED, "B * S * E must stay below 2^31");
+    return BLOCKFFN_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -168,7 +188,8 @@ size_t blockffn_router_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int dt
 blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *gain,
                                   const float *bias, float eps, int64_t T, int64_t d_h,
                                   int64_t E, int dtype, float *scores, float *logits,
-                                  void *workspace, size_t workspace_bytes, void *stream)
+                                  float sharpness, float *probs, void *workspace,
+                                  size_t workspace_bytes, void *stream)
 {
     blockffn_status_t st = check_dtype(dtype);
     if (st != BLOCKFFN_OK)
@@ -183,8 +204,10 @@ blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *g
     if (!aligned(x, ea) || !aligned(w_r, ea))
         return fail(BLOCKFFN_EUNSUPPORTED, "x and w_r must be " + std::to_string(ea) +
                                                "-byte aligned");
+    if (probs && !std::isfinite(sharpness))
+        return fail(BLOCKFFN_EINVAL, "sharpness must be finite");
     if (!aligned(scores, 4) || (logits && !aligned(logits, 4)) || (gain && !aligned(gain, 4)) ||
-        (bias && !aligned(bias, 4)))
+        (bias && !aligned(bias, 4)) || (probs && !aligned(probs, 4)))
         return fail(BLOCKFFN_EUNSUPPORTED, "float arrays must be 4-byte aligned");
     if (workspace) {
         if (!aligned(workspace, 256))
@@ -200,12 +223,13 @@ blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *g
     if (dtype == BLOCKFFN_BF16)
         err = blockffn::launch_router_bf16(static_cast<const uint16_t *>(x),
                                            static_cast<const uint16_t *>(w_r), gain, bias, eps,
-                                           T, d_h, E, scores, logits, workspace,
+                                           T, d_h, E, scores, logits, sharpness, probs,
+                                           workspace,
                                            workspace ? placement_xcds(s) : 0, s);
     else
         err = blockffn::launch_router_f32(static_cast<const float *>(x),
                                           static_cast<const float *>(w_r), gain, bias, eps, T,
-                                          d_h, E, scores, logits, s);
+                                          d_h, E, scores, logits, sharpness, probs, s);
     if (err != hipSuccess)
         return fail(BLOCKFFN_EHIP, std::string("router launch failed: ") + hipGetErrorString(err));
     g_last_error.clear();
@@ -288,6 +312,82 @@ blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const v
     }
     if (err != hipSuccess)
         return fail(BLOCKFFN_EHIP, std::string("chunk FFN launch failed: ") + hipGetErrorString(err));
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
+blockffn_status_t blockffn_add_layernorm(const void *y, const void *x, const float *gamma,
+                                         const float *beta, float eps, int64_t T, int64_t d_h,
+                                         int dtype, void *out, void *stream)
+{
+    blockffn_status_t st = check_dtype(dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if (!y || !x || !out)
+        return fail(BLOCKFFN_EINVAL, "y, x and out must not be NULL");
+    if (T <= 0 || d_h <= 0)
+        return fail(BLOCKFFN_EINVAL, "T and d_h must be positive (T=" + std::to_string(T) +
+                                         ", d_h=" + std::to_string(d_h) + ")");
+    if (!(eps >= 0.0f) || !std::isfinite(eps))
+        return fail(BLOCKFFN_EINVAL, "eps must be finite and >= 0");
+    const int64_t vec = dtype == BLOCKFFN_BF16 ? 8 : 4;
+    if (d_h % vec != 0 || d_h > ((int64_t)1 << 20) || T > ((int64_t)1 << 31) - 4)
+        return fail(BLOCKFFN_EUNSUPPORTED, "d_h must be a multiple of " + std::to_string(vec) +
+                                               " and at most 2^20, T below 2^31");
+    if (!aligned(y, 16) || !aligned(x, 16) || !aligned(out, 16) ||
+        (gamma && !aligned(gamma, 16)) || (beta && !aligned(beta, 16)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "y, x, out, gamma and beta must be 16-byte aligned");
+    const size_t bytes = (size_t)T * (size_t)d_h * (dtype == BLOCKFFN_BF16 ? 2 : 4);
+    if ((out != y && overlap(out, bytes, y, bytes)) || (out != x && overlap(out, bytes, x, bytes)))
+        return fail(BLOCKFFN_EINVAL, "out must be y, x, or not overlap them");
+    const hipError_t err = blockffn::launch_add_layernorm(
+        dtype == BLOCKFFN_BF16, y, x, gamma, beta, eps, T, d_h, out,
+        static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("layernorm launch failed: ") + hipGetErrorString(err));
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
+size_t blockffn_sparsity_losses_workspace_bytes(int64_t B, int64_t S, int64_t E, int64_t L)
+{
+    if (check_loss_sizes(B, S, E, L) != BLOCKFFN_OK)
+        return 0;
+    return blockffn::sparsity_losses_workspace_bytes(B, S, E, L);
+}
+
+blockffn_status_t blockffn_sparsity_losses(const float *probs, int64_t B, int64_t S, int64_t E,
+                                           float alpha, int64_t L, float lambda_al,
+                                           float lambda_cs, float *losses, float *grad,
+                                           void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!probs || !losses || !workspace)
+        return fail(BLOCKFFN_EINVAL, "probs, losses and workspace must not be NULL");
+    blockffn_status_t st = check_loss_sizes(B, S, E, L);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if (!std::isfinite(alpha) || !std::isfinite(lambda_al) || !std::isfinite(lambda_cs))
+        return fail(BLOCKFFN_EINVAL, "alpha, lambda_al and lambda_cs must be finite");
+    if (!aligned(probs, 4) || !aligned(losses, 4) || (grad && !aligned(grad, 4)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "probs, losses and grad must be 4-byte aligned");
+    if (!aligned(workspace, 256))
+        return fail(BLOCKFFN_EUNSUPPORTED, "workspace needs 256-byte alignment");
+    const size_t need = blockffn::sparsity_losses_workspace_bytes(B, S, E, L);
+    if (workspace_bytes < need)
+        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                             " bytes, needs " + std::to_string(need));
+    const size_t pbytes = (size_t)B * S * E * sizeof(float);
+    if ((grad && overlap(grad, pbytes, probs, pbytes)) ||
+        overlap(losses, 2 * sizeof(float), probs, pbytes) ||
+        (grad && overlap(losses, 2 * sizeof(float), grad, pbytes)) ||
+        overlap(workspace, need, probs, pbytes) || overlap(workspace, need, losses, 8) ||
+        (grad && overlap(workspace, need, grad, pbytes)))
+        return fail(BLOCKFFN_EINVAL, "probs, grad, losses and workspace must not overlap");
+    const hipError_t err = blockffn::launch_sparsity_losses(
+        probs, B, S, E, alpha, L, lambda_al, lambda_cs, losses, grad, workspace,
+        static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("loss launch failed: ") + hipGetErrorString(err));
     g_last_error.clear();
     return BLOCKFFN_OK;
 }

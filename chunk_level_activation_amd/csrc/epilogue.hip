@@ -1,0 +1,214 @@
+// Layer epilogue: residual + LayerNorm over the hidden axis (skill page, "Full
+// BlockFFN Layer with Combined Losses": the layer's output is nn.LayerNorm(d_h)
+// applied to the expert output plus the layer input).
+//
+//   v = y[t,:] + x[t,:],  mu = mean_j v_j,  var = mean_j (v_j - mu)^2   (biased)
+//   out[t,j] = (v_j - mu) / sqrt(var + eps) * gamma[j] + beta[j]
+//
+// HBM-bound: each row is read once from y and x and written once. One wavefront owns
+// a row; lane l holds the 16-byte vectors l, l + 64, ... of it in registers, so the
+// two row reductions (mean, then the centred sum of squares) cost no extra memory
+// traffic. Rows longer than the register window (64 lanes x 8 vectors) are read
+// three times instead (sum, centred squares, output); the re-reads mostly hit L2.
+#include "common.h"
+#include "plan.h"
+
+namespace blockffn {
+namespace {
+
+constexpr int kLnWaves = 4;                  // rows per workgroup
+constexpr int kLnMaxVec = 8;                 // register window: vectors per lane
+
+__device__ __forceinline__ float wave_sum(float v)
+{
+#pragma unroll
+    for (int m = 1; m < kWave; m <<= 1)
+        v += __shfl_xor(v, m);
+    return v;
+}
+
+// Element access for the two dtypes: a "vector" is 16 bytes (8 bf16 or 4 float).
+template <typename T> struct Vec;
+template <> struct Vec<uint16_t> {
+    static constexpr int W = 8;
+    __device__ static void load(const uint16_t *p, float *v)
+    {
+        const u32x4 u = *reinterpret_cast<const u32x4 *>(p);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(u[i] << 16);
+            v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+        }
+    }
+    __device__ static void store(uint16_t *p, const float *v)
+    {
+        u32x4 u;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            u[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+        *reinterpret_cast<u32x4 *>(p) = u;
+    }
+};
+template <> struct Vec<float> {
+    static constexpr int W = 4;
+    __device__ static void load(const float *p, float *v)
+    {
+        const float4 f = *reinterpret_cast<const float4 *>(p);
+        v[0] = f.x, v[1] = f.y, v[2] = f.z, v[3] = f.w;
+    }
+    __device__ static void store(float *p, const float *v)
+    {
+        *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+    }
+};
+
+// gamma and beta are 16-byte aligned and j0 is a multiple of W, so they are read
+// four floats at a time.
+template <typename T>
+__device__ __forceinline__ void affine_store(T *o, const float *__restrict__ gamma,
+                                             const float *__restrict__ beta, int j0,
+                                             float *v, float mu, float inv)
+{
+    constexpr int W = Vec<T>::W;
+#pragma unroll
+    for (int q = 0; q < W; q += 4) {
+        const float4 g = gamma ? *reinterpret_cast<const float4 *>(gamma + j0 + q)
+                               : make_float4(1.0f, 1.0f, 1.0f, 1.0f);
+        const float4 b = beta ? *reinterpret_cast<const float4 *>(beta + j0 + q)
+                              : make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+        v[q] = fmaf((v[q] - mu) * inv, g.x, b.x);
+        v[q + 1] = fmaf((v[q + 1] - mu) * inv, g.y, b.y);
+        v[q + 2] = fmaf((v[q + 2] - mu) * inv, g.z, b.z);
+        v[q + 3] = fmaf((v[q + 3] - mu) * inv, g.w, b.w);
+    }
+    Vec<T>::store(o, v);
+}
+
+// NV > 0: the row (d / W vectors, at most 64 * NV) stays in registers. NV == 0: any
+// row length, three passes. d is a multiple of the vector width W.
+template <typename T, int NV>
+__global__ void __launch_bounds__(kLnWaves * kWave)
+add_layernorm_kernel(const T *y, const T *x,
+                     const float *__restrict__ gamma, const float *__restrict__ beta,
+                     float eps, int64_t rows, int d, T *out)
+{
+    constexpr int W = Vec<T>::W;
+    const int lane = threadIdx.x % kWave;
+    const int64_t row = (int64_t)blockIdx.x * kLnWaves + threadIdx.x / kWave;
+    if (row >= rows)
+        return;
+    const int nvec = d / W;
+    const T *yr = y + row * d;
+    const T *xr = x + row * d;
+    T *orow = out + row * d;
+    const float rd = 1.0f / (float)d;
+
+    if constexpr (NV > 0) {
+        float v[NV][W];
+        float sum = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int vi = lane + k * kWave;
+            if (vi < nvec) {
+                float a[W], b[W];
+                Vec<T>::load(yr + vi * W, a);
+                Vec<T>::load(xr + vi * W, b);
+#pragma unroll
+                for (int i = 0; i < W; ++i) {
+                    v[k][i] = a[i] + b[i];
+                    sum += v[k][i];
+                }
+            }
+        }
+        const float mu = wave_sum(sum) * rd;
+        float sq = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NV; ++k)
+            if (lane + k * kWave < nvec)
+#pragma unroll
+                for (int i = 0; i < W; ++i) {
+                    const float c = v[k][i] - mu;
+                    sq = fmaf(c, c, sq);
+                }
+        const float inv = 1.0f / sqrtf(wave_sum(sq) * rd + eps);
+#pragma unroll
+        for (int k = 0; k < NV; ++k) {
+            const int vi = lane + k * kWave;
+            if (vi < nvec)
+                affine_store(orow + vi * W, gamma, beta, vi * W, v[k], mu, inv);
+        }
+    } else {
+        float sum = 0.0f;
+        for (int vi = lane; vi < nvec; vi += kWave) {
+            float a[W], b[W];
+            Vec<T>::load(yr + vi * W, a);
+            Vec<T>::load(xr + vi * W, b);
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                sum += a[i] + b[i];
+        }
+        const float mu = wave_sum(sum) * rd;
+        float sq = 0.0f;
+        for (int vi = lane; vi < nvec; vi += kWave) {
+            float a[W], b[W];
+            Vec<T>::load(yr + vi * W, a);
+            Vec<T>::load(xr + vi * W, b);
+#pragma unroll
+            for (int i = 0; i < W; ++i) {
+                const float c = a[i] + b[i] - mu;
+                sq = fmaf(c, c, sq);
+            }
+        }
+        const float inv = 1.0f / sqrtf(wave_sum(sq) * rd + eps);
+        // In place (out == y or out == x) is safe: a lane reads its vector of both
+        // inputs before it writes that vector, and no vector is read after it has
+        // been written.
+        for (int vi = lane; vi < nvec; vi += kWave) {
+            float a[W], b[W];
+            Vec<T>::load(yr + vi * W, a);
+            Vec<T>::load(xr + vi * W, b);
+#pragma unroll
+            for (int i = 0; i < W; ++i)
+                a[i] += b[i];
+            affine_store(orow + vi * W, gamma, beta, vi * W, a, mu, inv);
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_ln(const T *y, const T *x, const float *gamma, const float *beta, float eps,
+                     int64_t rows, int d, T *out, hipStream_t stream)
+{
+    const int nvec = d / Vec<T>::W;
+    const dim3 grid((unsigned)((rows + kLnWaves - 1) / kLnWaves)), block(kLnWaves * kWave);
+#define LN_LAUNCH(NV)                                                                      \
+    hipLaunchKernelGGL((add_layernorm_kernel<T, NV>), grid, block, 0, stream, y, x, gamma, \
+                       beta, eps, rows, d, out)
+    if (nvec <= kWave)
+        LN_LAUNCH(1);
+    else if (nvec <= 2 * kWave)
+        LN_LAUNCH(2);
+    else if (nvec <= 4 * kWave)
+        LN_LAUNCH(4);
+    else if (nvec <= kLnMaxVec * kWave)
+        LN_LAUNCH(kLnMaxVec);
+    else
+        LN_LAUNCH(0);
+#undef LN_LAUNCH
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_add_layernorm(int dtype_bf16, const void *y, const void *x, const float *gamma,
+                                const float *beta, float eps, int64_t T, int64_t d_h, void *out,
+                                hipStream_t stream)
+{
+    if (dtype_bf16)
+        return launch_ln(static_cast<const uint16_t *>(y), static_cast<const uint16_t *>(x),
+                         gamma, beta, eps, T, (int)d_h, static_cast<uint16_t *>(out), stream);
+    return launch_ln(static_cast<const float *>(y), static_cast<const float *>(x), gamma, beta,
+                     eps, T, (int)d_h, static_cast<float *>(out), stream);
+}
+
+}  // namespace blockffn

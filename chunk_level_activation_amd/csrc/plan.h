@@ -136,12 +136,30 @@ int router_splits(int64_t T, int64_t d_h);
 size_t router_workspace_bytes(int64_t T, int64_t d_h, int64_t E);
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const float *gain,
                               const float *bias, float eps, int64_t T, int64_t d_h,
-                              int64_t E, float *scores, float *logits, void *ws, int xcds,
-                              hipStream_t stream);
+                              int64_t E, float *scores, float *logits, float sharpness,
+                              float *probs, void *ws, int xcds, hipStream_t stream);
 // Checks that workgroup b of a launch runs on XCD b % nxcd (round-robin dispatch).
 hipError_t probe_xcd_placement(int nxcd, bool *round_robin);
 hipError_t launch_router_f32(const float *x, const float *w_r, const float *gain,
                              const float *bias, float eps, int64_t T, int64_t d_h,
-                             int64_t E, float *scores, float *logits, hipStream_t stream);
+                             int64_t E, float *scores, float *logits, float sharpness,
+                             float *probs, hipStream_t stream);
+
+// Residual + LayerNorm of the layer output over d_h (one wavefront per row). d_h is a
+// multiple of 8 (bf16) or 4 (fp32); out may be y or x.
+hipError_t launch_add_layernorm(int dtype_bf16, const void *y, const void *x, const float *gamma,
+                                const float *beta, float eps, int64_t T, int64_t d_h, void *out,
+                                hipStream_t stream);
+
+// Sparsity losses over probabilities [B, S, E] with chunks of L tokens. The workspace
+// (zero-filled once; its counter returns to zero after every call) holds an arrival
+// counter and one fp64 pair of partial sums per workgroup.
+constexpr size_t kLossControlBytes = 256;
+constexpr int64_t kLossMaxBlocks = 2048;
+int64_t sparsity_losses_blocks(int64_t B, int64_t S, int64_t E, int64_t L);
+size_t sparsity_losses_workspace_bytes(int64_t B, int64_t S, int64_t E, int64_t L);
+hipError_t launch_sparsity_losses(const float *p, int64_t B, int64_t S, int64_t E, float alpha,
+                                  int64_t L, float lambda_al, float lambda_cs, float *losses,
+                                  float *grad, void *ws, hipStream_t stream);
 
 }  // namespace blockffn

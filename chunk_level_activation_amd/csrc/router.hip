@@ -34,12 +34,21 @@ constexpr int kRouterMaxSplits = 8;
 // LOCAL: the S splits of a tile run on one XCD (the caller verified round-robin
 // placement and laid the grid out so), and their partials meet in that XCD's L2;
 // otherwise they meet in memory.
+// Activation probability of a score (skill page, "Router Architecture Setup": the
+// router also returns the sigmoid of the sharpened scores, used by the training
+// losses).
+__device__ __forceinline__ float router_prob(float s, float sharpness)
+{
+    return 1.0f / (1.0f + expf(-sharpness * s));
+}
+
 template <int ET, bool LOCAL>
 __global__ void __launch_bounds__(kRouterThreads)
 router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w_r,
                    const float *__restrict__ gain, const float *__restrict__ bias,
                    float eps, int64_t T, int d_h, int E, int S, int X,
                    float *__restrict__ scores, float *__restrict__ logits,
+                   float sharpness, float *__restrict__ probs,
                    float *__restrict__ part, uint32_t *__restrict__ arrive)
 {
     constexpr int KPARTS = kRouterWaves / ET;
@@ -189,9 +198,12 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
         for (int e = sub; e < E; e += 16) {
             const float l = lg[tt][e];
             const float r = l > 0.0f ? l : 0.0f;
-            scores[t * E + e] = r * inv * sgain[e];
+            const float s = r * inv * sgain[e];
+            scores[t * E + e] = s;
             if (logits)
                 logits[t * E + e] = l;
+            if (probs)
+                probs[t * E + e] = router_prob(s, sharpness);
         }
     }
 }
@@ -201,7 +213,7 @@ __global__ void __launch_bounds__(256)
 router_f32_kernel(const float *__restrict__ x, const float *__restrict__ w_r,
                   const float *__restrict__ gain, const float *__restrict__ bias, float eps,
                   int64_t T, int d_h, int E, float *__restrict__ scores,
-                  float *__restrict__ logits)
+                  float *__restrict__ logits, float sharpness, float *__restrict__ probs)
 {
     const int64_t t = blockIdx.x;
     const int e = threadIdx.x;
@@ -225,9 +237,12 @@ router_f32_kernel(const float *__restrict__ x, const float *__restrict__ w_r,
     }
     const float inv = 1.0f / sqrtf(red[0] / (float)E + eps);
     if (e < E) {
-        scores[t * E + e] = r * inv * (gain ? gain[e] : 1.0f);
+        const float s = r * inv * (gain ? gain[e] : 1.0f);
+        scores[t * E + e] = s;
         if (logits)
             logits[t * E + e] = l;
+        if (probs)
+            probs[t * E + e] = router_prob(s, sharpness);
     }
 }
 
@@ -255,8 +270,8 @@ size_t router_workspace_bytes(int64_t T, int64_t d_h, int64_t E)
 
 hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const float *gain,
                               const float *bias, float eps, int64_t T, int64_t d_h,
-                              int64_t E, float *scores, float *logits, void *ws, int xcds,
-                              hipStream_t stream)
+                              int64_t E, float *scores, float *logits, float sharpness,
+                              float *probs, void *ws, int xcds, hipStream_t stream)
 {
     const int64_t tiles = (T + kTileM - 1) / kTileM;
     const int S = ws ? router_splits(T, d_h) : 1;
@@ -270,7 +285,8 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const floa
     const int ET = (int)((E + 31) / 32);
 #define ROUTER_LAUNCH(N, L)                                                                 \
     hipLaunchKernelGGL((router_bf16_kernel<N, L>), grid, block, 0, stream, x, w_r, gain,    \
-                       bias, eps, T, (int)d_h, (int)E, S, X, scores, logits, part, arrive)
+                       bias, eps, T, (int)d_h, (int)E, S, X, scores, logits, sharpness, probs,    \
+                       part, arrive)
 #define ROUTER_LAUNCH_ET(L)   \
     if (ET <= 1)              \
         ROUTER_LAUNCH(1, L);  \
@@ -292,10 +308,11 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const floa
 
 hipError_t launch_router_f32(const float *x, const float *w_r, const float *gain,
                              const float *bias, float eps, int64_t T, int64_t d_h,
-                             int64_t E, float *scores, float *logits, hipStream_t stream)
+                             int64_t E, float *scores, float *logits, float sharpness,
+                             float *probs, hipStream_t stream)
 {
     hipLaunchKernelGGL(router_f32_kernel, dim3((unsigned)T), dim3(256), 0, stream, x, w_r,
-                       gain, bias, eps, T, (int)d_h, (int)E, scores, logits);
+                       gain, bias, eps, T, (int)d_h, (int)E, scores, logits, sharpness, probs);
     return hipGetLastError();
 }
 

@@ -197,3 +197,32 @@ def markov_scores(seed: int, T: int, E: int, tls: float = 0.8, cls: float = 0.7,
     """A fresh mask draw with scores, for rotating masks across benchmark steps."""
     rng = np.random.default_rng(seed)
     return scores_for_mask(rng, markov_active(rng, T, E, tls, cls, L))
+
+
+# ------------------------------------------------------------------ epilogue and losses
+
+def activation_probs(seed: int, B: int, S: int, E: int, tls: float = 0.8, cls: float = 0.7,
+                     L: int = 8) -> np.ndarray:
+    """float32 [B, S, E] activation probabilities for the sparsity losses: per sequence
+    a Markov on/off mask at (tls, cls), then U(0.5, 1) where on and U(0, 0.5) where
+    off, a stand-in for a trained router's probabilities (on/off structure with
+    locality, values spread over the whole open interval)."""
+    rng = np.random.default_rng(seed)
+    out = np.empty((B, S, E), np.float32)
+    for b in range(B):
+        act = markov_active(rng, S, E, tls, cls, L)
+        u = rng.random((S, E))
+        out[b] = np.where(act, 0.5 + 0.5 * u, 0.5 * u).astype(np.float32)
+    return out
+
+
+def layernorm_inputs(seed: int, T: int, d_h: int, bf16: bool):
+    """(y, x, gamma, beta) for the residual + LayerNorm epilogue: y ~ N(0, 1) standing
+    in for the expert output (unit-variance by the weight scaling of expert_weights),
+    x ~ N(0, 1), gamma ~ U(0.5, 1.5), beta ~ N(0, 0.1^2); y and x bf16-exact when bf16."""
+    rng = np.random.default_rng(seed)
+    y = gaussian(rng, (T, d_h), 1.0, bf16)
+    x = gaussian(rng, (T, d_h), 1.0, bf16)
+    gamma = rng.uniform(0.5, 1.5, d_h).astype(np.float32)
+    beta = (0.1 * rng.standard_normal(d_h)).astype(np.float32)
+    return y, x, gamma, beta

@@ -66,6 +66,12 @@ typedef enum { BLOCKFFN_F32 = 0, BLOCKFFN_BF16 = 1 } blockffn_dtype_t;
  *   eps     RMSNorm epsilon (torch's default for fp32 is 1.1920929e-07)
  *   scores  [T, E] float, written   post-RMSNorm scores (exactly 0 when inactive)
  *   logits  [T, E] float or NULL    pre-ReLU logits, written when given
+ *   sharpness, probs                activation probabilities (skill page, "Router
+ *           Architecture Setup": the router also returns the sigmoid of the
+ *           sharpened scores, which the training losses take):
+ *           probs [T, E] float or NULL, written when given with
+ *           probs[t,e] = 1 / (1 + exp(-sharpness * s[t,e])); sharpness must be
+ *           finite (the pages' default is 1). An inactive expert gets exactly 0.5.
  *   workspace, workspace_bytes      optional device scratch (NULL, 0 = none). With a
  *           workspace of at least blockffn_router_workspace_bytes(...) bytes,
  *           ZERO-FILLED before its first use, a bf16 call with few tokens splits the
@@ -79,7 +85,8 @@ typedef enum { BLOCKFFN_F32 = 0, BLOCKFFN_BF16 = 1 } blockffn_dtype_t;
 blockffn_status_t blockffn_router(const void *x, const void *w_r, const float *gain,
                                   const float *bias, float eps, int64_t T, int64_t d_h,
                                   int64_t E, int dtype, float *scores, float *logits,
-                                  void *workspace, size_t workspace_bytes, void *stream);
+                                  float sharpness, float *probs, void *workspace,
+                                  size_t workspace_bytes, void *stream);
 
 /*
  * Bytes of router workspace for these sizes (>= 256; 0 when the sizes are invalid,
@@ -134,6 +141,60 @@ blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const v
                                      void *workspace, size_t workspace_bytes,
                                      uint64_t *union_masks_out, int32_t *expert_lists_out,
                                      int32_t *union_counts_out, void *stream);
+
+/*
+ * Residual + LayerNorm of the layer output (skill page, "Full BlockFFN Layer with
+ * Combined Losses": the layer returns nn.LayerNorm(d_h) of the expert output plus
+ * the layer input):
+ *   v = y[t,:] + x[t,:],  mu = mean_j v_j,  var = mean_j (v_j - mu)^2  (biased)
+ *   out[t,j] = (v_j - mu) / sqrt(var + eps) * gamma[j] + beta[j]
+ *
+ *   y      [T, d_h] dtype   expert output (e.g. blockffn_chunk_ffn's y)
+ *   x      [T, d_h] dtype   layer input (the residual)
+ *   gamma  [d_h] float or NULL (= 1), beta [d_h] float or NULL (= 0)
+ *   eps    finite, >= 0 (nn.LayerNorm's default is 1e-5)
+ *   out    [T, d_h] dtype, written. It may be the same array as y or as x (in
+ *          place); any other overlap with them is rejected.
+ * fp32 arithmetic (two-pass mean and variance); bf16 output rounded to nearest even.
+ * Needs d_h % 8 == 0 (bf16) or d_h % 4 == 0 (fp32), d_h <= 2^20, and 16-byte aligned
+ * y, x, out, gamma, beta.
+ */
+blockffn_status_t blockffn_add_layernorm(const void *y, const void *x, const float *gamma,
+                                         const float *beta, float eps, int64_t T, int64_t d_h,
+                                         int dtype, void *out, void *stream);
+
+/*
+ * Bytes of workspace blockffn_sparsity_losses needs (0 when the sizes are invalid).
+ */
+size_t blockffn_sparsity_losses_workspace_bytes(int64_t B, int64_t S, int64_t E, int64_t L);
+
+/*
+ * The two sparsity training losses and their gradient (skill page, "Activation
+ * Locality Loss" and "Chunk Sparsification Loss"), over activation probabilities
+ * p [B, S, E] (B sequences of S tokens, e.g. the router's probs):
+ *   q = sigmoid(alpha (2p - 1))
+ *   AL = 1/max(S-1, 1) * sum_{i < S-1} mean_{b,e} -( q[b,i,e] log(q[b,i+1,e] + 1e-8)
+ *                                   + (1 - q[b,i,e]) log(1 - q[b,i+1,e] + 1e-8) )
+ *   CS = 1/ceil(S/L) * sum_c mean_{b,e} ( 1 - prod_{k in chunk c} (1 - p[b,k,e]) )
+ * with aligned chunks of L tokens, the last possibly partial (the pages use
+ * alpha = 2, L = 8).
+ *
+ *   probs    [B, S, E] float, device
+ *   losses   [2] float, device, written: losses[0] = AL, losses[1] = CS
+ *   grad     [B, S, E] float or NULL: OVERWRITTEN with
+ *            lambda_al * dAL/dp + lambda_cs * dCS/dp
+ *   workspace, workspace_bytes: at least blockffn_sparsity_losses_workspace_bytes
+ *            bytes, 256-byte aligned, ZERO-FILLED before its first use; it holds an
+ *            arrival counter that every call returns to zero. Calls that may run
+ *            concurrently need separate workspaces.
+ * fp32 arithmetic per element; the loss sums are accumulated in fp64 in a fixed
+ * order, so equal inputs give equal bits. probs, grad, losses and workspace must
+ * not overlap. Needs B * S * E < 2^31.
+ */
+blockffn_status_t blockffn_sparsity_losses(const float *probs, int64_t B, int64_t S, int64_t E,
+                                           float alpha, int64_t L, float lambda_al,
+                                           float lambda_cs, float *losses, float *grad,
+                                           void *workspace, size_t workspace_bytes, void *stream);
 
 /* Message describing the calling thread's last non-OK status ("" if none). */
 const char *blockffn_last_error(void);

@@ -29,9 +29,11 @@ def lib():
     return bf.load_library()
 
 
-def test_header_declares_the_two_calls():
+def test_header_declares_every_call():
     names = declared_functions()
-    for n in ("blockffn_router", "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
+    for n in ("blockffn_router", "blockffn_router_workspace_bytes", "blockffn_chunk_ffn",
+              "blockffn_chunk_ffn_workspace_bytes", "blockffn_add_layernorm",
+              "blockffn_sparsity_losses", "blockffn_sparsity_losses_workspace_bytes",
               "blockffn_last_error", "blockffn_version"):
         assert n in names
 
@@ -55,9 +57,10 @@ def ffn(lib, x=FAKE, scores=FAKE, w1=FAKE, w2=FAKE, T=32, d_h=2048, E=64, d_e=12
 
 
 def router(lib, x=FAKE, w_r=FAKE, gain=None, bias=None, eps=1e-6, T=32, d_h=2048, E=64,
-           dtype=1, scores=FAKE, logits=None, ws=None, ws_bytes=0):
+           dtype=1, scores=FAKE, logits=None, sharpness=1.0, probs=None, ws=None,
+           ws_bytes=0):
     return lib.blockffn_router(x, w_r, gain, bias, eps, T, d_h, E, dtype, scores, logits,
-                               ws, ws_bytes, None)
+                               sharpness, probs, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -86,9 +89,60 @@ def test_fp32_accepts_unaligned_sizes_but_checks_workspace(lib):
     (dict(E=300), 2), (dict(d_h=100), 2), (dict(x=FAKE_ODD), 2),
     (dict(scores=FAKE_ODD), 2), (dict(ws=FAKE + 4, ws_bytes=1 << 30), 2),
     (dict(ws=FAKE, ws_bytes=0), 3), (dict(ws=FAKE, ws_bytes=255), 3),
+    (dict(probs=FAKE + 0x100000, sharpness=float("inf")), 1),
+    (dict(probs=FAKE + 0x100000, sharpness=float("nan")), 1),
+    (dict(probs=FAKE_ODD), 2),
 ])
 def test_router_rejects(lib, kw, status):
     assert router(lib, **kw) == status
+
+
+def layernorm(lib, y=FAKE, x=FAKE + (1 << 24), gamma=None, beta=None, eps=1e-5, T=32,
+              d_h=2048, dtype=1, out=FAKE + (2 << 24)):
+    return lib.blockffn_add_layernorm(y, x, gamma, beta, eps, T, d_h, dtype, out, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(y=None), 1), (dict(x=None), 1), (dict(out=None), 1), (dict(T=0), 1),
+    (dict(d_h=0), 1), (dict(dtype=3), 1), (dict(eps=-1.0), 1), (dict(eps=float("inf")), 1),
+    (dict(d_h=2044), 2), (dict(dtype=0, d_h=2046), 2), (dict(y=FAKE + 8), 2),
+    (dict(gamma=FAKE + 4), 2), (dict(beta=FAKE + 8), 2),
+    # out may be y or x, but not overlap them partially
+    (dict(out=FAKE + 4096), 1), (dict(out=FAKE + (1 << 24) - 4096), 1),
+])
+def test_layernorm_rejects(lib, kw, status):
+    assert layernorm(lib, **kw) == status
+    assert bf.blockffn_last_error() != ""
+
+
+def losses(lib, probs=FAKE, B=2, S=4096, E=64, alpha=2.0, L=8, lal=1.0, lcs=1.0,
+           out=FAKE + (4 << 24), grad=FAKE + (8 << 24), ws=FAKE + (16 << 24),
+           ws_bytes=1 << 20):
+    return lib.blockffn_sparsity_losses(probs, B, S, E, alpha, L, lal, lcs, out, grad, ws,
+                                        ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(probs=None), 1), (dict(out=None), 1), (dict(ws=None), 1), (dict(B=0), 1),
+    (dict(S=0), 1), (dict(E=0), 1), (dict(L=0), 1), (dict(alpha=float("nan")), 1),
+    (dict(lal=float("inf")), 1),
+    (dict(B=1 << 16, S=1 << 16), 2), (dict(probs=FAKE + 2), 2), (dict(ws=FAKE + (16 << 24) + 4), 2),
+    (dict(ws_bytes=100), 3),
+    (dict(grad=FAKE + 4096), 1), (dict(out=FAKE + 8), 1),
+])
+def test_sparsity_losses_rejects(lib, kw, status):
+    assert losses(lib, **kw) == status
+    assert bf.blockffn_last_error() != ""
+
+
+def test_sparsity_losses_workspace_query(lib):
+    f = lib.blockffn_sparsity_losses_workspace_bytes
+    # counter block + one fp64 pair per workgroup (4096 tokens, 8-token chunks, 64
+    # experts: 32768 columns -> 128 workgroups)
+    assert f(1, 4096, 64, 8) == 256 + 128 * 16
+    assert f(64, 4096, 64, 8) == 256 + 2048 * 16
+    assert f(1, 4096, 64, 0) == 0
+    assert f(1, 0, 64, 8) == 0
 
 
 def test_router_workspace_query(lib):
