@@ -51,6 +51,8 @@ def parse_args(argv=None):
     ap.add_argument("--no-dense", action="store_true",
                     help="skip the all-experts-active comparison run")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the epilogue / loss kernel measurements")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="run one device-to-device copy of this many MiB first (a plain "
                          "kernel of known traffic, for scaling hardware byte counters)")
@@ -206,6 +208,12 @@ def main(argv=None):
         dense_ms = time_replays(g_dense, replays) / nsteps
         dense = {"ffn_ms": dense_ms, "ratio_dense_over_sparse": dense_ms / ffn_avg_ms}
 
+    extras = None
+    if not args.no_extras:
+        extras = bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain,
+                              router_out, y, ws, router_ws, counts, S, replays, wreplays,
+                              time_replays, capture)
+
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(args, cfg, np, inputs)
@@ -250,10 +258,104 @@ def main(argv=None):
             "mfma_frac": ffn_flops / (ffn_avg_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
         "dense_ffn": dense,
+        "extras": extras,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
     return 0
+
+
+def bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain, router_out, y, ws,
+                 router_ws, counts, S, replays, wreplays, time_replays, capture):
+    """The rest of the pages' layer around the hot path, measured the same way:
+    (1) the whole layer step with its epilogue (router with probabilities, chunk FFN,
+    residual + LayerNorm) over the same rotation; (2) the LayerNorm alone and (3) the
+    sparsity losses with their gradient alone, each over rotating input copies of at
+    least 512 MiB, timed with HIP events around graph replays."""
+    T, d_h, E, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["n"]
+    dev = torch.device("cuda:0")
+    nc, nd = len(copies), len(draws)
+    ln_g = torch.ones(d_h, dtype=torch.float32, device=dev)
+    ln_b = torch.zeros(d_h, dtype=torch.float32, device=dev)
+    probs = torch.empty((T, E), dtype=torch.float32, device=dev)
+    out = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
+
+    def layer_step(i):
+        w = copies[i % nc]
+        d = draws[i % nd]
+        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=router_out[i % nd],
+                           probs=probs, workspace=router_ws)
+        s = router_out[i % nd] if args.workload == "e2e" else d["scores"]
+        bf.blockffn_chunk_ffn(d["x"], s, w["w1"], w["w2"], n, y=y, workspace=ws,
+                              union_counts=counts[i % nd])
+        bf.blockffn_add_layernorm(y, d["x"], ln_g, ln_b, out=out)
+
+    g = capture(layer_step)
+    time_replays(g, wreplays)
+    layer_ms = time_replays(g, replays) / (replays * S)
+    del g
+
+    def rotating_ms(make, launch, bytes_per_set, launches=256):
+        """Average duration of one launch over rotating input sets (>= 512 MiB)."""
+        sets = max(2, math.ceil(512 * 2 ** 20 / bytes_per_set))
+        data = [make(k) for k in range(sets)]
+        launch(data[0])
+        torch.cuda.synchronize()
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            for k in range(launches):
+                launch(data[k % sets])
+        time_replays(gr, 2)
+        ms = time_replays(gr, 10) / (10 * launches)
+        del gr, data
+        torch.cuda.empty_cache()
+        return ms, sets
+
+    res = {"layer_with_epilogue": {
+        "what": "router (scores + probabilities) + chunk FFN + residual LayerNorm per "
+                "step, same rotation as the headline step",
+        "ms_per_step": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3)}}
+
+    # residual + LayerNorm at the end-to-end token count
+    T_ln = 4096
+    ln_bytes = 3 * T_ln * d_h * 2 + 2 * d_h * 4
+
+    def make_ln(k):
+        r = np.random.default_rng(1000 + k)
+        yk = torch.from_numpy(inputs.gaussian(r, (T_ln, d_h), 1.0, True)).to(dev, torch.bfloat16)
+        xk = torch.from_numpy(inputs.gaussian(r, (T_ln, d_h), 1.0, True)).to(dev, torch.bfloat16)
+        return yk, xk, torch.empty_like(xk)
+
+    ln_ms, ln_sets = rotating_ms(make_ln, lambda a: bf.blockffn_add_layernorm(
+        a[0], a[1], ln_g, ln_b, out=a[2]), ln_bytes)
+    res["add_layernorm"] = {
+        "shape": f"T={T_ln} d_h={d_h} bf16", "avg_launch_us": ln_ms * 1e3,
+        "algorithmic_bytes": ln_bytes, "achieved_gbs": ln_bytes / (ln_ms * 1e-3) / 1e9,
+        "frac_of_hbm_peak": ln_bytes / (ln_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+        "rotation_sets": ln_sets}
+
+    # sparsity losses + gradient: one 4096-token sequence and a 16 x 4096 batch
+    for B in (1, 16):
+        S_l, L = 4096, 8
+        l_bytes = 2 * B * S_l * E * 4
+        lws = bf.blockffn_sparsity_losses_workspace(B, S_l, E, L, dev)
+        lout = torch.empty(2, dtype=torch.float32, device=dev)
+
+        def make_l(k, B=B, S_l=S_l):
+            p = torch.from_numpy(inputs.activation_probs(2000 + k, B, S_l, E)).to(dev)
+            return p, torch.empty_like(p)
+
+        l_ms, l_sets = rotating_ms(make_l, lambda a, lws=lws, lout=lout:
+                                   bf.blockffn_sparsity_losses(a[0], 2.0, L, 0.1, 0.1,
+                                                               losses=lout, grad=a[1],
+                                                               workspace=lws), l_bytes)
+        res[f"sparsity_losses_B{B}"] = {
+            "shape": f"probs [{B}, {S_l}, {E}] fp32, L={L}, alpha=2, forward + gradient",
+            "avg_launch_us": l_ms * 1e3, "algorithmic_bytes": l_bytes,
+            "achieved_gbs": l_bytes / (l_ms * 1e-3) / 1e9,
+            "frac_of_hbm_peak": l_bytes / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "rotation_sets": l_sets}
+    return res
 
 
 def read_traffic(workload):

@@ -7,25 +7,20 @@
 //
 // HBM-bound: each row is read once from y and x and written once. One wavefront owns
 // a row; lane l holds the 16-byte vectors l, l + 64, ... of it in registers, so the
-// two row reductions (mean, then the centred sum of squares) cost no extra memory
-// traffic. Rows longer than the register window (64 lanes x 8 vectors) are read
-// three times instead (sum, centred squares, output); the re-reads mostly hit L2.
+// two row reductions (mean, then the centred sum of squares, both DPP trees) cost no
+// extra memory traffic. A workgroup of R rows stages gamma and beta in LDS once,
+// while its rows' loads are in flight, instead of every wavefront reading them again
+// after its reductions. Rows longer than the register window (64 lanes x 8 vectors)
+// are read three times instead (sum, centred squares, output); the re-reads mostly
+// hit L2.
 #include "common.h"
 #include "plan.h"
 
 namespace blockffn {
 namespace {
 
-constexpr int kLnWaves = 4;                  // rows per workgroup
 constexpr int kLnMaxVec = 8;                 // register window: vectors per lane
-
-__device__ __forceinline__ float wave_sum(float v)
-{
-#pragma unroll
-    for (int m = 1; m < kWave; m <<= 1)
-        v += __shfl_xor(v, m);
-    return v;
-}
+constexpr int kLnMaxWaves = 16;              // rows per workgroup, at most
 
 // Element access for the two dtypes: a "vector" is 16 bytes (8 bf16 or 4 float).
 template <typename T> struct Vec;
@@ -62,12 +57,12 @@ template <> struct Vec<float> {
     }
 };
 
-// gamma and beta are 16-byte aligned and j0 is a multiple of W, so they are read
-// four floats at a time.
+// out = (v - mu) * inv * gamma + beta for the W elements at j0. gamma and beta are
+// 16-byte aligned (global or LDS) and j0 is a multiple of W, so they are read four
+// floats at a time; NULL means 1 and 0.
 template <typename T>
-__device__ __forceinline__ void affine_store(T *o, const float *__restrict__ gamma,
-                                             const float *__restrict__ beta, int j0,
-                                             float *v, float mu, float inv)
+__device__ __forceinline__ void affine_store(T *o, const float *gamma, const float *beta,
+                                             int j0, float *v, float mu, float inv)
 {
     constexpr int W = Vec<T>::W;
 #pragma unroll
@@ -84,19 +79,23 @@ __device__ __forceinline__ void affine_store(T *o, const float *__restrict__ gam
     Vec<T>::store(o, v);
 }
 
-// NV > 0: the row (d / W vectors, at most 64 * NV) stays in registers. NV == 0: any
-// row length, three passes. d is a multiple of the vector width W.
+// NV > 0: the row (d / W vectors, at most 64 * NV) stays in registers, and gamma and
+// beta (when given) are staged in dynamic LDS: [gamma d floats][beta d floats].
+// NV == 0: any row length, three passes, gamma and beta read from global memory.
+// d is a multiple of the vector width W. The workgroup holds blockDim.x / 64 rows.
+// The early return of rows past the end is per wavefront, and only the NV == 0 path
+// (which has no barrier) takes it before the staging barrier.
 template <typename T, int NV>
-__global__ void __launch_bounds__(kLnWaves * kWave)
-add_layernorm_kernel(const T *y, const T *x,
-                     const float *__restrict__ gamma, const float *__restrict__ beta,
-                     float eps, int64_t rows, int d, T *out)
+__global__ void __launch_bounds__(kLnMaxWaves * kWave)
+add_layernorm_kernel(const T *y, const T *x, const float *__restrict__ gamma,
+                     const float *__restrict__ beta, float eps, int64_t rows, int d, T *out)
 {
     constexpr int W = Vec<T>::W;
+    extern __shared__ float4 ln_lds[];
     const int lane = threadIdx.x % kWave;
-    const int64_t row = (int64_t)blockIdx.x * kLnWaves + threadIdx.x / kWave;
-    if (row >= rows)
-        return;
+    const int waves = blockDim.x / kWave;
+    const int64_t row = (int64_t)blockIdx.x * waves + threadIdx.x / kWave;
+    const bool live = row < rows;
     const int nvec = d / W;
     const T *yr = y + row * d;
     const T *xr = x + row * d;
@@ -109,7 +108,7 @@ add_layernorm_kernel(const T *y, const T *x,
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int vi = lane + k * kWave;
-            if (vi < nvec) {
+            if (live && vi < nvec) {
                 float a[W], b[W];
                 Vec<T>::load(yr + vi * W, a);
                 Vec<T>::load(xr + vi * W, b);
@@ -120,7 +119,20 @@ add_layernorm_kernel(const T *y, const T *x,
                 }
             }
         }
-        const float mu = wave_sum(sum) * rd;
+        // stage gamma and beta while the row loads are in flight
+        float *sg = reinterpret_cast<float *>(ln_lds);
+        float *sb = sg + d;
+        const int d4 = d / 4;
+        for (int j = threadIdx.x; j < d4; j += blockDim.x) {
+            if (gamma)
+                ln_lds[j] = reinterpret_cast<const float4 *>(gamma)[j];
+            if (beta)
+                ln_lds[d4 + j] = reinterpret_cast<const float4 *>(beta)[j];
+        }
+        __syncthreads();
+        if (!live)
+            return;
+        const float mu = wave_sum_f32(sum) * rd;
         float sq = 0.0f;
 #pragma unroll
         for (int k = 0; k < NV; ++k)
@@ -130,14 +142,17 @@ add_layernorm_kernel(const T *y, const T *x,
                     const float c = v[k][i] - mu;
                     sq = fmaf(c, c, sq);
                 }
-        const float inv = 1.0f / sqrtf(wave_sum(sq) * rd + eps);
+        const float inv = 1.0f / sqrtf(wave_sum_f32(sq) * rd + eps);
 #pragma unroll
         for (int k = 0; k < NV; ++k) {
             const int vi = lane + k * kWave;
             if (vi < nvec)
-                affine_store(orow + vi * W, gamma, beta, vi * W, v[k], mu, inv);
+                affine_store(orow + vi * W, gamma ? sg : nullptr, beta ? sb : nullptr, vi * W,
+                             v[k], mu, inv);
         }
     } else {
+        if (!live)
+            return;
         float sum = 0.0f;
         for (int vi = lane; vi < nvec; vi += kWave) {
             float a[W], b[W];
@@ -147,7 +162,7 @@ add_layernorm_kernel(const T *y, const T *x,
             for (int i = 0; i < W; ++i)
                 sum += a[i] + b[i];
         }
-        const float mu = wave_sum(sum) * rd;
+        const float mu = wave_sum_f32(sum) * rd;
         float sq = 0.0f;
         for (int vi = lane; vi < nvec; vi += kWave) {
             float a[W], b[W];
@@ -159,7 +174,7 @@ add_layernorm_kernel(const T *y, const T *x,
                 sq = fmaf(c, c, sq);
             }
         }
-        const float inv = 1.0f / sqrtf(wave_sum(sq) * rd + eps);
+        const float inv = 1.0f / sqrtf(wave_sum_f32(sq) * rd + eps);
         // In place (out == y or out == x) is safe: a lane reads its vector of both
         // inputs before it writes that vector, and no vector is read after it has
         // been written.
@@ -175,25 +190,37 @@ add_layernorm_kernel(const T *y, const T *x,
     }
 }
 
+// Rows per workgroup: enough workgroups to spread over the chip (about two per CU
+// for large T), up to 16 rows sharing one staged copy of gamma and beta.
+int ln_rows_per_block(int64_t rows)
+{
+    int r = 1;
+    while (r < kLnMaxWaves && rows >= (int64_t)r * 2 * 512)
+        r *= 2;
+    return r;
+}
+
 template <typename T>
 hipError_t launch_ln(const T *y, const T *x, const float *gamma, const float *beta, float eps,
                      int64_t rows, int d, T *out, hipStream_t stream)
 {
     const int nvec = d / Vec<T>::W;
-    const dim3 grid((unsigned)((rows + kLnWaves - 1) / kLnWaves)), block(kLnWaves * kWave);
-#define LN_LAUNCH(NV)                                                                      \
-    hipLaunchKernelGGL((add_layernorm_kernel<T, NV>), grid, block, 0, stream, y, x, gamma, \
-                       beta, eps, rows, d, out)
+    const int R = ln_rows_per_block(rows);
+    const dim3 grid((unsigned)((rows + R - 1) / R)), block(R * kWave);
+    const size_t lds = (gamma || beta) ? 2 * (size_t)d * sizeof(float) : 0;
+#define LN_LAUNCH(NV, LDS)                                                                 \
+    hipLaunchKernelGGL((add_layernorm_kernel<T, NV>), grid, block, LDS, stream, y, x,      \
+                       gamma, beta, eps, rows, d, out)
     if (nvec <= kWave)
-        LN_LAUNCH(1);
+        LN_LAUNCH(1, lds);
     else if (nvec <= 2 * kWave)
-        LN_LAUNCH(2);
+        LN_LAUNCH(2, lds);
     else if (nvec <= 4 * kWave)
-        LN_LAUNCH(4);
+        LN_LAUNCH(4, lds);
     else if (nvec <= kLnMaxVec * kWave)
-        LN_LAUNCH(kLnMaxVec);
+        LN_LAUNCH(kLnMaxVec, lds);
     else
-        LN_LAUNCH(0);
+        LN_LAUNCH(0, 0);
 #undef LN_LAUNCH
     return hipGetLastError();
 }

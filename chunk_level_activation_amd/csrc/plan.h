@@ -152,9 +152,10 @@ hipError_t launch_add_layernorm(int dtype_bf16, const void *y, const void *x, co
                                 hipStream_t stream);
 
 // Sparsity losses over probabilities [B, S, E] with chunks of L tokens. The workspace
-// (zero-filled once; its counter returns to zero after every call) holds an arrival
-// counter and one fp64 pair of partial sums per workgroup.
-constexpr size_t kLossControlBytes = 256;
+// (zero-filled once; its counters return to zero after every call) holds the arrival
+// counters (a top counter and 64 group counters, 128 bytes apart) and one fp64 pair
+// of partial sums per workgroup.
+constexpr size_t kLossControlBytes = 65 * 128;   // top counter + 64 group counters
 constexpr int64_t kLossMaxBlocks = 2048;
 int64_t sparsity_losses_blocks(int64_t B, int64_t S, int64_t E, int64_t L);
 size_t sparsity_losses_workspace_bytes(int64_t B, int64_t S, int64_t E, int64_t L);

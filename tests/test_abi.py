@@ -137,10 +137,12 @@ def test_sparsity_losses_rejects(lib, kw, status):
 
 def test_sparsity_losses_workspace_query(lib):
     f = lib.blockffn_sparsity_losses_workspace_bytes
-    # counter block + one fp64 pair per workgroup (4096 tokens, 8-token chunks, 64
-    # experts: 32768 columns -> 128 workgroups)
-    assert f(1, 4096, 64, 8) == 256 + 128 * 16
-    assert f(64, 4096, 64, 8) == 256 + 2048 * 16
+    # counter lines (top + 64 groups) + one fp64 pair per workgroup, for the most
+    # workgroups a launch
+    # may use (4096 tokens, 8-token chunks, 64 experts: 32768 columns -> 512 one-wave
+    # workgroups)
+    assert f(1, 4096, 64, 8) == 65 * 128 + 512 * 16
+    assert f(64, 4096, 64, 8) == 65 * 128 + 2048 * 16
     assert f(1, 4096, 64, 0) == 0
     assert f(1, 0, 64, 8) == 0
 

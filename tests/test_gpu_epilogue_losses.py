@@ -175,7 +175,7 @@ def test_sparsity_losses_deterministic_and_workspace_reset():
     p = inputs.activation_probs(77, B, S, E)
     ws = bf.blockffn_sparsity_losses_workspace(B, S, E, L, DEV)
     l1, g1 = run_losses(p, ws=ws)
-    assert not ws[:256].cpu().numpy().any()
+    assert not ws[:65 * 128].cpu().numpy().any()
     l2, g2 = run_losses(p, ws=ws)
     assert np.array_equal(l1, l2) and np.array_equal(g1, g2)
     check_losses(p, 2.0, L, 1.0, 1.0, l1, g1)
@@ -212,3 +212,34 @@ def test_sparsity_losses_exact_zeros_and_ones(L):
     c0 = (3 // L) * L
     others = [t for t in range(c0, min(c0 + L, S)) if t != 3]
     assert np.all(g_cs[0, others, 2] == 0.0)
+
+
+def _offset_copy(a):
+    """A device copy of `a` that starts 4 bytes into its allocation: not 16-byte
+    aligned, so the kernel takes one expert per thread."""
+    n = a.size
+    buf = torch.zeros(n + 4, dtype=torch.float32, device=DEV)
+    view = buf[1:1 + n].view(a.shape)
+    view.copy_(torch.from_numpy(np.ascontiguousarray(a)))
+    return view
+
+
+@pytest.mark.parametrize("B,S,E,offset", [
+    (16, 4096, 64, False),     # the benchmarked batch: four experts per thread
+    (16, 4096, 64, True),      # same, one expert per thread, 2048 workgroups
+    (320, 100, 64, False),     # four experts per thread with a ragged last chunk
+    (512, 100, 40, False),     # E = 40, four experts per thread
+])
+def test_sparsity_losses_large(B, S, E, offset):
+    p = inputs.activation_probs(B + S + E, B, S, E)
+    pd = _offset_copy(p) if offset else dev(p)
+    gd = _offset_copy(np.zeros_like(p)) if offset else None
+    ws = bf.blockffn_sparsity_losses_workspace(B, S, E, 8, DEV)
+    l1, g1 = bf.blockffn_sparsity_losses(pd, 2.0, 8, 0.1, 0.3, grad=gd, workspace=ws)
+    torch.cuda.synchronize()
+    l1, g1 = l1.cpu().numpy(), g1.cpu().numpy()
+    check_losses(p, 2.0, 8, 0.1, 0.3, l1, g1)
+    l2, g2 = bf.blockffn_sparsity_losses(pd, 2.0, 8, 0.1, 0.3, grad=gd, workspace=ws)
+    torch.cuda.synchronize()
+    assert np.array_equal(l1, l2.cpu().numpy()) and np.array_equal(g1, g2.cpu().numpy())
+    assert not ws[:65 * 128].cpu().numpy().any()
