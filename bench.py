@@ -360,7 +360,8 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain, router_o
 
 def read_traffic(workload):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current kernel source; else None."""
+    taken on the current source of the measured kernel (the files its
+    `kernel_sources` line names); else None."""
     import hashlib
     path = os.path.join(ROOT, "profiles", f"ffn_{workload}_traffic.txt")
     if not os.path.exists(path):
@@ -371,8 +372,11 @@ def read_traffic(workload):
             k, v = line.split(":", 1)
             kv[k.strip()] = v.strip()
     src = os.path.join(ROOT, "chunk_level_activation_amd", "csrc")
+    names = kv.get("kernel_sources", "").split()
+    if not names or not all(os.path.exists(os.path.join(src, fn)) for fn in names):
+        return None
     h = hashlib.sha256()
-    for fn in sorted(os.listdir(src)):
+    for fn in names:
         h.update(open(os.path.join(src, fn), "rb").read())
     if kv.get("kernel_source_sha256") != h.hexdigest():
         return None
