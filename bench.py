@@ -42,7 +42,8 @@ def parse_args(argv=None):
     ap.add_argument("--steps", type=int, default=2000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="decode",
-                    choices=["decode", "prefill", "large", "e2e"])
+                    choices=["decode", "prefill", "large", "e2e", "rec256", "rec512",
+                             "rec256_prefill"])
     ap.add_argument("--rotate-mib", type=int, default=768,
                     help="total size of the distinct weight copies cycled through")
     ap.add_argument("--draws", type=int, default=16)

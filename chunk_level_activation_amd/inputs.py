@@ -139,12 +139,19 @@ def expert_weights(rng, E, d_e, d_h, bf16):
 #   large    d_h=4096, E=128, d_e=128, T=512,  n=32, bf16, Markov at (tls, cls) or dense
 #   e2e      d_h=2048, E=64,  d_e=128, T=4096, n=32, bf16, router with a logit shift
 #            giving ~80% zeros after ReLU
+#   rec256, rec512          d_h=2048, E=40, d_e=256 / 512, T=32, n=32, bf16, Markov
+#            80/70: the expert count and widths the skill page recommends ("Key
+#            Hyperparameters"), one decode chunk
+#   rec256_prefill          the same with d_e=256 and T=2048
 WORKLOADS = {
     "tiny": dict(d_h=256, E=16, d_e=64, T=64, n=8, dtype="f32"),
     "decode": dict(d_h=2048, E=64, d_e=128, T=32, n=32, dtype="bf16"),
     "prefill": dict(d_h=2048, E=64, d_e=128, T=2048, n=32, dtype="bf16"),
     "large": dict(d_h=4096, E=128, d_e=128, T=512, n=32, dtype="bf16"),
     "e2e": dict(d_h=2048, E=64, d_e=128, T=4096, n=32, dtype="bf16"),
+    "rec256": dict(d_h=2048, E=40, d_e=256, T=32, n=32, dtype="bf16"),
+    "rec512": dict(d_h=2048, E=40, d_e=512, T=32, n=32, dtype="bf16"),
+    "rec256_prefill": dict(d_h=2048, E=40, d_e=256, T=2048, n=32, dtype="bf16"),
 }
 
 # z such that P(N(0,1) > z) = 0.2: a logit shift of -z * ||W_r[e]|| leaves each

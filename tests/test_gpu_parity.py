@@ -127,6 +127,9 @@ DECODE = [
     ("d_h=4096", 32, 64, 4096, 128, 0.8, 0.7, False),
     ("E=128", 32, 128, 2048, 128, 0.8, 0.7, False),
     ("d_e=256", 32, 32, 2048, 256, 0.8, 0.7, False),
+    ("recommended E=40 d_e=256", 32, 40, 2048, 256, 0.8, 0.7, False),
+    ("recommended E=40 d_e=512", 32, 40, 2048, 512, 0.8, 0.7, False),
+    ("recommended d_e=512 T=7", 7, 40, 2048, 512, 0.8, 0.7, False),
 ]
 
 
@@ -190,6 +193,8 @@ GROUPED = [
     ("E=128", 96, 32, 128, 512, 128, False),
     ("d_h=256", 64, 32, 16, 256, 128, False),
     ("all experts active", 64, 32, 64, 1024, 128, True),
+    ("recommended E=40 d_e=256", 128, 32, 40, 2048, 256, False),
+    ("recommended E=40 d_e=512", 96, 32, 40, 2048, 512, False),
 ]
 
 
