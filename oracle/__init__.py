@@ -1,5 +1,6 @@
-"""CPU oracle for the BlockFFN layer forward (router + chunk-union expert FFN), its
-residual + LayerNorm epilogue and the two sparsity training losses with gradients.
+"""CPU oracle for the BlockFFN layer (router + chunk-union expert FFN, forward and
+backward), its residual + LayerNorm epilogue and the two sparsity training losses
+with gradients.
 
 TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the benchmark's
 CPU-baseline leg use this package; the GPU library never imports, links or calls it,
@@ -91,6 +92,9 @@ def _bind(lib):
     lib.oracle_locality_loss_grad.restype = None
     lib.oracle_chunk_sparsification_loss_grad.argtypes = [P, I64, I64, I64, I64, P]
     lib.oracle_chunk_sparsification_loss_grad.restype = None
+    lib.oracle_layer_backward.argtypes = [P, P, P, P, D, P, P, I64, I64, I64, I64, I64, P, P,
+                                          D, P, P, P, P, P, P, P, P, P, P]
+    lib.oracle_layer_backward.restype = None
     _lib = lib
     return lib
 
@@ -228,6 +232,33 @@ def chunk_sparsification_loss_grad(p, L: int = 8) -> np.ndarray:
     g = np.empty((B, S, E), np.float64)
     _load().oracle_chunk_sparsification_loss_grad(_ptr(p), B, S, E, int(L), _ptr(g))
     return g
+
+
+def layer_backward(x, w_r, w1, w2, dy, n: int, gain=None, bias=None, eps: float = FP32_EPS,
+                   dprobs=None, sharpness: float = 1.0) -> dict:
+    """Gradients (float64) of sum(dy * y) + sum(dprobs * probs) for the layer
+    y = chunk_ffn(x, router(x)), probs = sigmoid(sharpness * scores): a dict with dx,
+    dw_r, dgain, dbias, dw1, dw2 (see oracle_layer_backward in the C file)."""
+    lib = _load()
+    x, w_r, w1, w2, dy = _f32(x), _f32(w_r), _f32(w1), _f32(w2), _f32(dy)
+    T, d_h = x.shape
+    E, d_e, _ = w1.shape
+    assert w_r.shape == (E, d_h) and w2.shape == (E, d_h, d_e) and dy.shape == (T, d_h)
+    assert d_e <= 4096
+    gain = None if gain is None else _f32(gain)
+    bias = None if bias is None else _f32(bias)
+    dprobs = None if dprobs is None else _f32(dprobs)
+    out = dict(dx=np.empty((T, d_h)), dw_r=np.empty((E, d_h)), dgain=np.empty(E),
+               dbias=np.empty(E), dw1=np.empty((E, d_e, d_h)), dw2=np.empty((E, d_h, d_e)))
+    logits, scores, ds = np.empty((T, E)), np.empty((T, E)), np.empty((T, E))
+    da = np.empty((T, E, d_e))
+    lib.oracle_layer_backward(_ptr(x), _ptr(w_r), _ptr(gain), _ptr(bias), float(eps),
+                              _ptr(w1), _ptr(w2), T, d_h, E, d_e, int(n), _ptr(dy),
+                              _ptr(dprobs), float(sharpness), _ptr(out["dx"]),
+                              _ptr(out["dw_r"]), _ptr(out["dgain"]), _ptr(out["dbias"]),
+                              _ptr(out["dw1"]), _ptr(out["dw2"]), _ptr(logits), _ptr(scores),
+                              _ptr(ds), _ptr(da))
+    return out
 
 
 # --------------------------------------------------------------------------------

@@ -1,5 +1,6 @@
 /*
- * CPU oracle for the BlockFFN layer forward: router and chunk-union expert FFN.
+ * CPU oracle for the BlockFFN layer: router and chunk-union expert FFN (forward and
+ * backward), the residual + LayerNorm epilogue and the two sparsity losses.
  *
  * THIS FILE IS TEST INFRASTRUCTURE. Only the test suite, the smoke check and the
  * benchmark's CPU-baseline leg load it. The GPU library shares no code with it and
@@ -364,4 +365,160 @@ void oracle_chunk_sparsification_loss_grad(const float *p, int64_t B, int64_t S,
                     grad[(b * S + k) * E + e] = scale * others;
                 }
         }
+}
+
+/*
+ * Layer backward ([S1]-[S3], [S6]): gradients of
+ *     L = sum_{t,j} dy[t,j] y[t,j]  +  sum_{t,e} dprobs[t,e] probs[t,e]
+ * where y is the chunk-union FFN of x under the router's scores s (computed here in
+ * double from x, W_r, gain, bias, eps) and probs = sigmoid(sharpness * s). dprobs may
+ * be NULL (no probability term). The chain rule on the definitions above:
+ *
+ *   expert e in U_c(t), a = W1_e x_t, h = swish(a), z = W2_e h, y_t += s[t,e] z:
+ *     ds[t,e]  = dy_t . z
+ *     dW2_e   += s[t,e] dy_t h^T
+ *     da       = (s[t,e] W2_e^T dy_t) * swish'(a),  swish'(a) = sig(a) (1 + a (1 - sig(a)))
+ *     dW1_e   += da x_t^T,     dx_t += W1_e^T da
+ *   experts outside U_c(t) are not evaluated: their ds is left 0, which only the
+ *   ReLU-killed (inactive) logits would see;
+ *   probabilities: ds[t,e] += dprobs[t,e] sharpness p (1 - p), p = sigmoid(sharpness s)
+ *   RMSNorm over experts, s_e = g_e r_e inv, inv = (mean_j r_j^2 + eps)^(-1/2):
+ *     dr_j = g_j inv ds_j - inv^3 r_j / E * sum_e g_e r_e ds_e,  dgain_e += ds_e r_e inv
+ *   ReLU: dl = dr where l > 0, else 0 (also at l == 0)
+ *   router linear: dW_r += dl x_t^T, dbias += dl, dx_t += W_r^T dl
+ *
+ * Shapes as in the forward calls; outputs (double, overwritten): dx [T, d_h],
+ * dw_r [E, d_h], dgain [E], dbias [E], dw1 [E, d_e, d_h], dw2 [E, d_h, d_e].
+ * Scratch: logits, scores, ds [T, E] and da [T, E, d_e] doubles (caller-owned).
+ */
+void oracle_layer_backward(const float *x, const float *w_r, const float *gain,
+                           const float *bias, double eps, const float *w1, const float *w2,
+                           int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n,
+                           const float *dy, const float *dprobs, double sharpness,
+                           double *dx, double *dw_r, double *dgain, double *dbias,
+                           double *dw1, double *dw2,
+                           double *logits, double *scores, double *ds, double *da)
+{
+    const int64_t C = (T + n - 1) / n;
+    oracle_router(x, w_r, gain, bias, eps, T, d_h, E, logits, scores);
+    for (int64_t i = 0; i < T * E; ++i)
+        ds[i] = 0.0;
+    for (int64_t i = 0; i < T * E * d_e; ++i)
+        da[i] = 0.0;
+
+    /* experts: each thread owns whole experts, so dW1_e / dW2_e need no locking */
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t e = 0; e < E; ++e) {
+        double *g1 = dw1 + e * d_e * d_h, *g2 = dw2 + e * d_h * d_e;
+        const float *w1e = w1 + e * d_e * d_h, *w2e = w2 + e * d_h * d_e;
+        double a[4096], h[4096], sg[4096];   /* d_e <= 4096 */
+        for (int64_t i = 0; i < d_e * d_h; ++i)
+            g1[i] = 0.0, g2[i] = 0.0;
+        for (int64_t c = 0; c < C; ++c) {
+            const int64_t t0 = c * n, t1 = t0 + n < T ? t0 + n : T;
+            int used = 0;   /* e in U_c: some token of the chunk has a nonzero score */
+            for (int64_t t = t0; t < t1; ++t)
+                if (scores[t * E + e] != 0.0)
+                    used = 1;
+            if (!used)
+                continue;
+            for (int64_t t = t0; t < t1; ++t) {
+                const float *xt = x + t * d_h, *dyt = dy + t * d_h;
+                const double s = scores[t * E + e];
+                for (int64_t k = 0; k < d_e; ++k) {
+                    double acc = 0.0;
+                    for (int64_t j = 0; j < d_h; ++j)
+                        acc += (double)w1e[k * d_h + j] * (double)xt[j];
+                    a[k] = acc;
+                    sg[k] = 1.0 / (1.0 + exp(-acc));
+                    h[k] = acc * sg[k];
+                }
+                /* ds = dy . (W2 h); dW2 += s dy h^T */
+                double dsv = 0.0;
+                for (int64_t j = 0; j < d_h; ++j) {
+                    double z = 0.0;
+                    for (int64_t k = 0; k < d_e; ++k)
+                        z += (double)w2e[j * d_e + k] * h[k];
+                    dsv += (double)dyt[j] * z;
+                    for (int64_t k = 0; k < d_e; ++k)
+                        g2[j * d_e + k] += s * (double)dyt[j] * h[k];
+                }
+                ds[t * E + e] = dsv;
+                /* da = (s W2^T dy) * swish'(a); dW1 += da x^T */
+                double *dat = da + (t * E + e) * d_e;
+                for (int64_t k = 0; k < d_e; ++k) {
+                    double dh = 0.0;
+                    for (int64_t j = 0; j < d_h; ++j)
+                        dh += (double)w2e[j * d_e + k] * s * (double)dyt[j];
+                    dat[k] = dh * (sg[k] * (1.0 + a[k] * (1.0 - sg[k])));
+                    for (int64_t j = 0; j < d_h; ++j)
+                        g1[k * d_h + j] += dat[k] * (double)xt[j];
+                }
+            }
+        }
+    }
+
+    /* per token: dx from the experts, then the router */
+#pragma omp parallel for schedule(static)
+    for (int64_t t = 0; t < T; ++t) {
+        double *dxt = dx + t * d_h;
+        for (int64_t j = 0; j < d_h; ++j)
+            dxt[j] = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            const double *dat = da + (t * E + e) * d_e;
+            const float *w1e = w1 + e * d_e * d_h;
+            for (int64_t k = 0; k < d_e; ++k)
+                if (dat[k] != 0.0)
+                    for (int64_t j = 0; j < d_h; ++j)
+                        dxt[j] += (double)w1e[k * d_h + j] * dat[k];
+        }
+        double *dst = ds + t * E;
+        const double *lt = logits + t * E;
+        if (dprobs)
+            for (int64_t e = 0; e < E; ++e) {
+                const double p = 1.0 / (1.0 + exp(-sharpness * scores[t * E + e]));
+                dst[e] += (double)dprobs[t * E + e] * sharpness * p * (1.0 - p);
+            }
+        double sumsq = 0.0, coup = 0.0;
+        for (int64_t e = 0; e < E; ++e) {
+            const double r = lt[e] > 0.0 ? lt[e] : 0.0;
+            sumsq += r * r;
+        }
+        const double inv = 1.0 / sqrt(sumsq / (double)E + eps);
+        for (int64_t e = 0; e < E; ++e) {
+            const double r = lt[e] > 0.0 ? lt[e] : 0.0;
+            coup += (gain ? (double)gain[e] : 1.0) * r * dst[e];
+        }
+        /* dl (kept in ds's row: dst[e] becomes dl[t,e] after the gain term is read) */
+        for (int64_t e = 0; e < E; ++e) {
+            const int active = lt[e] > 0.0;
+            const double r = active ? lt[e] : 0.0;
+            const double g = gain ? (double)gain[e] : 1.0;
+            const double dr = g * inv * dst[e] - inv * inv * inv * r / (double)E * coup;
+            /* keep ds_e * r_e * inv for dgain in the logit's slot (the logit is no longer
+               needed), dl in ds's slot */
+            logits[t * E + e] = dst[e] * r * inv;
+            dst[e] = active ? dr : 0.0;
+        }
+        for (int64_t e = 0; e < E; ++e)
+            for (int64_t j = 0; j < d_h; ++j)
+                dxt[j] += (double)w_r[e * d_h + j] * dst[e];
+    }
+
+    /* router parameters: sums over tokens in ascending order */
+#pragma omp parallel for schedule(static)
+    for (int64_t e = 0; e < E; ++e) {
+        double gsum = 0.0, bsum = 0.0;
+        for (int64_t j = 0; j < d_h; ++j)
+            dw_r[e * d_h + j] = 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const double dl = ds[t * E + e];
+            gsum += logits[t * E + e];
+            bsum += dl;
+            for (int64_t j = 0; j < d_h; ++j)
+                dw_r[e * d_h + j] += dl * (double)x[t * d_h + j];
+        }
+        dgain[e] = gsum;
+        dbias[e] = bsum;
+    }
 }

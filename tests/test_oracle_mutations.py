@@ -9,6 +9,7 @@ import os
 import pytest
 
 import oracle
+import test_oracle_backward_pins as bpins
 import test_oracle_loss_pins as lpins
 import test_oracle_pins as pins
 
@@ -72,6 +73,30 @@ MUTATIONS = [
      "double dn = -(c / (nx + LOSS_LOG_EPS) - (1.0 - c) / (1.0 - nx + LOSS_LOG_EPS));",
      "double dn = (c / (nx + LOSS_LOG_EPS) - (1.0 - c) / (1.0 - nx + LOSS_LOG_EPS));"),
     ("sparsification grad includes its own factor", "if (j != k)", "if (1)"),
+    ("backward: swish slope without its second term",
+     "dat[k] = dh * (sg[k] * (1.0 + a[k] * (1.0 - sg[k])));", "dat[k] = dh * sg[k];"),
+    ("backward: dW2 without the score", "g2[j * d_e + k] += s * (double)dyt[j] * h[k];",
+     "g2[j * d_e + k] += (double)dyt[j] * h[k];"),
+    ("backward: hidden gradient without the score",
+     "dh += (double)w2e[j * d_e + k] * s * (double)dyt[j];",
+     "dh += (double)w2e[j * d_e + k] * (double)dyt[j];"),
+    ("backward: rmsnorm coupling sign",
+     "const double dr = g * inv * dst[e] - inv * inv * inv * r / (double)E * coup;",
+     "const double dr = g * inv * dst[e] + inv * inv * inv * r / (double)E * coup;"),
+    ("backward: rmsnorm coupling without 1/E",
+     "const double dr = g * inv * dst[e] - inv * inv * inv * r / (double)E * coup;",
+     "const double dr = g * inv * dst[e] - inv * inv * inv * r * coup;"),
+    ("backward: relu gate dropped", "dst[e] = active ? dr : 0.0;", "dst[e] = dr;"),
+    ("backward: probability slope without sharpness",
+     "dst[e] += (double)dprobs[t * E + e] * sharpness * p * (1.0 - p);",
+     "dst[e] += (double)dprobs[t * E + e] * p * (1.0 - p);"),
+    ("backward: gain gradient without the norm", "logits[t * E + e] = dst[e] * r * inv;",
+     "logits[t * E + e] = dst[e] * r;"),
+    ("backward: router term of dx dropped",
+     "dxt[j] += (double)w_r[e * d_h + j] * dst[e];", "dxt[j] += 0.0 * dst[e];"),
+    ("backward: dW_r from the wrong token row",
+     "dw_r[e * d_h + j] += dl * (double)x[t * d_h + j];",
+     "dw_r[e * d_h + j] += dl * (double)x[(T - 1 - t) * d_h + j];"),
 ]
 
 PIN_TESTS = [
@@ -96,6 +121,8 @@ PIN_TESTS = [
     lambda: lpins.test_locality_grad_finite_differences(2.0),
     lambda: lpins.test_sparsification_grad_finite_differences(9, 4),
     lpins.test_sparsification_grad_closed_forms,
+    lambda: bpins.test_backward_matches_torch_autograd(bpins.CASES[0]),
+    lambda: bpins.test_backward_matches_torch_autograd(bpins.CASES[1]),
 ]
 
 
