@@ -356,6 +356,126 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain, router_o
             "achieved_gbs": l_bytes / (l_ms * 1e-3) / 1e9,
             "frac_of_hbm_peak": l_bytes / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rotation_sets": l_sets}
+    res.update(bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts,
+                              time_replays))
+    return res
+
+
+def bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts, time_replays):
+    """The layer backward (router recomputed, expert pass, weight gradients, dx, router
+    backward) at the workload's size over the same rotation, and at 2048 tokens. The
+    roofline figures: flops of the five expert products per (chunk, union expert)
+    plus the router's two, and the bytes of the unique weights read, x and dy read,
+    and dx, dW_r, dW1, dW2 written (fp32)."""
+    T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
+    dev = torch.device("cuda:0")
+    nc, nd = len(copies), len(draws)
+    f32 = torch.float32
+    res = {}
+
+    def outputs(Tb):
+        return dict(dx=torch.empty((Tb, d_h), dtype=f32, device=dev),
+                    dw_r=torch.empty((E, d_h), dtype=f32, device=dev),
+                    dw1=torch.empty((E, d_e, d_h), dtype=f32, device=dev),
+                    dw2=torch.empty((E, d_h, d_e), dtype=f32, device=dev),
+                    dgain=torch.empty(E, dtype=f32, device=dev),
+                    dbias=torch.empty(E, dtype=f32, device=dev))
+
+    def figures(Tb, union_sum, used_experts, ms):
+        flops = union_sum * 10.0 * d_h * d_e * min(n, Tb) + 4.0 * Tb * E * d_h
+        nbytes = (used_experts * 2 * d_h * d_e * 2 + 2 * Tb * d_h * 2 + Tb * d_h * 4 +
+                  E * d_h * 4 + 2 * E * d_e * d_h * 4)
+        return {"avg_launch_us": ms * 1e3, "algorithmic_flops": flops,
+                "algorithmic_bytes": nbytes,
+                "achieved_tflops": flops / (ms * 1e-3) / 1e12,
+                "mfma_frac": flops / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                "achieved_gbs": nbytes / (ms * 1e-3) / 1e9,
+                "hbm_frac": nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+
+    # (1) the workload's own size, rotating weight copies and draws (dy = another draw)
+    bws = torch.empty(bf.blockffn_layer_backward_workspace_bytes(T, d_h, E, d_e, n),
+                      dtype=torch.uint8, device=dev)
+    out = outputs(T)
+
+    def bwd(i):
+        w = copies[i % nc]
+        d = draws[i % nd]
+        bf.blockffn_layer_backward(d["x"], w["w_r"], w["w1"], w["w2"], draws[(i + 1) % nd]["x"],
+                                   n, gain=gain, bias=w["bias"], out=out, workspace=bws)
+
+    S = 16
+    for i in range(2):
+        bwd(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(S):
+            bwd(i)
+    time_replays(g, 2)
+    ms = time_replays(g, 10) / (10 * S)
+    del g
+    # unions of the router's scores: the backward recomputes them; count from a forward
+    sc = torch.empty((T, E), dtype=f32, device=dev)
+    cnt = torch.zeros(-(-T // n), dtype=torch.int32, device=dev)
+    lists = torch.empty((-(-T // n), E), dtype=torch.int32, device=dev)
+    union_sum, used = 0.0, 0.0
+    y = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
+    for i in range(S):
+        w = copies[i % nc]
+        d = draws[i % nd]
+        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=sc)
+        bf.blockffn_chunk_ffn(d["x"], sc, w["w1"], w["w2"], n, y=y, union_counts=cnt,
+                              expert_lists=lists)
+        c = cnt.cpu().numpy()
+        union_sum += float(c.sum())
+        used += float(len(set(lists.cpu().numpy()[lists.cpu().numpy() >= 0].tolist())))
+    res["layer_backward"] = dict(
+        shape=f"T={T} d_h={d_h} E={E} d_e={d_e} n={n} bf16, router scores (logit shift "
+              f"for ~80% zeros), fp32 gradients", **figures(T, union_sum / S, used / S, ms))
+
+    # (2) 2048 tokens on two weight copies
+    Tp = 2048
+    rng = np.random.default_rng(77)
+    xs = [torch.from_numpy(inputs.gaussian(rng, (Tp, d_h), 1.0, True)).to(dev, torch.bfloat16)
+          for _ in range(2)]
+    dys = [torch.from_numpy(inputs.gaussian(rng, (Tp, d_h), 1.0, True)).to(dev, torch.bfloat16)
+           for _ in range(2)]
+    bws = torch.empty(bf.blockffn_layer_backward_workspace_bytes(Tp, d_h, E, d_e, n),
+                      dtype=torch.uint8, device=dev)
+    outp = outputs(Tp)
+
+    def bwdp(i):
+        w = copies[i % 2]
+        bf.blockffn_layer_backward(xs[i % 2], w["w_r"], w["w1"], w["w2"], dys[i % 2], n,
+                                   gain=gain, bias=w["bias"], out=outp, workspace=bws)
+
+    for i in range(2):
+        bwdp(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(4):
+            bwdp(i)
+    time_replays(g, 2)
+    ms = time_replays(g, 5) / (5 * 4)
+    del g
+    scp = torch.empty((Tp, E), dtype=f32, device=dev)
+    Cp = -(-Tp // n)
+    cntp = torch.zeros(Cp, dtype=torch.int32, device=dev)
+    listp = torch.empty((Cp, E), dtype=torch.int32, device=dev)
+    yp = torch.empty((Tp, d_h), dtype=torch.bfloat16, device=dev)
+    usum, used = 0.0, 0.0
+    for i in range(2):
+        w = copies[i]
+        bf.blockffn_router(xs[i], w["w_r"], gain, w["bias"], scores=scp)
+        bf.blockffn_chunk_ffn(xs[i], scp, w["w1"], w["w2"], n, y=yp, union_counts=cntp,
+                              expert_lists=listp)
+        usum += float(cntp.cpu().numpy().sum())
+        lp = listp.cpu().numpy()
+        used += float(len(set(lp[lp >= 0].tolist())))
+    res["layer_backward_T2048"] = dict(
+        shape=f"T={Tp} d_h={d_h} E={E} d_e={d_e} n={n} bf16, router scores, fp32 gradients",
+        **figures(Tp, usum / 2, used / 2, ms))
     return res
 
 

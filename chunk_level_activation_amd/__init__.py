@@ -23,6 +23,7 @@ __all__ = [
     "blockffn_chunk_ffn", "blockffn_chunk_ffn_workspace_bytes",
     "blockffn_chunk_ffn_workspace", "blockffn_add_layernorm", "blockffn_sparsity_losses",
     "blockffn_sparsity_losses_workspace_bytes", "blockffn_sparsity_losses_workspace",
+    "blockffn_layer_backward", "blockffn_layer_backward_workspace_bytes",
     "blockffn_last_error", "blockffn_version", "load_library",
 ]
 
@@ -73,6 +74,11 @@ def load_library():
     lib.blockffn_sparsity_losses.argtypes = [P, I64, I64, I64, F, I64, F, F, P, P, P,
                                              ctypes.c_size_t, P]
     lib.blockffn_sparsity_losses.restype = I
+    lib.blockffn_layer_backward_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.blockffn_layer_backward_workspace_bytes.restype = ctypes.c_size_t
+    lib.blockffn_layer_backward.argtypes = [P, P, P, P, F, P, P, I64, I64, I64, I64, I64, I, P,
+                                            P, F, P, P, P, P, P, P, P, ctypes.c_size_t, P]
+    lib.blockffn_layer_backward.restype = I
     lib.blockffn_last_error.argtypes = []
     lib.blockffn_last_error.restype = ctypes.c_char_p
     lib.blockffn_version.argtypes = []
@@ -275,3 +281,55 @@ def blockffn_sparsity_losses(probs, alpha: float = 2.0, L: int = 8, lambda_al: f
             workspace.numel() * workspace.element_size(), _stream(stream)]
     _check(lib.blockffn_sparsity_losses(*args))
     return losses, grad
+
+
+def blockffn_layer_backward_workspace_bytes(T: int, d_h: int, E: int, d_e: int, n: int,
+                                            dtype: int = BLOCKFFN_BF16) -> int:
+    nbytes = load_library().blockffn_layer_backward_workspace_bytes(T, d_h, E, d_e, n, dtype)
+    if nbytes == 0:
+        raise BlockFFNError(2, blockffn_last_error())
+    return int(nbytes)
+
+
+def blockffn_layer_backward(x, w_r, w1, w2, dy, n: int, gain=None, bias=None,
+                            eps: float = FP32_EPS, *, dprobs=None, sharpness: float = 1.0,
+                            want_gain=True, want_bias=True, out=None, workspace=None,
+                            stream=None):
+    """Gradients of sum(dy * y) + sum(dprobs * probs) for the layer (see blockffn.h):
+    a dict of float32 tensors dx [T, d_h], dw_r [E, d_h], dw1 [E, d_e, d_h],
+    dw2 [E, d_h, d_e], dgain [E] and dbias [E] (the last two when asked for). x, w_r,
+    w1, w2 and dy are bfloat16. `out` may hold preallocated output tensors under
+    those names."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    E, d_e, _ = w1.shape
+    if tuple(w_r.shape) != (E, d_h) or tuple(w2.shape) != (E, d_h, d_e) or \
+            tuple(dy.shape) != (T, d_h):
+        raise ValueError("w_r [E, d_h], w2 [E, d_h, d_e] and dy [T, d_h] expected")
+    code = _dtype_code(x)
+    dev = x.device
+    f32 = torch.float32
+    shapes = dict(dx=(T, d_h), dw_r=(E, d_h), dw1=(E, d_e, d_h), dw2=(E, d_h, d_e))
+    if want_gain:
+        shapes["dgain"] = (E,)
+    if want_bias:
+        shapes["dbias"] = (E,)
+    out = dict(out or {})
+    for k, shp in shapes.items():
+        if k not in out:
+            out[k] = torch.empty(shp, dtype=f32, device=dev)
+        elif tuple(out[k].shape) != shp or out[k].dtype != f32:
+            raise ValueError(f"out[{k!r}] must be float32 {shp}")
+    nbytes = blockffn_layer_backward_workspace_bytes(T, d_h, E, d_e, n, code)
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", f32), _dev(bias, "bias", f32),
+            float(eps), _dev(w1, "w1"), _dev(w2, "w2"), T, d_h, E, d_e, int(n), code,
+            _dev(dy, "dy", x.dtype), _dev(dprobs, "dprobs", f32), float(sharpness),
+            _dev(out["dx"], "dx"), _dev(out["dw_r"], "dw_r"), _dev(out.get("dgain"), "dgain"),
+            _dev(out.get("dbias"), "dbias"), _dev(out["dw1"], "dw1"), _dev(out["dw2"], "dw2"),
+            _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+            _stream(stream)]
+    _check(lib.blockffn_layer_backward(*args))
+    return out

@@ -392,4 +392,88 @@ blockffn_status_t blockffn_sparsity_losses(const float *probs, int64_t B, int64_
     return BLOCKFFN_OK;
 }
 
+size_t blockffn_layer_backward_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                               int64_t n, int dtype)
+{
+    if (check_dtype(dtype) != BLOCKFFN_OK)
+        return 0;
+    if (dtype != BLOCKFFN_BF16) {
+        fail(BLOCKFFN_EUNSUPPORTED, "the layer backward takes bf16 inputs only");
+        return 0;
+    }
+    if (!blockffn::backward_supported(T, d_h, E, d_e, n)) {
+        fail(BLOCKFFN_EUNSUPPORTED, "layer backward needs T, n >= 1, 1 <= E <= 256, "
+                                    "d_h % 256 == 0 and d_e % 128 == 0 (and 32-bit offsets)");
+        return 0;
+    }
+    return blockffn::backward_workspace_bytes(T, d_h, E, d_e, n);
+}
+
+blockffn_status_t blockffn_layer_backward(const void *x, const void *w_r, const float *gain,
+                                          const float *bias, float eps, const void *w1,
+                                          const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                          int64_t d_e, int64_t n, int dtype, const void *dy,
+                                          const float *dprobs, float sharpness, float *dx,
+                                          float *dw_r, float *dgain, float *dbias, float *dw1,
+                                          float *dw2, void *workspace, size_t workspace_bytes,
+                                          void *stream)
+{
+    blockffn_status_t st = check_dtype(dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if (!x || !w_r || !w1 || !w2 || !dy || !dx || !dw_r || !dw1 || !dw2 || !workspace)
+        return fail(BLOCKFFN_EINVAL,
+                    "x, w_r, w1, w2, dy, dx, dw_r, dw1, dw2 and workspace must not be NULL");
+    if (T <= 0 || d_h <= 0 || E <= 0 || d_e <= 0 || n <= 0)
+        return fail(BLOCKFFN_EINVAL, "T, d_h, E, d_e and n must be positive");
+    if (!(eps >= 0.0f) || !std::isfinite(eps) || !std::isfinite(sharpness))
+        return fail(BLOCKFFN_EINVAL, "eps must be finite and >= 0, sharpness finite");
+    if (dtype != BLOCKFFN_BF16)
+        return fail(BLOCKFFN_EUNSUPPORTED, "the layer backward takes bf16 inputs only");
+    if (!blockffn::backward_supported(T, d_h, E, d_e, n))
+        return fail(BLOCKFFN_EUNSUPPORTED, "layer backward needs 1 <= E <= 256, d_h % 256 == 0 "
+                                           "and d_e % 128 == 0 (and 32-bit offsets)");
+    if (!aligned(x, 16) || !aligned(w_r, 16) || !aligned(w1, 16) || !aligned(w2, 16) ||
+        !aligned(dy, 16) || !aligned(dx, 16) || !aligned(dw_r, 4) || !aligned(dw1, 4) ||
+        !aligned(dw2, 4) || (gain && !aligned(gain, 4)) || (bias && !aligned(bias, 4)) ||
+        (dgain && !aligned(dgain, 4)) || (dbias && !aligned(dbias, 4)) ||
+        (dprobs && !aligned(dprobs, 4)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x, w_r, w1, w2, dy and dx must be 16-byte aligned, "
+                                           "float arrays 4-byte aligned");
+    if (!aligned(workspace, 256))
+        return fail(BLOCKFFN_EUNSUPPORTED, "workspace needs 256-byte alignment");
+    const size_t need = blockffn::backward_workspace_bytes(T, d_h, E, d_e, n);
+    if (workspace_bytes < need)
+        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                             " bytes, needs " + std::to_string(need));
+    blockffn::BackwardArgs b;
+    b.x = static_cast<const uint16_t *>(x);
+    b.w_r = static_cast<const uint16_t *>(w_r);
+    b.w1 = static_cast<const uint16_t *>(w1);
+    b.w2 = static_cast<const uint16_t *>(w2);
+    b.dy = static_cast<const uint16_t *>(dy);
+    b.gain = gain;
+    b.bias = bias;
+    b.dprobs = dprobs;
+    b.eps = eps;
+    b.sharpness = sharpness;
+    b.T = T;
+    b.d_h = d_h;
+    b.E = E;
+    b.d_e = d_e;
+    b.n = n;
+    b.dx = dx;
+    b.dw_r = dw_r;
+    b.dgain = dgain;
+    b.dbias = dbias;
+    b.dw1 = dw1;
+    b.dw2 = dw2;
+    const hipError_t err =
+        blockffn::launch_layer_backward(b, workspace, static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("backward launch failed: ") + hipGetErrorString(err));
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
 }  // extern "C"

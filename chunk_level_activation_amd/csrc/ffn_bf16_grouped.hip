@@ -358,6 +358,24 @@ size_t grouped_tile_bytes(int64_t CT, int64_t E)
     return (size_t)E * CT * 4 + (size_t)E * 4;
 }
 
+hipError_t launch_expert_tiles(const FfnPlan &p, const uint64_t *masks, int32_t *tile_list,
+                               int32_t *tile_count, hipStream_t stream)
+{
+    GroupedArgs a{};
+    a.masks = masks;
+    a.tile_list = tile_list;
+    a.tile_count = tile_count;
+    a.T = p.T;
+    a.n = (int)p.n;
+    a.E = (int)p.E;
+    a.C = (int)p.C;
+    a.MPC = (int)p.MPC;
+    a.CT = (int)p.CT;
+    a.W = (int)p.W;
+    hipLaunchKernelGGL(expert_tiles_kernel, dim3((unsigned)p.E), dim3(256), 0, stream, a);
+    return hipGetLastError();
+}
+
 hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const float *scores,
                                    const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *ws,
                                    uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,

@@ -123,6 +123,10 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
                                    const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *ws,
                                    uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,
                                    hipStream_t stream);
+// Per-expert ascending lists of the 32-token chunk tiles whose chunk uses the expert
+// (tile_list [E][CT], tile_count [E]) from the chunk union masks [C][W].
+hipError_t launch_expert_tiles(const FfnPlan &p, const uint64_t *masks, int32_t *tile_list,
+                               int32_t *tile_count, hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnPlan &p, const float *x, const float *scores,
                           const float *w1, const float *w2, float *y, void *ws,
                           hipStream_t stream);
@@ -162,5 +166,17 @@ size_t sparsity_losses_workspace_bytes(int64_t B, int64_t S, int64_t E, int64_t 
 hipError_t launch_sparsity_losses(const float *p, int64_t B, int64_t S, int64_t E, float alpha,
                                   int64_t L, float lambda_al, float lambda_cs, float *losses,
                                   float *grad, void *ws, hipStream_t stream);
+
+// Layer backward (bf16): sizes it takes, workspace bytes, launches.
+bool backward_supported(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n);
+size_t backward_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n);
+struct BackwardArgs {
+    const uint16_t *x, *w_r, *w1, *w2, *dy;
+    const float *gain, *bias, *dprobs;
+    float eps, sharpness;
+    int64_t T, d_h, E, d_e, n;
+    float *dx, *dw_r, *dgain, *dbias, *dw1, *dw2;
+};
+hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t stream);
 
 }  // namespace blockffn

@@ -196,6 +196,52 @@ blockffn_status_t blockffn_sparsity_losses(const float *probs, int64_t B, int64_
                                            float lambda_cs, float *losses, float *grad,
                                            void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * Bytes of workspace blockffn_layer_backward needs (0 when the sizes are invalid or
+ * unsupported).
+ */
+size_t blockffn_layer_backward_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                               int64_t n, int dtype);
+
+/*
+ * Layer backward (skill page, "Architecture Overview": the ReLU + RMSNorm router is
+ * differentiable and trained end to end; "Core Concept"; "Router Architecture
+ * Setup"): the gradients of
+ *     L = sum_{t,j} dy[t,j] y[t,j] + sum_{t,e} dprobs[t,e] probs[t,e]
+ * where y = blockffn_chunk_ffn(x, scores, W1, W2, n) with scores from
+ * blockffn_router(x, W_r, gain, bias, eps) and probs = sigmoid(sharpness * scores).
+ * The router is recomputed inside the call. By the chain rule, for e in U_c(t) with
+ * a = W1_e x_t and h = swish(a):
+ *     ds[t,e] = dy_t . W2_e h,   dW2_e += s dy_t h^T,
+ *     da = s (W2_e^T dy_t) * swish'(a),   dW1_e += da x_t^T,   dx_t += W1_e^T da;
+ * then ds += dprobs sharpness p (1 - p), the RMSNorm backward over the experts, the
+ * ReLU (derivative 0 where the logit is not > 0) and the router linear:
+ *     dW_r += dl x_t^T,  dbias += dl,  dx_t += W_r^T dl,  dgain_e += ds r / rms.
+ *
+ *   x, w_r, gain, bias, eps, w1, w2, T, d_h, E, d_e, n: as in the forward calls
+ *   dtype   BLOCKFFN_BF16 only (x, w_r, w1, w2, dy bf16); others return EUNSUPPORTED
+ *   dy      [T, d_h] bf16   gradient of y
+ *   dprobs  [T, E] float or NULL (no probability term); sharpness as in the router
+ *   dx      [T, d_h] float, written (16-byte aligned)
+ *   dw_r    [E, d_h] float, dw1 [E, d_e, d_h] float, dw2 [E, d_h, d_e] float: written
+ *           (experts no chunk uses get zeros)
+ *   dgain, dbias  [E] float or NULL: written when given
+ *   workspace, workspace_bytes: at least blockffn_layer_backward_workspace_bytes(...),
+ *           256-byte aligned, scratch only (no zero-fill needed); calls that may run
+ *           concurrently need separate workspaces.
+ * Needs 1 <= E <= 256, d_h % 256 == 0, d_e % 128 == 0. fp32 accumulation; the
+ * recomputed hidden activations and their gradients are rounded to bf16 before the
+ * weight-gradient and dx products. Every sum runs in a fixed order.
+ */
+blockffn_status_t blockffn_layer_backward(const void *x, const void *w_r, const float *gain,
+                                          const float *bias, float eps, const void *w1,
+                                          const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                          int64_t d_e, int64_t n, int dtype, const void *dy,
+                                          const float *dprobs, float sharpness, float *dx,
+                                          float *dw_r, float *dgain, float *dbias, float *dw1,
+                                          float *dw2, void *workspace, size_t workspace_bytes,
+                                          void *stream);
+
 /* Message describing the calling thread's last non-OK status ("" if none). */
 const char *blockffn_last_error(void);
 

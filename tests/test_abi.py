@@ -196,3 +196,34 @@ def test_product_path_has_no_oracle_dependency():
                 assert "oracle" not in text.lower(), fn
     deps = os.popen(f"ldd {bf.library_path}").read()
     assert "liboracle" not in deps
+
+
+def backward(lib, x=FAKE, w_r=FAKE, gain=None, bias=None, eps=1e-6, w1=FAKE, w2=FAKE, T=64,
+             d_h=2048, E=64, d_e=128, n=32, dtype=1, dy=FAKE, dprobs=None, sharpness=1.0,
+             dx=FAKE, dw_r=FAKE, dgain=None, dbias=None, dw1=FAKE, dw2=FAKE, ws=FAKE,
+             ws_bytes=1 << 40):
+    return lib.blockffn_layer_backward(x, w_r, gain, bias, eps, w1, w2, T, d_h, E, d_e, n, dtype,
+                                       dy, dprobs, sharpness, dx, dw_r, dgain, dbias, dw1, dw2,
+                                       ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(dy=None), 1), (dict(dx=None), 1), (dict(dw1=None), 1),
+    (dict(ws=None), 1), (dict(T=0), 1), (dict(n=0), 1), (dict(dtype=5), 1),
+    (dict(eps=-1.0), 1), (dict(sharpness=float("nan")), 1),
+    (dict(dtype=0), 2), (dict(d_h=2080), 2), (dict(d_e=64), 2), (dict(E=300), 2),
+    (dict(x=FAKE + 8), 2), (dict(dx=FAKE + 4), 2), (dict(ws=FAKE + 16), 2),
+    (dict(ws_bytes=4096), 3),
+])
+def test_layer_backward_rejects(lib, kw, status):
+    assert backward(lib, **kw) == status
+    assert bf.blockffn_last_error() != ""
+
+
+def test_layer_backward_workspace_query(lib):
+    f = lib.blockffn_layer_backward_workspace_bytes
+    # hidden-activation gradients in three layouts dominate: 3 x CT x E x 32 x d_e bf16
+    assert f(2048, 2048, 64, 128, 32, 1) >= 3 * 64 * 64 * 32 * 128 * 2
+    assert f(2048, 2048, 64, 128, 32, 0) == 0      # bf16 only
+    assert f(2048, 2048, 64, 64, 32, 1) == 0       # d_e % 128
+    assert f(0, 2048, 64, 128, 32, 1) == 0
