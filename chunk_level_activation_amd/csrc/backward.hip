@@ -23,13 +23,16 @@
 //      [tile][d_h][32 tokens], so the weight-gradient products, whose k is the token,
 //      read k-contiguous operands;
 //   2. expert_pass_kernel, workgroup = (expert e, 4 of its tiles): a = X W1_e^T and
-//      G = DY W2_e over d_h (W2 tiles transposed in LDS), then ds, and dA and SH in bf16
-//      in both [token][unit] and [unit][token] order;
+//      G = DY W2_e over d_h (B = W2^T rows), then ds, and dA and SH in bf16 in both
+//      [token][unit] and [unit][token] order;
 //   3. wgrad_kernel, workgroup = (expert, dW1 or dW2, 128 x 128 output tile): k over the
 //      expert's tiles' tokens; every output element is owned by one workgroup (an
 //      expert no chunk uses gets zeros);
-//   4. dx_kernel, workgroup = (tile, 256 columns): k over the chunk's union experts x
-//      d_e (W1 tiles transposed in LDS);
+//   4. dx_kernel, workgroup = (4 tiles, 128 columns, expert split): k over the union of
+//      the 4 chunks' unions x d_e, B = W1^T rows (W1 and W2 are transposed once per call
+//      into the workspace, for the experts some chunk uses, so every product reads
+//      k-contiguous operands); with few tiles the experts are split over workgroups
+//      and the fp32 partials added in split order;
 //   5. router_token_kernel: per token, dl and the router's share of dx;
 //      router_param_kernel: dW_r, dgain, dbias as sums over the tokens in order.
 // Every sum runs in a fixed order, so equal inputs give equal bits.
@@ -77,37 +80,28 @@ __device__ __forceinline__ void zero_acc(f32x16 &a)
         a[v] = 0.0f;
 }
 
-// One k step (kBK = 32) of a wave's 64 x 64 block: rows [wm*64, +64) of As, columns
-// [wn*64, +64) of Bs, both stored [row][k] with pitch kLP.
+// One k step (BK) of a wave's 64 x 64 block: rows [wm*64, +64) of As, columns
+// [wn*64, +64) of Bs, both stored [row][k] with pitch BK + 8.
+template <int BK>
 __device__ __forceinline__ void mma_64x64(const uint16_t *As, const uint16_t *Bs, f32x16 (&acc)[2][2],
                                           int wm, int wn, int lane)
 {
+    constexpr int P = BK + 8;
     const int r = lane & 31, kg = lane >> 5;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
+    for (int ks = 0; ks < BK / 16; ++ks) {
         bf16x8 a[2], b[2];
 #pragma unroll
         for (int i = 0; i < 2; ++i)
-            a[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * 64 + i * 32 + r) * kLP + ks * 16 + kg * 8]);
+            a[i] = *reinterpret_cast<const bf16x8 *>(&As[(wm * 64 + i * 32 + r) * P + ks * 16 + kg * 8]);
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * 64 + j * 32 + r) * kLP + ks * 16 + kg * 8]);
+            b[j] = *reinterpret_cast<const bf16x8 *>(&Bs[(wn * 64 + j * 32 + r) * P + ks * 16 + kg * 8]);
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
             for (int j = 0; j < 2; ++j)
                 acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-}
-
-// Stores eight bf16 values (one 16-byte global load of 8 consecutive n at one k) into
-// a [n][k] LDS tile: element i goes to row n0 + i, column k.
-__device__ __forceinline__ void store_transposed(uint16_t *S, int n0, int k, u32x4 v)
-{
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        S[(n0 + 2 * q) * kLP + k] = (uint16_t)(v[q] & 0xffffu);
-        S[(n0 + 2 * q + 1) * kLP + k] = (uint16_t)(v[q] >> 16);
     }
 }
 
@@ -143,15 +137,49 @@ __global__ void __launch_bounds__(kBT) transpose_tiles_kernel(const uint16_t *sr
     }
 }
 
+// Per expert, dst[e] = src[e]^T for an R x Cc bf16 matrix (64 x 64 blocks through LDS);
+// experts that no chunk uses are skipped (their copy is never read).
+__global__ void __launch_bounds__(kBT) transpose_weights_kernel(const uint16_t *src, int R, int Cc,
+                                                                const int32_t *tile_count,
+                                                                uint16_t *dst)
+{
+    __shared__ uint16_t t[64][64 + 8];
+    const int e = blockIdx.z;
+    if (tile_count[e] == 0)
+        return;
+    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
+    const uint16_t *s = src + (int64_t)e * R * Cc;
+    uint16_t *o = dst + (int64_t)e * R * Cc;
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int v = q * kBT + tid, row = v / 8, cv = v % 8;
+        *reinterpret_cast<u32x4 *>(&t[row][cv * 8]) =
+            *reinterpret_cast<const u32x4 *>(&s[(int64_t)(r0 + row) * Cc + c0 + cv * 8]);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+        const int v = q * kBT + tid, col = v / 8, rv = v % 8;
+        u32x4 w;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            w[i] = (uint32_t)t[rv * 8 + 2 * i][col] | ((uint32_t)t[rv * 8 + 2 * i + 1][col] << 16);
+        *reinterpret_cast<u32x4 *>(&o[(int64_t)(c0 + col) * R + r0 + rv * 8]) = w;
+    }
+}
+
 // ------------------------------------------------------------------ 2. expert pass
 struct PassArgs {
-    const uint16_t *x, *dy, *w1, *w2;
+    const uint16_t *x, *dy, *w1, *w2t;    // w2t [E][d_e][d_h]: W2 transposed
     const float *scores;          // recomputed forward scores [T][E]
     const int32_t *tile_list, *tile_count;
     float *ds;                    // [T][E], written for e in U_c(t)
     uint16_t *da_tu, *da_ut, *sh_ut;
     Dims d;
 };
+
+constexpr int kPK = 64;                   // expert pass: k per staged step
+constexpr int kPP = kPK + 8;              // its LDS pitch (bf16): 144 bytes
 
 __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
 {
@@ -160,7 +188,7 @@ __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
     const int cnt = a.tile_count[e];
     if (grp * kPassTiles >= cnt)
         return;
-    __shared__ uint16_t As1[kTM * kLP], Bs1[kTM * kLP], As2[kTM * kLP], Bs2[kTM * kLP];
+    __shared__ uint16_t As1[kTM * kPP], Bs1[kTM * kPP], As2[kTM * kPP], Bs2[kTM * kPP];
     __shared__ float red[kTM][65];
     __shared__ float dsacc[kTM], scol[kTM];
     __shared__ int64_t tok[kTM];
@@ -181,25 +209,21 @@ __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)d.T * d.d_h * 2);
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, (uint64_t)d.T * d.d_h * 2);
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
-    const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(a.w2, (uint64_t)d.E * d.d_h * d.d_e * 2);
-    // k-contiguous staging: vector q = tid + 256 i is row q / 4, k offset (q % 4) * 8.
-    // Transposed W2 staging: wave group g = 2 wave + i covers k [8 (g % 4), +8) x
-    // n [64 (g / 4), +64); lane: k = lane % 8, n = 8 (lane / 8) .. +8.
-    int srow[2], skv[2], tk[2], tn[2];
-    uint32_t xoff[2], dyoff[2];
+    const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(a.w2t, (uint64_t)d.E * d.d_e * d.d_h * 2);
+    // staging: vector q = tid + 256 i (i < 4) is row q / 8, k offset (q % 8) * 8; all four
+    // operands are k-contiguous rows (x, dy: tokens; W1, W2^T: hidden units)
+    constexpr int kV = kTM * kPK / 8 / kBT;    // 4 vectors per thread per operand
+    int srow[kV], skv[kV];
+    uint32_t xoff[kV];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < kV; ++i) {
         const int q = tid + i * kBT;
-        srow[i] = q >> 2;
-        skv[i] = (q & 3) * 8;
+        srow[i] = q >> 3;
+        skv[i] = (q & 7) * 8;
         const int64_t t = tok[srow[i]];
         xoff[i] = t >= 0 ? (uint32_t)((t * d.d_h + skv[i]) * 2) : kOOB;
-        dyoff[i] = xoff[i];
-        const int g = 2 * wave + i;
-        tk[i] = (g & 3) * 8 + (lane & 7);
-        tn[i] = (g >> 2) * 64 + (lane >> 3) * 8;
     }
-    const int KS = d.d_h / kBK;
+    const int KS = d.d_h / kPK;
     for (int u0 = 0; u0 < d.d_e; u0 += kTM) {
         f32x16 acc1[2][2], acc2[2][2];
 #pragma unroll
@@ -209,31 +233,35 @@ __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
                 zero_acc(acc1[i][j]);
                 zero_acc(acc2[i][j]);
             }
-        u32x4 rxv[2], rw1v[2], rdyv[2], rw2v[2];
+        u32x4 rxv[kV], rw1v[kV], rdyv[kV], rw2v[kV];
         auto load_step = [&](int s) {
+            const uint32_t ko = (uint32_t)(s * kPK * 2);
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                const uint32_t ko = (uint32_t)(s * kBK * 2);
-                rxv[i] = load16(rx, xoff[i] == kOOB ? kOOB : xoff[i] + ko);
-                rdyv[i] = load16(rdy, dyoff[i] == kOOB ? kOOB : dyoff[i] + ko);
-                rw1v[i] = load16(rw1, (uint32_t)((((int64_t)e * d.d_e + u0 + srow[i]) * d.d_h + s * kBK + skv[i]) * 2));
-                rw2v[i] = load16(rw2, (uint32_t)((((int64_t)e * d.d_h + s * kBK + tk[i]) * d.d_e + u0 + tn[i]) * 2));
+            for (int i = 0; i < kV; ++i) {
+                const uint32_t xo = xoff[i] == kOOB ? kOOB : xoff[i] + ko;
+                const uint32_t wo =
+                    (uint32_t)((((int64_t)e * d.d_e + u0 + srow[i]) * d.d_h + skv[i]) * 2) + ko;
+                rxv[i] = load16(rx, xo);
+                rdyv[i] = load16(rdy, xo);
+                rw1v[i] = load16(rw1, wo);
+                rw2v[i] = load16(rw2, wo);
             }
         };
         load_step(0);
         for (int s = 0; s < KS; ++s) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<u32x4 *>(&As1[srow[i] * kLP + skv[i]]) = rxv[i];
-                *reinterpret_cast<u32x4 *>(&Bs1[srow[i] * kLP + skv[i]]) = rw1v[i];
-                *reinterpret_cast<u32x4 *>(&As2[srow[i] * kLP + skv[i]]) = rdyv[i];
-                store_transposed(Bs2, tn[i], tk[i], rw2v[i]);
+            for (int i = 0; i < kV; ++i) {
+                const int o = srow[i] * kPP + skv[i];
+                *reinterpret_cast<u32x4 *>(&As1[o]) = rxv[i];
+                *reinterpret_cast<u32x4 *>(&Bs1[o]) = rw1v[i];
+                *reinterpret_cast<u32x4 *>(&As2[o]) = rdyv[i];
+                *reinterpret_cast<u32x4 *>(&Bs2[o]) = rw2v[i];
             }
             __syncthreads();
             if (s + 1 < KS)
                 load_step(s + 1);
-            mma_64x64(As1, Bs1, acc1, wm, wn, lane);
-            mma_64x64(As2, Bs2, acc2, wm, wn, lane);
+            mma_64x64<kPK>(As1, Bs1, acc1, wm, wn, lane);
+            mma_64x64<kPK>(As2, Bs2, acc2, wm, wn, lane);
             __syncthreads();
         }
         // epilogue: Swish, its slope, the score
@@ -365,7 +393,7 @@ __global__ void __launch_bounds__(kBT, 2) wgrad_kernel(WgradArgs a)
         __syncthreads();
         if (s + 1 < cnt)
             load_step(s + 1);
-        mma_64x64(As, Bs, acc, wm, wn, lane);
+        mma_64x64<kBK>(As, Bs, acc, wm, wn, lane);
         __syncthreads();
     }
     float *out = kind == 0 ? a.dw1 + (int64_t)e * d.d_e * d.d_h : a.dw2 + (int64_t)e * d.d_h * d.d_e;
@@ -383,80 +411,131 @@ __global__ void __launch_bounds__(kBT, 2) wgrad_kernel(WgradArgs a)
 
 // ------------------------------------------------------------------ 4. dx from the experts
 struct DxArgs {
-    const uint16_t *w1;
+    const uint16_t *w1t;                  // [E][d_h][d_e]: W1 transposed
     const uint16_t *da_tu;                // [CT][E][32][d_e]
-    const int32_t *lists, *counts;        // chunk unions
-    float *dx;
+    const uint64_t *masks;                // [C][W] chunk unions
+    float *dx;                            // [T][d_h] (splits == 1)
+    float *part;                          // [splits][CT][32][d_h] (splits > 1)
+    int splits;
     Dims d;
 };
 
+constexpr int kXTiles = 4;                // chunk tiles (128 rows) per dx workgroup
+
+// Workgroup = (4 consecutive tiles, 128 output columns, expert split z): k runs over the
+// experts of the 4 tiles' chunks' unions (ascending; split z takes a contiguous share)
+// x d_e. A = dA rows (a tile whose chunk does not use the expert reads zeros), B = W1^T
+// rows; both k-contiguous.
 __global__ void __launch_bounds__(kBT, 2) dx_kernel(DxArgs a)
 {
     const Dims &d = a.d;
-    const int tile = blockIdx.x, nb = blockIdx.y * kXN;
-    const int c = tile / d.MPC;
-    const int ne = a.counts[c];
-    __shared__ uint16_t As[kTileM * kLP], Bs[kXN * kLP];
+    const int tg = blockIdx.x, nb = blockIdx.y * kTM, z = blockIdx.z;
+    __shared__ uint16_t As[kTM * kLP], Bs[kTM * kLP];
+    __shared__ uint64_t um[kXTiles][4];     // union masks of the 4 tiles' chunks
+    __shared__ int elist[256];
+    __shared__ int ecount;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const __amdgpu_buffer_rsrc_t rda = make_rsrc(a.da_tu, (uint64_t)d.CT * d.E * kTileM * d.d_e * 2);
-    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
-    // A: 32 rows x 32 k = 128 vectors (threads 0..127): row tid / 4, k (tid % 4) * 8.
-    // B (transposed W1): wave group g = 4 wave + i covers k [8 (g % 4), +8) x
-    // n [64 (g / 4), +64); lane: k = lane % 8, n = 8 (lane / 8) .. +8.
-    const int arow = (tid & 127) >> 2, akv = (tid & 3) * 8;
-    int tk[4], tn[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int g = 4 * wave + i;
-        tk[i] = (g & 3) * 8 + (lane & 7);
-        tn[i] = (g >> 2) * 64 + (lane >> 3) * 8;
+    const int wm = wave & 1, wn = wave >> 1;
+    if (tid < kXTiles * 4) {
+        const int q = tid / 4, w = tid % 4, tile = tg * kXTiles + q;
+        um[q][w] = (tile < d.CT && w < d.W) ? a.masks[(int64_t)(tile / d.MPC) * d.W + w] : 0ull;
     }
-    f32x16 acc[2];
-    zero_acc(acc[0]);
-    zero_acc(acc[1]);
-    const int US = d.d_e / kBK;
-    const int steps = ne * US;
-    u32x4 ra, rb[4];
-    auto load_step = [&](int s) {
-        const int e = a.lists[(int64_t)c * d.E + s / US];
-        const int u0 = (s % US) * kBK;
-        ra = load16(rda, tid < 128 ? (uint32_t)(((((int64_t)tile * d.E + e) * kTileM + arow) * d.d_e + u0 + akv) * 2) : kOOB);
+    __syncthreads();
+    if (tid == 0) {
+        int c = 0;
+        for (int e = 0; e < d.E; ++e) {
+            const uint64_t bit = 1ull << (e & 63);
+            if ((um[0][e >> 6] | um[1][e >> 6] | um[2][e >> 6] | um[3][e >> 6]) & bit)
+                elist[c++] = e;
+        }
+        ecount = c;
+    }
+    __syncthreads();
+    const int ne = ecount;
+    const int e_lo = (int)((int64_t)z * ne / a.splits), e_hi = (int)((int64_t)(z + 1) * ne / a.splits);
+    const __amdgpu_buffer_rsrc_t rda = make_rsrc(a.da_tu, (uint64_t)d.CT * d.E * kTileM * d.d_e * 2);
+    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(a.w1t, (uint64_t)d.E * d.d_e * d.d_h * 2);
+    int srow[2], skv[2];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            rb[i] = load16(rw1, (uint32_t)((((int64_t)e * d.d_e + u0 + tk[i]) * d.d_h + nb + tn[i]) * 2));
+    for (int i = 0; i < 2; ++i) {
+        const int q = tid + i * kBT;
+        srow[i] = q >> 2;
+        skv[i] = (q & 3) * 8;
+    }
+    f32x16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            zero_acc(acc[i][j]);
+    const int US = d.d_e / kBK;
+    const int steps = (e_hi - e_lo) * US;
+    u32x4 ra[2], rb[2];
+    auto load_step = [&](int s) {
+        const int e = elist[e_lo + s / US];
+        const int u0 = (s % US) * kBK;
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = srow[i] / kTileM, tile = tg * kXTiles + q;
+            const bool use = tile < d.CT && ((um[q][e >> 6] >> (e & 63)) & 1ull);
+            ra[i] = load16(rda, use ? (uint32_t)(((((int64_t)tile * d.E + e) * kTileM + srow[i] % kTileM) * d.d_e +
+                                                  u0 + skv[i]) * 2)
+                                    : kOOB);
+            rb[i] = load16(rw1, (uint32_t)((((int64_t)e * d.d_h + nb + srow[i]) * d.d_e + u0 + skv[i]) * 2));
+        }
     };
     if (steps > 0)
         load_step(0);
-    const int r = lane & 31, kg = lane >> 5;
     for (int s = 0; s < steps; ++s) {
-        if (tid < 128)
-            *reinterpret_cast<u32x4 *>(&As[arow * kLP + akv]) = ra;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            store_transposed(Bs, tn[i], tk[i], rb[i]);
+        for (int i = 0; i < 2; ++i) {
+            *reinterpret_cast<u32x4 *>(&As[srow[i] * kLP + skv[i]]) = ra[i];
+            *reinterpret_cast<u32x4 *>(&Bs[srow[i] * kLP + skv[i]]) = rb[i];
+        }
         __syncthreads();
         if (s + 1 < steps)
             load_step(s + 1);
-#pragma unroll
-        for (int ks = 0; ks < kBK / 16; ++ks) {
-            const bf16x8 av = *reinterpret_cast<const bf16x8 *>(&As[r * kLP + ks * 16 + kg * 8]);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const bf16x8 bv =
-                    *reinterpret_cast<const bf16x8 *>(&Bs[(wave * 64 + j * 32 + r) * kLP + ks * 16 + kg * 8]);
-                acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[j], 0, 0, 0);
-            }
-        }
+        mma_64x64<kBK>(As, Bs, acc, wm, wn, lane);
         __syncthreads();
     }
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t t = tile_token(d, tile, acc_row(v, lane));
-            if (t >= 0)
-                a.dx[t * d.d_h + nb + wave * 64 + j * 32 + (lane & 31)] = acc[j][v];
-        }
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+                const int row = wm * 64 + i * 32 + acc_row(v, lane);
+                const int tile = tg * kXTiles + row / kTileM;
+                const int col = nb + wn * 64 + j * 32 + (lane & 31);
+                if (tile >= d.CT)
+                    continue;
+                if (a.splits == 1) {
+                    const int64_t t = tile_token(d, tile, row % kTileM);
+                    if (t >= 0)
+                        a.dx[t * d.d_h + col] = acc[i][j][v];
+                } else {
+                    a.part[(((int64_t)z * d.CT + tile) * kTileM + row % kTileM) * d.d_h + col] = acc[i][j][v];
+                }
+            }
+}
+
+// dx = the expert splits' partials added in split order (rows with a token only).
+__global__ void __launch_bounds__(kBT) dx_reduce_kernel(DxArgs a)
+{
+    const Dims &d = a.d;
+    const int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x;    // over CT * 32 * d_h
+    if (i >= (int64_t)d.CT * kTileM * d.d_h)
+        return;
+    const int col = (int)(i % d.d_h);
+    const int64_t rt = i / d.d_h;
+    const int tile = (int)(rt / kTileM), r = (int)(rt % kTileM);
+    const int64_t t = tile_token(d, tile, r);
+    if (t < 0)
+        return;
+    float sum = 0.0f;
+    for (int z = 0; z < a.splits; ++z)
+        sum += a.part[((int64_t)z * d.CT * kTileM + rt) * d.d_h + col];
+    a.dx[t * d.d_h + col] = sum;
 }
 
 // ------------------------------------------------------------------ 5. router backward
@@ -471,113 +550,203 @@ struct RouterArgs {
     Dims d;
 };
 
-__device__ __forceinline__ float block_sum(float v, float *sh)
-{
-    // fixed order: wave DPP trees, then the 4 wave sums in order
-    v = wave_sum_f32(v);
-    const int tid = threadIdx.x;
-    __syncthreads();
-    if (tid % kWave == 0)
-        sh[tid / kWave] = v;
-    __syncthreads();
-    return (sh[0] + sh[1]) + (sh[2] + sh[3]);
-}
+constexpr int kRtTokens = 4;              // tokens per router-token workgroup (one per wave)
+constexpr int kRtPer = 256 / kWave;       // experts per lane (E <= 256)
 
+// Per token (one wavefront each, kRtTokens per workgroup): ds (masked to the chunk's
+// union, plus the probability term), the RMSNorm and ReLU backward -> dl, and the gain
+// term; then dx[t] += W_r^T dl for the workgroup's tokens, each W_r row loaded once for
+// all of them (experts in order, eight rows in flight).
 __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
 {
     const Dims &d = a.d;
-    const int64_t t = blockIdx.x;
-    const int tid = threadIdx.x, e = tid;
-    const int c = (int)(t / d.n);
-    __shared__ float red[4];
-    __shared__ float dl_s[256];
-    const bool ve = e < d.E;
-    const float l = ve ? a.logits[t * d.E + e] : 0.0f;
-    const float r = l > 0.0f ? l : 0.0f;
-    const float inv = 1.0f / sqrtf(block_sum(r * r, red) / (float)d.E + a.eps);
-    float ds = 0.0f;
-    if (ve) {
-        if ((a.masks[(int64_t)c * d.W + (e >> 6)] >> (e & 63)) & 1ull)
-            ds = a.ds[t * d.E + e];
-        if (a.dprobs) {
-            const float p = 1.0f / (1.0f + expf(-a.sharpness * a.scores[t * d.E + e]));
-            ds += a.dprobs[t * d.E + e] * a.sharpness * p * (1.0f - p);
-        }
-    }
-    const float g = ve && a.gain ? a.gain[e] : 1.0f;
-    const float coup = block_sum(ve ? g * r * ds : 0.0f, red);
-    const float dr = g * inv * ds - inv * inv * inv * r / (float)d.E * coup;
-    const float dl = (ve && l > 0.0f) ? dr : 0.0f;
-    dl_s[tid] = dl;
-    if (ve) {
-        a.dl[t * d.E + e] = dl;
-        a.gt[t * d.E + e] = ds * r * inv;
-    }
-    __syncthreads();
-    // dx[t] += W_r^T dl, eight columns per thread, experts in order
-    for (int jv = tid; jv < d.d_h / 8; jv += kBT) {
-        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        for (int k = 0; k < d.E; ++k) {
-            const u32x4 w = *reinterpret_cast<const u32x4 *>(&a.w_r[(int64_t)k * d.d_h + jv * 8]);
-            const float dk = dl_s[k];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int64_t t0 = (int64_t)blockIdx.x * kRtTokens;
+    __shared__ float dl_s[kRtTokens][256];
+    {
+        const int64_t t = t0 + wave;
+        const bool vt = t < d.T;
+        const int c = vt ? (int)(t / d.n) : 0;
+        float l[kRtPer], r[kRtPer], ds[kRtPer], g[kRtPer];
+        float sq = 0.0f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                acc[2 * q] = fmaf(dk, __uint_as_float(w[q] << 16), acc[2 * q]);
-                acc[2 * q + 1] = fmaf(dk, __uint_as_float(w[q] & 0xffff0000u), acc[2 * q + 1]);
+        for (int i = 0; i < kRtPer; ++i) {
+            const int e = lane + i * kWave;
+            const bool ve = vt && e < d.E;
+            l[i] = ve ? a.logits[t * d.E + e] : 0.0f;
+            r[i] = l[i] > 0.0f ? l[i] : 0.0f;
+            sq = fmaf(r[i], r[i], sq);
+            ds[i] = 0.0f;
+            if (ve) {
+                if ((a.masks[(int64_t)c * d.W + (e >> 6)] >> (e & 63)) & 1ull)
+                    ds[i] = a.ds[t * d.E + e];
+                if (a.dprobs) {
+                    const float p = 1.0f / (1.0f + expf(-a.sharpness * a.scores[t * d.E + e]));
+                    ds[i] += a.dprobs[t * d.E + e] * a.sharpness * p * (1.0f - p);
+                }
+            }
+            g[i] = ve && a.gain ? a.gain[e] : 1.0f;
+        }
+        const float inv = 1.0f / sqrtf(wave_sum_f32(sq) / (float)d.E + a.eps);
+        float cp = 0.0f;
+#pragma unroll
+        for (int i = 0; i < kRtPer; ++i)
+            cp = fmaf(g[i] * r[i], ds[i], cp);
+        const float coup = wave_sum_f32(cp);
+#pragma unroll
+        for (int i = 0; i < kRtPer; ++i) {
+            const int e = lane + i * kWave;
+            const float dr = g[i] * inv * ds[i] - inv * inv * inv * r[i] / (float)d.E * coup;
+            const float dl = l[i] > 0.0f ? dr : 0.0f;
+            dl_s[wave][e] = dl;
+            if (vt && e < d.E) {
+                a.dl[t * d.E + e] = dl;
+                a.gt[t * d.E + e] = ds[i] * r[i] * inv;
             }
         }
-        float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + jv * 8]);
-        float4 o0 = o[0], o1 = o[1];
-        o0.x += acc[0], o0.y += acc[1], o0.z += acc[2], o0.w += acc[3];
-        o1.x += acc[4], o1.y += acc[5], o1.z += acc[6], o1.w += acc[7];
-        o[0] = o0;
-        o[1] = o1;
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w_r, (uint64_t)d.E * d.d_h * 2);
+    for (int jv = tid; jv < d.d_h / 8; jv += kBT) {
+        float acc[kRtTokens][8];
+#pragma unroll
+        for (int k = 0; k < kRtTokens; ++k)
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+                acc[k][q] = 0.0f;
+        for (int k0 = 0; k0 < d.E; k0 += 8) {
+            u32x4 w[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+                w[u] = load16(rw, k0 + u < d.E ? (uint32_t)((((int64_t)(k0 + u)) * d.d_h + jv * 8) * 2) : kOOB);
+#pragma unroll
+            for (int u = 0; u < 8; ++u)
+#pragma unroll
+                for (int k = 0; k < kRtTokens; ++k) {
+                    const float dk = k0 + u < d.E ? dl_s[k][k0 + u] : 0.0f;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        acc[k][2 * q] = fmaf(dk, __uint_as_float(w[u][q] << 16), acc[k][2 * q]);
+                        acc[k][2 * q + 1] = fmaf(dk, __uint_as_float(w[u][q] & 0xffff0000u), acc[k][2 * q + 1]);
+                    }
+                }
+        }
+#pragma unroll
+        for (int k = 0; k < kRtTokens; ++k) {
+            const int64_t t = t0 + k;
+            if (t >= d.T)
+                continue;
+            float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + jv * 8]);
+            float4 o0 = o[0], o1 = o[1];
+            o0.x += acc[k][0], o0.y += acc[k][1], o0.z += acc[k][2], o0.w += acc[k][3];
+            o1.x += acc[k][4], o1.y += acc[k][5], o1.z += acc[k][6], o1.w += acc[k][7];
+            o[0] = o0;
+            o[1] = o1;
+        }
     }
 }
 
 constexpr int kRpE = 8;       // experts per router-parameter workgroup
+constexpr int kRpTargetBlocks = 1024;
 
-// dW_r[e][j] = sum_t dl[t][e] x[t][j] (tokens in order); the workgroups of column block
-// 0 also sum dgain and dbias.
-__global__ void __launch_bounds__(kBT) router_param_kernel(RouterArgs a)
+// Token splits of the router-parameter sums: enough workgroups to fill the chip,
+// at least 32 tokens per split.
+int router_param_splits(int64_t T, int64_t d_h, int64_t E)
+{
+    const int64_t base = ((E + kRpE - 1) / kRpE) * (d_h / kBT);
+    int64_t s = (kRpTargetBlocks + base - 1) / base;
+    const int64_t smax = (T + 31) / 32;
+    if (s > smax)
+        s = smax;
+    return s < 1 ? 1 : (int)s;
+}
+
+// Partial dW_r over token split z: part[z][e][j] = sum_{t in split z} dl[t][e] x[t][j],
+// tokens in order.
+__global__ void __launch_bounds__(kBT) router_param_kernel(RouterArgs a, int splits, float *part)
 {
     const Dims &d = a.d;
-    const int e0 = blockIdx.x * kRpE, j = blockIdx.y * kBT + threadIdx.x, tid = threadIdx.x;
+    const int e0 = blockIdx.x * kRpE, j = blockIdx.y * kBT + threadIdx.x, z = blockIdx.z;
+    const int64_t per = (d.T + splits - 1) / splits;
+    const int64_t t0 = z * per, t1 = t0 + per < d.T ? t0 + per : d.T;
+    // dl[t][e0 .. e0+8) of 128 tokens at a time staged in LDS (read back as broadcasts);
+    // x of 16 tokens in flight at a time
+    __shared__ float dls[128][kRpE];
+    const int tid = threadIdx.x;
     float acc[kRpE];
 #pragma unroll
     for (int q = 0; q < kRpE; ++q)
         acc[q] = 0.0f;
-    for (int64_t t = 0; t < d.T; ++t) {
-        const float xv = bf16_to_f32(a.x[t * d.d_h + j]);
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)d.T * d.d_h * 2);
+    for (int64_t tb = t0; tb < t1; tb += 128) {
+        {
+            const int64_t t = tb + tid / 2;
+            const int q0 = (tid % 2) * 4;
 #pragma unroll
-        for (int q = 0; q < kRpE; ++q)
-            if (e0 + q < d.E)
-                acc[q] = fmaf(a.dl[t * d.E + e0 + q], xv, acc[q]);
+            for (int q = 0; q < 4; ++q)
+                dls[tid / 2][q0 + q] = (t < t1 && e0 + q0 + q < d.E) ? a.dl[t * d.E + e0 + q0 + q] : 0.0f;
+        }
+        __syncthreads();
+        const int nt = (int)(t1 - tb < 128 ? t1 - tb : 128);
+        for (int u0 = 0; u0 < nt; u0 += 16) {
+            float xv[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const uint32_t off = u0 + u < nt ? (uint32_t)(((tb + u0 + u) * d.d_h + j) * 2) : kOOB;
+                xv[u] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, (int)off, 0, 0)
+                                        << 16);
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+                for (int q = 0; q < kRpE; ++q)
+                    acc[q] = fmaf(dls[u0 + u][q], xv[u], acc[q]);
+        }
+        __syncthreads();
     }
 #pragma unroll
     for (int q = 0; q < kRpE; ++q)
         if (e0 + q < d.E)
-            a.dw_r[(int64_t)(e0 + q) * d.d_h + j] = acc[q];
+            part[((int64_t)z * d.E + e0 + q) * d.d_h + j] = acc[q];
+}
+
+// dW_r = the splits' partials added in split order; the workgroups of column block 0
+// also sum dgain and dbias (thread = (expert q = tid % 8, token slice tid / 8 of 32),
+// then the 32 slices in order).
+__global__ void __launch_bounds__(kBT) router_param_reduce_kernel(RouterArgs a, int splits,
+                                                                  const float *part)
+{
+    const Dims &d = a.d;
+    const int e0 = blockIdx.x * kRpE, j = blockIdx.y * kBT + threadIdx.x, tid = threadIdx.x;
+#pragma unroll
+    for (int q = 0; q < kRpE; ++q)
+        if (e0 + q < d.E) {
+            float sum = 0.0f;
+#pragma unroll 8
+            for (int z = 0; z < splits; ++z)
+                sum += part[((int64_t)z * d.E + e0 + q) * d.d_h + j];
+            a.dw_r[(int64_t)(e0 + q) * d.d_h + j] = sum;
+        }
     if (blockIdx.y != 0)
         return;
-    // dgain, dbias: thread = (expert q = tid % 8, token slice tid / 8 of 32), then the
-    // 32 slices in order
     __shared__ float pg[kBT], pb[kBT];
     const int q = tid % kRpE, sl = tid / kRpE;
     float sg = 0.0f, sb = 0.0f;
-    if (e0 + q < d.E)
+    if (e0 + q < d.E) {
+#pragma unroll 8
         for (int64_t t = sl; t < d.T; t += kBT / kRpE) {
             sg += a.gt[t * d.E + e0 + q];
             sb += a.dl[t * d.E + e0 + q];
         }
+    }
     pg[tid] = sg;
     pb[tid] = sb;
     __syncthreads();
     if (tid < kRpE && e0 + tid < d.E) {
         float g = 0.0f, b = 0.0f;
-        for (int s = 0; s < kBT / kRpE; ++s) {
-            g += pg[s * kRpE + tid];
-            b += pb[s * kRpE + tid];
+        for (int s2 = 0; s2 < kBT / kRpE; ++s2) {
+            g += pg[s2 * kRpE + tid];
+            b += pb[s2 * kRpE + tid];
         }
         if (a.dgain)
             a.dgain[e0 + tid] = g;
@@ -591,9 +760,24 @@ struct BwdLayout {
     FfnPlan p;
     size_t masks, lists, counts, tile_list, tile_count;
     size_t logits, scores, ds, dl, gt;
-    size_t xt, dyt, da_tu, da_ut, sh_ut;
+    size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, w1t, w2t, dx_part;
+    int dx_splits;
     size_t total;
 };
+
+constexpr int kDxTargetBlocks = 256;
+
+// Expert splits of the dx products: enough workgroups for one per CU.
+int dx_splits(int64_t CT, int64_t d_h, int64_t E)
+{
+    const int64_t base = ((CT + kXTiles - 1) / kXTiles) * (d_h / kTM);
+    int64_t s = (kDxTargetBlocks + base - 1) / base;
+    if (s > E)
+        s = E;
+    if (s > 32)
+        s = 32;
+    return s < 1 ? 1 : (int)s;
+}
 
 BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
 {
@@ -621,6 +805,11 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
     L.da_tu = take(2 * p.CT * E * kTileM * d_e);
     L.da_ut = take(2 * p.CT * E * kTileM * d_e);
     L.sh_ut = take(2 * p.CT * E * kTileM * d_e);
+    L.rp_part = take(4 * (size_t)router_param_splits(T, d_h, E) * E * d_h);
+    L.w1t = take(2 * (size_t)E * d_e * d_h);
+    L.w2t = take(2 * (size_t)E * d_e * d_h);
+    L.dx_splits = dx_splits(p.CT, d_h, E);
+    L.dx_part = take(L.dx_splits > 1 ? 4 * (size_t)L.dx_splits * p.CT * kTileM * d_h : 0);
     L.total = off;
     L.p.off_masks = L.masks;
     L.p.off_lists = L.lists;
@@ -675,6 +864,13 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     d.W = (int)p.W;
     d.MPC = (int)p.MPC;
     d.CT = (int)p.CT;
+    uint16_t *w1t = reinterpret_cast<uint16_t *>(at(L.w1t));
+    uint16_t *w2t = reinterpret_cast<uint16_t *>(at(L.w2t));
+    // W1 [E][d_e][d_h] -> [E][d_h][d_e], W2 [E][d_h][d_e] -> [E][d_e][d_h], used experts only
+    hipLaunchKernelGGL(transpose_weights_kernel, dim3((unsigned)(b.d_h / 64), (unsigned)(b.d_e / 64), (unsigned)b.E),
+                       dim3(kBT), 0, stream, b.w1, (int)b.d_e, (int)b.d_h, tile_count, w1t);
+    hipLaunchKernelGGL(transpose_weights_kernel, dim3((unsigned)(b.d_e / 64), (unsigned)(b.d_h / 64), (unsigned)b.E),
+                       dim3(kBT), 0, stream, b.w2, (int)b.d_h, (int)b.d_e, tile_count, w2t);
     uint16_t *xt = reinterpret_cast<uint16_t *>(at(L.xt));
     uint16_t *dyt = reinterpret_cast<uint16_t *>(at(L.dyt));
     const dim3 tgrid((unsigned)p.CT, (unsigned)(b.d_h / kTrCols));
@@ -685,7 +881,7 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     pa.x = b.x;
     pa.dy = b.dy;
     pa.w1 = b.w1;
-    pa.w2 = b.w2;
+    pa.w2t = w2t;
     pa.scores = scores;
     pa.tile_list = tile_list;
     pa.tile_count = tile_count;
@@ -711,14 +907,22 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)wblocks), dim3(kBT), 0, stream, wa);
 
     DxArgs xa;
-    xa.w1 = b.w1;
+    xa.w1t = w1t;
     xa.da_tu = pa.da_tu;
-    xa.lists = reinterpret_cast<const int32_t *>(at(L.lists));
-    xa.counts = reinterpret_cast<const int32_t *>(at(L.counts));
+    xa.masks = masks;
     xa.dx = b.dx;
+    xa.part = reinterpret_cast<float *>(at(L.dx_part));
+    xa.splits = L.dx_splits;
     xa.d = d;
-    hipLaunchKernelGGL(dx_kernel, dim3((unsigned)p.CT, (unsigned)(b.d_h / kXN)), dim3(kBT), 0,
-                       stream, xa);
+    hipLaunchKernelGGL(dx_kernel,
+                       dim3((unsigned)((p.CT + kXTiles - 1) / kXTiles), (unsigned)(b.d_h / kTM),
+                            (unsigned)L.dx_splits),
+                       dim3(kBT), 0, stream, xa);
+    if (L.dx_splits > 1) {
+        const int64_t nel = p.CT * kTileM * b.d_h;
+        hipLaunchKernelGGL(dx_reduce_kernel, dim3((unsigned)((nel + kBT - 1) / kBT)), dim3(kBT), 0,
+                           stream, xa);
+    }
 
     RouterArgs ra;
     ra.x = b.x;
@@ -738,9 +942,15 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     ra.eps = b.eps;
     ra.sharpness = b.sharpness;
     ra.d = d;
-    hipLaunchKernelGGL(router_token_kernel, dim3((unsigned)b.T), dim3(kBT), 0, stream, ra);
-    hipLaunchKernelGGL(router_param_kernel, dim3((unsigned)((b.E + kRpE - 1) / kRpE), (unsigned)(b.d_h / kBT)),
-                       dim3(kBT), 0, stream, ra);
+    hipLaunchKernelGGL(router_token_kernel, dim3((unsigned)((b.T + kRtTokens - 1) / kRtTokens)), dim3(kBT), 0,
+                       stream, ra);
+    const int splits = router_param_splits(b.T, b.d_h, b.E);
+    float *rp = reinterpret_cast<float *>(at(L.rp_part));
+    const unsigned eb = (unsigned)((b.E + kRpE - 1) / kRpE), jb = (unsigned)(b.d_h / kBT);
+    hipLaunchKernelGGL(router_param_kernel, dim3(eb, jb, (unsigned)splits), dim3(kBT), 0, stream,
+                       ra, splits, rp);
+    hipLaunchKernelGGL(router_param_reduce_kernel, dim3(eb, jb), dim3(kBT), 0, stream, ra,
+                       splits, static_cast<const float *>(rp));
     return hipGetLastError();
 }
 

@@ -335,7 +335,7 @@ hipError_t probe_xcd_placement(int nxcd, bool *round_robin)
     static uint32_t host[kBlocks];
     if (err == hipSuccess)
         err = hipMemcpy(host, buf, sizeof(host), hipMemcpyDeviceToHost);
-    hipFree(buf);
+    (void)hipFree(buf);
     if (err != hipSuccess)
         return err;
     bool ok = nxcd > 0;

@@ -248,7 +248,7 @@ struct DownState {
 __device__ void down_issue_w2(const Chunk1Args &a, const Rsrc &r, const Shared &sh, DownState &d,
                               int batch)
 {
-    const int lane = threadIdx.x % kWave, col = lane & 31, kg = lane >> 5;
+    const int lane = threadIdx.x % kWave, kg = lane >> 5;
 #pragma unroll
     for (int i = 0; i < kDnMaxUnitsPerWave; ++i) {
         const int u = d.pp + 4 * (batch * kDnMaxUnitsPerWave + i);

@@ -65,6 +65,8 @@ CASES = [
     ("one token, no bias", 5, 1, 256, 16, 128, 32, True, False, False, True, 1.0),
     ("decode shape", 6, 32, 2048, 64, 128, 32, True, False, False, False, 1.0),
     ("multi-chunk E=40", 7, 128, 512, 40, 128, 32, True, True, False, False, 1.0),
+    # enough tiles that dx runs one workgroup per (4 tiles, 128 columns), no expert split
+    ("many tiles, unsplit dx", 10, 16384, 256, 4, 128, 32, False, False, False, False, 1.0),
 ]
 
 
