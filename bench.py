@@ -1,24 +1,26 @@
 #!/usr/bin/env python3
 """Benchmark of the BlockFFN layer forward on one MI355X.
 
-One step = the whole layer over one batch: blockffn_router on the batch's tokens,
-then blockffn_chunk_ffn on the same tokens. Default workload (the decode /
-speculative-verification chunk): d_h=2048, E=64 experts, d_e=128, T = n = 32
-tokens, bf16 weights and activations, fp32 accumulation. The FFN's scores come from
-per-expert two-state Markov masks at 80% token-level and 70% 8-token chunk-level
-sparsity (the sparsity the pages report for trained BlockFFN models), with active
-scores |N(0,1)| + 0.1; they stand in for a trained router, whose weights are not
-available. The router still runs every step on the step's tokens (its output goes
-to its own buffer), so the step time contains every kernel of the layer.
+One step = the whole layer over one batch: blockffn_layer_forward (the router, then
+the chunked expert FFN on the router's scores). Default workload (the decode /
+speculative-verification chunk): d_h=2048, E=64 experts, d_e=128, T = n = 32 tokens,
+bf16 weights and activations, fp32 accumulation; at this size router and FFN run in
+one launch. No trained router is available, so the inputs are drawn to make the
+router's activity follow per-expert two-state Markov masks at 80% token-level and 70%
+8-token chunk-level sparsity (the sparsity the pages report for trained BlockFFN
+models): W_r has orthonormal rows and every token x_t is built so that W_r x_t has the
+mask's signs (positive |N(0,1)| + 0.1 where active), plus Gaussian noise orthogonal
+to W_r. The router still computes every logit from x each step.
 
 Inputs are resident in HBM before timing starts. Each step uses the next of several
-distinct weight copies (>= 512 MiB in all) and the next of 16 mask/token draws, so
-the 256 MB Infinity Cache cannot serve a weight set twice in a row.
+distinct weight copies (>= 512 MiB in all) and the next of 16 mask draws, so the
+256 MB Infinity Cache cannot serve a weight set twice in a row.
 
-Prints ONE JSON line (see the keys below). `roofline` is for the chunk-FFN kernel:
-algorithmic bytes per call (the union experts' W1 and W2 slices, plus x, scores and
-y) over its average duration, measured with HIP events around each call in the timed
-region on the stream it runs on.
+Prints ONE JSON line (see the keys below). `roofline` is for the dominant kernel: the
+one-launch layer kernel at the decode chunk (its duration is the step's), else the
+chunk-FFN launches: algorithmic bytes per call (the union experts' W1 and W2 slices,
+W_r when the router is inside, x and y) over its average duration, measured with HIP
+events around graph replays on the stream it runs on.
 """
 from __future__ import annotations
 
@@ -61,38 +63,50 @@ def parse_args(argv=None):
 
 
 def make_inputs(args, torch, np, inputs):
+    """Weight copies, mask draws, and the x of each of the S steps of one captured
+    graph (x depends on the copy's W_r and the draw's mask)."""
     cfg = dict(inputs.WORKLOADS[args.workload])
     T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
     dev = torch.device("cuda:0")
     bf16 = torch.bfloat16
+    markov = args.workload != "e2e"
 
     def to_dev(a, dtype=bf16):
         return torch.from_numpy(np.ascontiguousarray(a)).to(dev, dtype)
 
     copy_bytes = 2 * (2 * E * d_e * d_h + E * d_h)
     ncopies = max(2, math.ceil(args.rotate_mib * 2 ** 20 / copy_bytes))
-    copies = []
+    copies, w_r_host = [], []
     for i in range(ncopies):
         rng = np.random.default_rng(args.seed * 1000 + 100 + i)
         w1, w2 = inputs.expert_weights(rng, E, d_e, d_h, True)
-        w_r = inputs.gaussian(rng, (E, d_h), 1.0 / np.sqrt(d_h), True)
-        bias = inputs.router_shift(w_r, 0.8)
-        copies.append(dict(w1=to_dev(w1), w2=to_dev(w2), w_r=to_dev(w_r),
-                           bias=to_dev(bias, torch.float32)))
+        if markov:
+            w_r = inputs.router_weight_orthonormal(rng, E, d_h, True)
+            bias = None
+        else:
+            w_r = inputs.gaussian(rng, (E, d_h), 1.0 / np.sqrt(d_h), True)
+            bias = to_dev(inputs.router_shift(w_r, 0.8), torch.float32)
+        w_r_host.append(w_r)
+        copies.append(dict(w1=to_dev(w1), w2=to_dev(w2), w_r=to_dev(w_r), bias=bias))
         del w1, w2
     draws = []
     for i in range(args.draws):
         rng = np.random.default_rng(args.seed * 1000 + 500 + i)
-        x = inputs.gaussian(rng, (T, d_h), 1.0, True)
-        if args.workload == "e2e":
-            scores = None
-        else:
-            act = inputs.markov_active(rng, T, E, 0.8, 0.7, 8)
-            scores = to_dev(inputs.scores_for_mask(rng, act), torch.float32)
+        act = inputs.markov_active(rng, T, E, 0.8, 0.7, 8) if markov else None
+        x = None if markov else to_dev(inputs.gaussian(rng, (T, d_h), 1.0, True))
         dense = to_dev((np.abs(rng.standard_normal((T, E))) + 0.1).astype(np.float32),
                        torch.float32)
-        draws.append(dict(x=to_dev(x), scores=scores, dense=dense))
-    return cfg, copies, draws
+        draws.append(dict(act=act, x=x, dense=dense))
+    nc, nd = len(copies), len(draws)
+    S = nc * nd // math.gcd(nc, nd)
+    xs = []
+    for i in range(S):
+        if markov:
+            rng = np.random.default_rng(args.seed * 1000 + 900 + i)
+            xs.append(to_dev(inputs.tokens_for_mask(rng, w_r_host[i % nc], draws[i % nd]["act"], True)))
+        else:
+            xs.append(draws[i % nd]["x"])
+    return cfg, copies, draws, xs, S
 
 
 def main(argv=None):
@@ -116,37 +130,36 @@ def main(argv=None):
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    cfg, copies, draws = make_inputs(args, torch, np, inputs)
+    cfg, copies, draws, xs, S = make_inputs(args, torch, np, inputs)
     T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
     C = -(-T // n)
     dev = torch.device("cuda:0")
     gain = torch.ones(E, dtype=torch.float32, device=dev)
-    router_out = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in draws]
     y = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
+    lws = bf.blockffn_layer_forward_workspace(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16, dev)
     ws = bf.blockffn_chunk_ffn_workspace(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16, dev)
     router_ws = bf.blockffn_router_workspace(T, d_h, E, bf.BLOCKFFN_BF16, dev)
-    counts = [torch.zeros(C, dtype=torch.int32, device=dev) for _ in draws]
+    fused = bf.blockffn_layer_forward_fused(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16)
+    counts = [torch.zeros(C, dtype=torch.int32, device=dev) for _ in range(S)]
+    scores = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(S)]
     nc, nd = len(copies), len(draws)
-    # One captured graph holds S consecutive steps, S a multiple of both rotation
-    # lengths, so every replay walks the same sequence of weight copies and draws.
-    S = nc * nd // math.gcd(nc, nd)
+
+    # step i uses weight copy i % nc and the x drawn for step i % S (S = lcm of the two
+    # rotation lengths, so every replay of an S-step graph walks the same sequence)
+    def step(i):
+        w, k = copies[i % nc], i % S
+        bf.blockffn_layer_forward(xs[k], w["w_r"], w["w1"], w["w2"], n, gain=gain, bias=w["bias"],
+                                  y=y, workspace=lws)
+
+    def router(i):
+        w, k = copies[i % nc], i % S
+        bf.blockffn_router(xs[k], w["w_r"], gain, w["bias"], scores=scores[k], workspace=router_ws)
 
     def ffn(i, dense=False):
-        w = copies[i % nc]
-        d = draws[i % nd]
-        if args.workload == "e2e":
-            s = router_out[i % nd]
-        else:
-            s = d["dense"] if dense else d["scores"]
-        bf.blockffn_chunk_ffn(d["x"], s, w["w1"], w["w2"], n, y=y, workspace=ws,
-                              union_counts=counts[i % nd])
-
-    def step(i):
-        w = copies[i % nc]
-        d = draws[i % nd]
-        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=router_out[i % nd],
-                           workspace=router_ws)
-        ffn(i)
+        w, k = copies[i % nc], i % S
+        s = draws[i % nd]["dense"] if dense else scores[k]
+        bf.blockffn_chunk_ffn(xs[k], s, w["w1"], w["w2"], n, y=y, workspace=ws,
+                              union_counts=counts[k])
 
     def capture(body):
         g = torch.cuda.CUDAGraph()
@@ -166,9 +179,12 @@ def main(argv=None):
         torch.cuda.synchronize()
         return t0.elapsed_time(t1)
 
-    # eager warm-up (loads the code objects), then the captured loops
+    # eager warm-up (loads the code objects); the router's scores of every step, for
+    # the FFN-alone timing and the realised unions
     for i in range(min(args.warmup, 2 * S)):
         step(i)
+    for i in range(S):
+        router(i)
     torch.cuda.synchronize()
     g_step = capture(step)
     g_ffn = capture(ffn)
@@ -179,9 +195,14 @@ def main(argv=None):
     total_ms = time_replays(g_step, replays)
     nsteps = replays * S
     ms_per_step = total_ms / nsteps
-    # the chunk-FFN calls alone, same rotation: average duration of one launch
+    # the chunk-FFN calls alone on the router's scores, same rotation
     time_replays(g_ffn, wreplays)
     ffn_avg_ms = time_replays(g_ffn, replays) / nsteps
+    # the router and the chunk FFN as separate launches (the unfused layer)
+    g_sep = capture(lambda i: (router(i), ffn(i)))
+    time_replays(g_sep, wreplays)
+    sep_ms = time_replays(g_sep, replays) / nsteps
+    del g_sep
 
     # Python-launched steps, for comparison (host-bound at these sizes)
     eager_n = min(200, nsteps)
@@ -192,14 +213,24 @@ def main(argv=None):
     torch.cuda.synchronize()
     eager_ms = (time.perf_counter() - te) * 1e3 / eager_n
 
-    # Realised unions of the draws (the FFN wrote them during the run).
-    cnt = np.stack([c.cpu().numpy() for c in counts])            # [draws, C]
-    union_experts = float(np.mean([cnt[i % nd].sum() for i in range(S)]))  # per step
-    weight_bytes = union_experts * 2 * d_h * d_e * 2                    # W1 + W2, bf16
-    act_bytes = T * d_h * 2 + T * E * 4 + T * d_h * 2                  # x, scores, y
-    ffn_bytes = weight_bytes + act_bytes
-    achieved_gbs = ffn_bytes / (ffn_avg_ms * 1e-3) / 1e9
-    ffn_flops = union_experts * n * 4 * d_h * d_e
+    # Realised unions (the FFN-alone graph wrote them).
+    cnt = np.stack([c.cpu().numpy() for c in counts])            # [S, C]
+    union_experts = float(cnt.sum(axis=1).mean())                 # per step
+    weight_bytes = union_experts * 2 * d_h * d_e * 2               # W1 + W2, bf16
+    act_bytes = T * d_h * 2 + T * d_h * 2                          # x, y
+    if fused:
+        kernel_bytes = weight_bytes + act_bytes + E * d_h * 2       # + W_r
+        kernel_ms = ms_per_step
+        kernel_name = "layer forward, router and chunk FFN in one launch (blockffn_layer_forward)"
+        timing = "HIP events around graph replays of the steps (one launch each)"
+    else:
+        kernel_bytes = weight_bytes + act_bytes + T * E * 4         # + scores
+        kernel_ms = ffn_avg_ms
+        kernel_name = "chunk FFN (blockffn_chunk_ffn)"
+        timing = ("HIP events around graph replays of the chunk-FFN calls alone (same "
+                  "rotation), divided by the number of calls")
+    achieved_gbs = kernel_bytes / (kernel_ms * 1e-3) / 1e9
+    flops = union_experts * n * 4 * d_h * d_e + (2 * T * E * d_h if fused else 0)
     tokens_per_s = T / (ms_per_step * 1e-3)
 
     dense = None
@@ -211,15 +242,21 @@ def main(argv=None):
 
     extras = None
     if not args.no_extras:
-        extras = bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain,
-                              router_out, y, ws, router_ws, counts, S, replays, wreplays,
-                              time_replays, capture)
+        extras = bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws,
+                              replays, wreplays, time_replays, capture)
+        extras["unfused_layer"] = {
+            "what": "blockffn_router + blockffn_chunk_ffn as two launches, same inputs",
+            "ms_per_step": sep_ms, "tokens_per_s": T / (sep_ms * 1e-3),
+            "chunk_ffn_ms": ffn_avg_ms}
 
     cpu = None
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(args, cfg, np, inputs)
 
     traffic = read_traffic(args.workload)
+    activity = ("router activity following Markov masks at 80% TLS / 70% 8-token CLS "
+                "(orthonormal W_r, x drawn for the masks)" if args.workload != "e2e" else
+                "router with a logit shift for ~80% zeros, i.i.d. x")
     out = {
         "metric": "tokens/s + effective HBM GB/s (% of peak) of BlockFFN layer, n=32 chunks",
         "value": tokens_per_s,
@@ -234,10 +271,9 @@ def main(argv=None):
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": f"{args.workload}: d_h={d_h} E={E} d_e={d_e} T={T} n={n} bf16"
-                        + ("" if args.workload == "e2e" else
-                           ", Markov scores 80% TLS / 70% 8-token CLS")
-                        + "; router + chunk FFN per step",
+            "workload": f"{args.workload}: d_h={d_h} E={E} d_e={d_e} T={T} n={n} bf16, "
+                        f"{activity}; router + chunk FFN per step"
+                        + (" in one launch" if fused else ""),
             "global_batch": T, "seq_len": n, "parallelism": "none (1 GPU)",
             "weight_copies": nc, "rotation_mib": round(nc * 2 * (2 * E * d_e * d_h + E * d_h) / 2 ** 20),
             "union_experts_per_step": union_experts,
@@ -245,18 +281,17 @@ def main(argv=None):
                       f"step {eager_ms:.4f} ms",
         },
         "roofline": {
-            "kernel": "chunk FFN (blockffn_chunk_ffn)",
+            "kernel": kernel_name,
             "bound": "hbm",
             "achieved": achieved_gbs,
             "peak": HBM_PEAK_GBS,
             "unit": "GB/s",
             "frac": achieved_gbs / HBM_PEAK_GBS,
             "traffic": traffic,
-            "algorithmic_bytes_per_launch": ffn_bytes,
-            "avg_launch_ms": ffn_avg_ms,
-            "launch_timing": "HIP events around graph replays of the chunk-FFN calls "
-                             "alone (same rotation), divided by the number of calls",
-            "mfma_frac": ffn_flops / (ffn_avg_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+            "algorithmic_bytes_per_launch": kernel_bytes,
+            "avg_launch_ms": kernel_ms,
+            "launch_timing": timing,
+            "mfma_frac": flops / (kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
         },
         "dense_ffn": dense,
         "extras": extras,
@@ -266,30 +301,25 @@ def main(argv=None):
     return 0
 
 
-def bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain, router_out, y, ws,
-                 router_ws, counts, S, replays, wreplays, time_replays, capture):
+def bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws, replays,
+                 wreplays, time_replays, capture):
     """The rest of the pages' layer around the hot path, measured the same way:
-    (1) the whole layer step with its epilogue (router with probabilities, chunk FFN,
-    residual + LayerNorm) over the same rotation; (2) the LayerNorm alone and (3) the
-    sparsity losses with their gradient alone, each over rotating input copies of at
-    least 512 MiB, timed with HIP events around graph replays."""
+    (1) the layer step with its residual + LayerNorm epilogue over the same rotation;
+    (2) the LayerNorm alone and (3) the sparsity losses with their gradient alone, each
+    over rotating input copies of at least 512 MiB; (4) the layer backward; all timed
+    with HIP events around graph replays."""
     T, d_h, E, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["n"]
     dev = torch.device("cuda:0")
-    nc, nd = len(copies), len(draws)
+    nc = len(copies)
     ln_g = torch.ones(d_h, dtype=torch.float32, device=dev)
     ln_b = torch.zeros(d_h, dtype=torch.float32, device=dev)
-    probs = torch.empty((T, E), dtype=torch.float32, device=dev)
     out = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
 
     def layer_step(i):
-        w = copies[i % nc]
-        d = draws[i % nd]
-        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=router_out[i % nd],
-                           probs=probs, workspace=router_ws)
-        s = router_out[i % nd] if args.workload == "e2e" else d["scores"]
-        bf.blockffn_chunk_ffn(d["x"], s, w["w1"], w["w2"], n, y=y, workspace=ws,
-                              union_counts=counts[i % nd])
-        bf.blockffn_add_layernorm(y, d["x"], ln_g, ln_b, out=out)
+        w, k = copies[i % nc], i % S
+        bf.blockffn_layer_forward(xs[k], w["w_r"], w["w1"], w["w2"], n, gain=gain, bias=w["bias"],
+                                  y=y, workspace=lws)
+        bf.blockffn_add_layernorm(y, xs[k], ln_g, ln_b, out=out)
 
     g = capture(layer_step)
     time_replays(g, wreplays)
@@ -313,8 +343,8 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain, router_o
         return ms, sets
 
     res = {"layer_with_epilogue": {
-        "what": "router (scores + probabilities) + chunk FFN + residual LayerNorm per "
-                "step, same rotation as the headline step",
+        "what": "blockffn_layer_forward + residual LayerNorm per step, same rotation as "
+                "the headline step",
         "ms_per_step": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3)}}
 
     # residual + LayerNorm at the end-to-end token count
@@ -356,12 +386,12 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, draws, gain, router_o
             "achieved_gbs": l_bytes / (l_ms * 1e-3) / 1e9,
             "frac_of_hbm_peak": l_bytes / (l_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "rotation_sets": l_sets}
-    res.update(bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts,
+    res.update(bench_backward(args, torch, np, bf, inputs, cfg, copies, xs, S, gain,
                               time_replays))
     return res
 
 
-def bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts, time_replays):
+def bench_backward(args, torch, np, bf, inputs, cfg, copies, xs, S_all, gain, time_replays):
     """The layer backward (router recomputed, expert pass, weight gradients, dx, router
     backward) at the workload's size over the same rotation, and at 2048 tokens. The
     roofline figures: flops of the five expert products per (chunk, union expert)
@@ -369,7 +399,7 @@ def bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts
     and dx, dW_r, dW1, dW2 written (fp32)."""
     T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
     dev = torch.device("cuda:0")
-    nc, nd = len(copies), len(draws)
+    nc = len(copies)
     f32 = torch.float32
     res = {}
 
@@ -399,8 +429,7 @@ def bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts
 
     def bwd(i):
         w = copies[i % nc]
-        d = draws[i % nd]
-        bf.blockffn_layer_backward(d["x"], w["w_r"], w["w1"], w["w2"], draws[(i + 1) % nd]["x"],
+        bf.blockffn_layer_backward(xs[i % S_all], w["w_r"], w["w1"], w["w2"], xs[(i + 1) % S_all],
                                    n, gain=gain, bias=w["bias"], out=out, workspace=bws)
 
     S = 16
@@ -422,22 +451,28 @@ def bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts
     y = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
     for i in range(S):
         w = copies[i % nc]
-        d = draws[i % nd]
-        bf.blockffn_router(d["x"], w["w_r"], gain, w["bias"], scores=sc)
-        bf.blockffn_chunk_ffn(d["x"], sc, w["w1"], w["w2"], n, y=y, union_counts=cnt,
+        bf.blockffn_router(xs[i % S_all], w["w_r"], gain, w["bias"], scores=sc)
+        bf.blockffn_chunk_ffn(xs[i % S_all], sc, w["w1"], w["w2"], n, y=y, union_counts=cnt,
                               expert_lists=lists)
         c = cnt.cpu().numpy()
         union_sum += float(c.sum())
         used += float(len(set(lists.cpu().numpy()[lists.cpu().numpy() >= 0].tolist())))
     res["layer_backward"] = dict(
-        shape=f"T={T} d_h={d_h} E={E} d_e={d_e} n={n} bf16, router scores (logit shift "
-              f"for ~80% zeros), fp32 gradients", **figures(T, union_sum / S, used / S, ms))
+        shape=f"T={T} d_h={d_h} E={E} d_e={d_e} n={n} bf16, the workload's router inputs, "
+              f"fp32 gradients", **figures(T, union_sum / S, used / S, ms))
 
     # (2) 2048 tokens on two weight copies
     Tp = 2048
     rng = np.random.default_rng(77)
-    xs = [torch.from_numpy(inputs.gaussian(rng, (Tp, d_h), 1.0, True)).to(dev, torch.bfloat16)
-          for _ in range(2)]
+
+    def tokens(ci):
+        w = copies[ci]
+        if w["bias"] is not None:          # the logit-shift router: i.i.d. tokens
+            return inputs.gaussian(rng, (Tp, d_h), 1.0, True)
+        act = inputs.markov_active(rng, Tp, E, 0.8, 0.7, 8)
+        return inputs.tokens_for_mask(rng, w["w_r"].float().cpu().numpy(), act, True)
+
+    xs = [torch.from_numpy(tokens(ci)).to(dev, torch.bfloat16) for ci in range(2)]
     dys = [torch.from_numpy(inputs.gaussian(rng, (Tp, d_h), 1.0, True)).to(dev, torch.bfloat16)
            for _ in range(2)]
     bws = torch.empty(bf.blockffn_layer_backward_workspace_bytes(Tp, d_h, E, d_e, n),
@@ -474,7 +509,8 @@ def bench_backward(args, torch, np, bf, inputs, cfg, copies, draws, gain, counts
         lp = listp.cpu().numpy()
         used += float(len(set(lp[lp >= 0].tolist())))
     res["layer_backward_T2048"] = dict(
-        shape=f"T={Tp} d_h={d_h} E={E} d_e={d_e} n={n} bf16, router scores, fp32 gradients",
+        shape=f"T={Tp} d_h={d_h} E={E} d_e={d_e} n={n} bf16, router inputs as the "
+              f"workload's, fp32 gradients",
         **figures(Tp, usum / 2, used / 2, ms))
     return res
 
@@ -512,10 +548,15 @@ def cpu_baseline(args, cfg, np, inputs):
     steps (router + chunk FFN) on fresh draws until the time budget is spent."""
     import oracle
     T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
+    markov = args.workload != "e2e"
     rng = np.random.default_rng(args.seed * 1000 + 100)
     w1, w2 = inputs.expert_weights(rng, E, d_e, d_h, True)
-    w_r = inputs.gaussian(rng, (E, d_h), 1.0 / np.sqrt(d_h), True)
-    bias = inputs.router_shift(w_r, 0.8)
+    if markov:
+        w_r = inputs.router_weight_orthonormal(rng, E, d_h, True)
+        bias = None
+    else:
+        w_r = inputs.gaussian(rng, (E, d_h), 1.0 / np.sqrt(d_h), True)
+        bias = inputs.router_shift(w_r, 0.8)
     # bounded token sample: at most 4 chunks per oracle step for the large workloads
     Ts = min(T, 4 * n)
     tokens = 0
@@ -523,13 +564,12 @@ def cpu_baseline(args, cfg, np, inputs):
     t0 = time.perf_counter()
     while True:
         rng = np.random.default_rng(args.seed * 1000 + 500 + steps)
-        x = inputs.gaussian(rng, (Ts, d_h), 1.0, True)
-        _, s_router = oracle.router(x, w_r, bias=bias)
-        if args.workload == "e2e":
-            s = s_router.astype(np.float32)
+        if markov:
+            x = inputs.tokens_for_mask(rng, w_r, inputs.markov_active(rng, Ts, E, 0.8, 0.7, 8), True)
         else:
-            s = inputs.scores_for_mask(rng, inputs.markov_active(rng, Ts, E, 0.8, 0.7, 8))
-        oracle.chunk_ffn(x, s, w1, w2, n)
+            x = inputs.gaussian(rng, (Ts, d_h), 1.0, True)
+        _, s_router = oracle.router(x, w_r, bias=bias)
+        oracle.chunk_ffn(x, s_router.astype(np.float32), w1, w2, n)
         tokens += Ts
         steps += 1
         el = time.perf_counter() - t0

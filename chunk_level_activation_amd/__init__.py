@@ -24,6 +24,8 @@ __all__ = [
     "blockffn_chunk_ffn_workspace", "blockffn_add_layernorm", "blockffn_sparsity_losses",
     "blockffn_sparsity_losses_workspace_bytes", "blockffn_sparsity_losses_workspace",
     "blockffn_layer_backward", "blockffn_layer_backward_workspace_bytes",
+    "blockffn_layer_forward", "blockffn_layer_forward_workspace_bytes",
+    "blockffn_layer_forward_workspace", "blockffn_layer_forward_fused",
     "blockffn_last_error", "blockffn_version", "load_library",
 ]
 
@@ -79,6 +81,13 @@ def load_library():
     lib.blockffn_layer_backward.argtypes = [P, P, P, P, F, P, P, I64, I64, I64, I64, I64, I, P,
                                             P, F, P, P, P, P, P, P, P, ctypes.c_size_t, P]
     lib.blockffn_layer_backward.restype = I
+    lib.blockffn_layer_forward_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.blockffn_layer_forward_workspace_bytes.restype = ctypes.c_size_t
+    lib.blockffn_layer_forward.argtypes = [P, P, P, P, F, P, P, I64, I64, I64, I64, I64, I, P, P,
+                                           P, ctypes.c_size_t, P]
+    lib.blockffn_layer_forward.restype = I
+    lib.blockffn_layer_forward_fused.argtypes = [I64, I64, I64, I64, I64, I, P]
+    lib.blockffn_layer_forward_fused.restype = I
     lib.blockffn_last_error.argtypes = []
     lib.blockffn_last_error.restype = ctypes.c_char_p
     lib.blockffn_version.argtypes = []
@@ -333,3 +342,54 @@ def blockffn_layer_backward(x, w_r, w1, w2, dy, n: int, gain=None, bias=None,
             _stream(stream)]
     _check(lib.blockffn_layer_backward(*args))
     return out
+
+
+def blockffn_layer_forward_workspace_bytes(T: int, d_h: int, E: int, d_e: int, n: int,
+                                           dtype: int) -> int:
+    nbytes = load_library().blockffn_layer_forward_workspace_bytes(T, d_h, E, d_e, n, dtype)
+    if nbytes == 0:
+        raise BlockFFNError(1, blockffn_last_error())
+    return int(nbytes)
+
+
+def blockffn_layer_forward_workspace(T: int, d_h: int, E: int, d_e: int, n: int, dtype: int,
+                                     device="cuda"):
+    """A zero-filled layer workspace: it must start zeroed and every call returns it to
+    that state."""
+    import torch
+    return torch.zeros(blockffn_layer_forward_workspace_bytes(T, d_h, E, d_e, n, dtype),
+                       dtype=torch.uint8, device=device)
+
+
+def blockffn_layer_forward(x, w_r, w1, w2, n: int, gain=None, bias=None, eps: float = FP32_EPS,
+                           *, y=None, scores=None, workspace=None, stream=None):
+    """y [T, d_h] = chunk FFN of x under the router's scores (see blockffn.h); `scores`
+    ([T, E] float32), when given, receives the scores."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    E, d_e, _ = w1.shape
+    if tuple(w_r.shape) != (E, d_h) or tuple(w2.shape) != (E, d_h, d_e):
+        raise ValueError("w_r must be [E, d_h], w2 [E, d_h, d_e]")
+    if w_r.dtype != x.dtype or w1.dtype != x.dtype or w2.dtype != x.dtype:
+        raise TypeError("x, w_r, w1 and w2 must share a dtype")
+    code = _dtype_code(x)
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = blockffn_layer_forward_workspace(T, d_h, E, d_e, n, code, x.device)
+    args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
+            _dev(bias, "bias", torch.float32), float(eps), _dev(w1, "w1"), _dev(w2, "w2"),
+            T, d_h, E, d_e, int(n), code, _dev(y, "y", x.dtype),
+            _dev(scores, "scores", torch.float32), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    _check(lib.blockffn_layer_forward(*args))
+    return y
+
+
+def blockffn_layer_forward_fused(T: int, d_h: int, E: int, d_e: int, n: int, dtype: int,
+                                 stream=None) -> bool:
+    """True when blockffn_layer_forward runs router and FFN in one launch for these
+    sizes on the current device."""
+    return bool(load_library().blockffn_layer_forward_fused(T, d_h, E, d_e, n, dtype,
+                                                            _stream(stream)))

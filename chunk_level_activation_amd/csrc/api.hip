@@ -476,4 +476,96 @@ blockffn_status_t blockffn_layer_backward(const void *x, const void *w_r, const 
     return BLOCKFFN_OK;
 }
 
+// Layer workspace: [chunk-FFN workspace][scores T x E fp32][router workspace].
+namespace {
+struct LayerWs {
+    size_t ffn, scores, router, total;
+};
+LayerWs layer_ws(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n, int dtype)
+{
+    LayerWs w{};
+    w.ffn = blockffn_chunk_ffn_workspace_bytes(T, d_h, E, d_e, n, dtype);
+    w.router = blockffn_router_workspace_bytes(T, d_h, E, dtype);
+    if (w.ffn == 0 || w.router == 0)
+        return w;
+    w.scores = blockffn::align_up(w.ffn, 256);
+    const size_t router_off = blockffn::align_up(w.scores + (size_t)T * E * 4, 256);
+    w.total = router_off + w.router;
+    w.router = router_off;
+    return w;
+}
+}  // namespace
+
+size_t blockffn_layer_forward_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                              int64_t n, int dtype)
+{
+    if (check_ffn_sizes(T, d_h, E, d_e, n, dtype) != BLOCKFFN_OK)
+        return 0;
+    return layer_ws(T, d_h, E, d_e, n, dtype).total;
+}
+
+int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n,
+                                 int dtype, void *stream)
+{
+    if (check_ffn_sizes(T, d_h, E, d_e, n, dtype) != BLOCKFFN_OK)
+        return 0;
+    const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
+    int xcds = 0, members = 0;
+    return p.decode && decode_grid(static_cast<hipStream_t>(stream), p, &xcds, &members) &&
+                   blockffn::layer_decode_supported(E, d_h, members)
+               ? 1
+               : 0;
+}
+
+blockffn_status_t blockffn_layer_forward(const void *x, const void *w_r, const float *gain,
+                                         const float *bias, float eps, const void *w1,
+                                         const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                         int64_t d_e, int64_t n, int dtype, void *y, float *scores,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    blockffn_status_t st = check_ffn_sizes(T, d_h, E, d_e, n, dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if (!x || !w_r || !w1 || !w2 || !y || !workspace)
+        return fail(BLOCKFFN_EINVAL, "x, w_r, w1, w2, y and workspace must not be NULL");
+    if (!(eps >= 0.0f))
+        return fail(BLOCKFFN_EINVAL, "eps must be >= 0");
+    const size_t ea = dtype == BLOCKFFN_BF16 ? 16 : 4;
+    if (!aligned(x, ea) || !aligned(w_r, ea) || !aligned(w1, ea) || !aligned(w2, ea) ||
+        !aligned(y, ea))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x, w_r, w1, w2 and y must be " + std::to_string(ea) +
+                                               "-byte aligned");
+    if ((scores && !aligned(scores, 4)) || (gain && !aligned(gain, 4)) || (bias && !aligned(bias, 4)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "float arrays must be 4-byte aligned");
+    if (!aligned(workspace, 256))
+        return fail(BLOCKFFN_EUNSUPPORTED, "workspace needs 256-byte alignment");
+    const LayerWs L = layer_ws(T, d_h, E, d_e, n, dtype);
+    if (workspace_bytes < L.total)
+        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                             " bytes, needs " + std::to_string(L.total));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
+    int xcds = 0, members = 0;
+    if (p.decode && decode_grid(s, p, &xcds, &members) &&
+        blockffn::layer_decode_supported(E, d_h, members)) {
+        // one launch: the router computed by every workgroup from its staged x
+        const hipError_t err = blockffn::launch_layer_bf16_decode(
+            p, xcds, members, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_r),
+            gain, bias, eps, static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w2),
+            static_cast<uint16_t *>(y), scores, workspace, s);
+        if (err != hipSuccess)
+            return fail(BLOCKFFN_EHIP, std::string("layer launch failed: ") + hipGetErrorString(err));
+        g_last_error.clear();
+        return BLOCKFFN_OK;
+    }
+    char *base = static_cast<char *>(workspace);
+    float *sc = scores ? scores : reinterpret_cast<float *>(base + L.scores);
+    st = blockffn_router(x, w_r, gain, bias, eps, T, d_h, E, dtype, sc, nullptr, 1.0f, nullptr,
+                         base + L.router, workspace_bytes - L.router, stream);
+    if (st != BLOCKFFN_OK)
+        return st;
+    return blockffn_chunk_ffn(x, sc, w1, w2, T, d_h, E, d_e, n, dtype, y, workspace, L.scores,
+                              nullptr, nullptr, nullptr, stream);
+}
+
 }  // extern "C"

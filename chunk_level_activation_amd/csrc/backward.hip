@@ -115,7 +115,7 @@ __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 __global__ void __launch_bounds__(kBT) transpose_tiles_kernel(const uint16_t *src, Dims d,
                                                               uint16_t *dst)
 {
-    __shared__ uint16_t t[kTileM][kTrCols + 8];
+    __shared__ alignas(16) uint16_t t[kTileM][kTrCols + 8];
     const int tile = blockIdx.x, jb = blockIdx.y * kTrCols, tid = threadIdx.x;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint64_t)d.T * d.d_h * 2);
 #pragma unroll
@@ -143,7 +143,7 @@ __global__ void __launch_bounds__(kBT) transpose_weights_kernel(const uint16_t *
                                                                 const int32_t *tile_count,
                                                                 uint16_t *dst)
 {
-    __shared__ uint16_t t[64][64 + 8];
+    __shared__ alignas(16) uint16_t t[64][64 + 8];
     const int e = blockIdx.z;
     if (tile_count[e] == 0)
         return;
@@ -188,7 +188,7 @@ __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
     const int cnt = a.tile_count[e];
     if (grp * kPassTiles >= cnt)
         return;
-    __shared__ uint16_t As1[kTM * kPP], Bs1[kTM * kPP], As2[kTM * kPP], Bs2[kTM * kPP];
+    __shared__ alignas(16) uint16_t As1[kTM * kPP], Bs1[kTM * kPP], As2[kTM * kPP], Bs2[kTM * kPP];
     __shared__ float red[kTM][65];
     __shared__ float dsacc[kTM], scol[kTM];
     __shared__ int64_t tok[kTM];
@@ -341,7 +341,7 @@ __global__ void __launch_bounds__(kBT, 2) wgrad_kernel(WgradArgs a)
     const int M = kind == 0 ? d.d_e : d.d_h, N = kind == 0 ? d.d_h : d.d_e;
     const int MT = M / kTM;
     const int mt = t2 % MT, nt = t2 / MT;
-    __shared__ uint16_t As[kTM * kLP], Bs[kTM * kLP];
+    __shared__ alignas(16) uint16_t As[kTM * kLP], Bs[kTM * kLP];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave & 1, wn = wave >> 1;
     const int cnt = a.tile_count[e];
@@ -430,7 +430,7 @@ __global__ void __launch_bounds__(kBT, 2) dx_kernel(DxArgs a)
 {
     const Dims &d = a.d;
     const int tg = blockIdx.x, nb = blockIdx.y * kTM, z = blockIdx.z;
-    __shared__ uint16_t As[kTM * kLP], Bs[kTM * kLP];
+    __shared__ alignas(16) uint16_t As[kTM * kLP], Bs[kTM * kLP];
     __shared__ uint64_t um[kXTiles][4];     // union masks of the 4 tiles' chunks
     __shared__ int elist[256];
     __shared__ int ecount;

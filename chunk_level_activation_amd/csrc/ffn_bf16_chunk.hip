@@ -85,8 +85,8 @@ struct Shared {
     int list[256];
     int flag;
     float s_col[kTileM];
-    float red[4][2][kTileM][33];              // up: [row quarter][k half]; down: [part][half]
-    uint16_t xs[kTileM * kXPitch];            // staged x slice (up items)
+    alignas(16) float red[4][2][kTileM][33];  // up: [row quarter][k half]; down: [part][half]
+    alignas(16) uint16_t xs[kTileM * kXPitch];  // staged x slice (up items)
 };
 
 struct Rsrc {

@@ -233,3 +233,31 @@ def layernorm_inputs(seed: int, T: int, d_h: int, bf16: bool):
     gamma = rng.uniform(0.5, 1.5, d_h).astype(np.float32)
     beta = (0.1 * rng.standard_normal(d_h)).astype(np.float32)
     return y, x, gamma, beta
+
+
+# ------------------------------------------------------------------ router inputs with a prescribed activity
+
+def router_weight_orthonormal(rng: np.random.Generator, E: int, d_h: int, bf16: bool) -> np.ndarray:
+    """W_r [E, d_h] with orthonormal rows (from the QR factor of a Gaussian matrix): the
+    same scale as W_r ~ N(0, 1/d_h), and W_r W_r^T = I (up to bf16 rounding)."""
+    q, _ = np.linalg.qr(rng.standard_normal((d_h, E)))
+    w = q.T.astype(np.float32)
+    return round_bf16(w) if bf16 else w
+
+
+def tokens_for_mask(rng: np.random.Generator, w_r: np.ndarray, active: np.ndarray,
+                    bf16: bool) -> np.ndarray:
+    """x [T, d_h] whose router logits W_r x_t equal a prescribed c_t: c[t,e] =
+    |N(0,1)| + 0.1 where active[t,e], -(|N(0,1)| + 0.1) elsewhere, so a router with
+    these orthonormal W_r rows (and no logit shift) is active exactly on the mask.
+    x_t = W_r^T c_t + the component of z_t ~ N(0, I) orthogonal to W_r's rows, so x
+    keeps unit-variance coordinates. With bf16 rounding of x and W_r the logits move
+    by ~1e-3 at d_h = 2048, far below the 0.1 margin, so the mask is exact."""
+    T, E = active.shape
+    w = w_r.astype(np.float64)
+    mag = np.abs(rng.standard_normal((T, E))) + 0.1
+    c = np.where(active, mag, -mag)
+    z = rng.standard_normal((T, w.shape[1]))
+    x = c @ w + z - (z @ w.T) @ w
+    x = x.astype(np.float32)
+    return round_bf16(x) if bf16 else x

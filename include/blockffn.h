@@ -143,6 +143,41 @@ blockffn_status_t blockffn_chunk_ffn(const void *x, const float *scores, const v
                                      int32_t *union_counts_out, void *stream);
 
 /*
+ * Bytes of workspace blockffn_layer_forward needs (0 when the sizes are invalid).
+ */
+size_t blockffn_layer_forward_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                              int64_t n, int dtype);
+
+/*
+ * The whole layer forward, router then chunked expert FFN (skill page, "Architecture
+ * Overview" and "Core Concept"): y = blockffn_chunk_ffn(x, s, W1, W2, n) with
+ * s = blockffn_router(x, W_r, gain, bias, eps). Arguments as in those two calls;
+ * scores [T, E] float or NULL receives s. The workspace (at least
+ * blockffn_layer_forward_workspace_bytes(...), 256-byte aligned) must be ZERO-FILLED
+ * before its first use; every call returns its counters to zero. For one chunk of at
+ * most 32 tokens in bf16 with E <= 64 and d_h a multiple of 256 up to 2048 (and the
+ * chunk FFN's single-chunk schedule available) the router runs inside the FFN launch:
+ * the workgroups that share an XCD split the E logits between them (fp32 sums of bf16
+ * products, the eight eighths of d_h added in order), exchange them through that
+ * XCD's L2, and each applies bias, ReLU, RMSNorm and gain itself. The scores can then
+ * differ from blockffn_router's in the last bits (summation order), within the
+ * router's tolerance. Otherwise the call is blockffn_router followed by
+ * blockffn_chunk_ffn.
+ */
+blockffn_status_t blockffn_layer_forward(const void *x, const void *w_r, const float *gain,
+                                         const float *bias, float eps, const void *w1,
+                                         const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                         int64_t d_e, int64_t n, int dtype, void *y, float *scores,
+                                         void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * 1 when blockffn_layer_forward with these sizes runs router and FFN in one launch on
+ * the current device (probing the device on first use), else 0.
+ */
+int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n,
+                                 int dtype, void *stream);
+
+/*
  * Residual + LayerNorm of the layer output (skill page, "Full BlockFFN Layer with
  * Combined Losses": the layer returns nn.LayerNorm(d_h) of the expert output plus
  * the layer input):

@@ -98,3 +98,19 @@ def test_e2e_router_shift_gives_80_percent_zeros():
     inp = inputs.make_workload("e2e", seed=0, T=1024)
     l, _ = oracle.router(inp.x, inp.w_r, bias=inp.bias)
     assert abs((l <= 0).mean() - 0.8) < 0.01
+
+
+def test_tokens_for_mask_give_the_mask():
+    """Router inputs drawn for a mask: W_r has orthonormal rows and the logits W_r x
+    (plain float64 products) are positive exactly where the mask is set, with a margin
+    of at least 0.1 - 1e-2 after bf16 rounding; x has unit-variance coordinates."""
+    rng = np.random.default_rng(3)
+    w = inputs.router_weight_orthonormal(rng, 64, 2048, True)
+    gram = w.astype(np.float64) @ w.astype(np.float64).T
+    assert np.abs(gram - np.eye(64)).max() < 2e-2
+    act = inputs.markov_active(rng, 64, 64, 0.8, 0.7, 8)
+    x = inputs.tokens_for_mask(rng, w, act, True)
+    logits = x.astype(np.float64) @ w.astype(np.float64).T
+    assert np.array_equal(logits > 0, act)
+    assert np.abs(logits).min() > 0.09
+    assert abs(x.std() - 1.0) < 0.05
