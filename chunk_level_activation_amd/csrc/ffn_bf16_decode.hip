@@ -57,7 +57,7 @@ constexpr int kThreads = 512;        // 8 waves
 constexpr int kWaves = kThreads / kWave;
 static_assert(kWaves == 8, "the fused router splits d_h into eighths, one per wave");
 constexpr int kMaxXLoads = 16;       // 16-byte x chunks per thread: d_h <= 2048
-constexpr int kMaxScoreLoads = 8;    // scores per thread: T * E <= 4096
+constexpr int kMaxScoreLoads = 8;    // scores per thread (token tid/16, experts tid%16 + 16 i): E <= 128
 constexpr int kMaxKSteps = 16;       // 32-wide k steps per up wave: d_h / 4 <= 512
 constexpr int kGroupUnitsMax = 1024; // hidden units of the union per group
 constexpr int kMaxRows = 32;         // W1 rows (hidden units) per member
@@ -99,7 +99,7 @@ struct DecodeArgs {
 };
 
 struct Shared {
-    uint64_t mask[kMaxWords];
+    uint64_t wmask[kWaves][kMaxWords];
     int list[256];
     int flag;
     int rflag;
@@ -112,32 +112,50 @@ struct Shared {
     alignas(16) uint16_t xs[kTileM * kMaxDh];   // x, 16-byte chunk c of token t at chunk c ^ (t & 15)
 };
 
-// Union of the experts active in the chunk from the scores each thread holds (entry
-// tid + 512 i of the T x E array; entries past the end read as zero), ascending list
-// in LDS; returns |U|. sh.mask must be zero and visible on entry.
-__device__ int union_from_scores(const DecodeArgs &a, Shared &sh, const float (&sv)[kMaxScoreLoads])
+// Union of the experts active in the chunk, ascending list in LDS; returns |U| and
+// leaves the mask words in wm. Thread tid holds in sv[i] the score of token tid / 16
+// and expert tid % 16 + 16 i (zero past T and past E), so a wave covers 4 tokens:
+// one ballot per i and an OR of its four 16-bit token groups give the wave's bits of
+// experts 16 i .. 16 i + 15; the 8 waves meet in LDS.
+__device__ int union_of_tile(const DecodeArgs &a, Shared &sh, const float (&sv)[kMaxScoreLoads],
+                             uint64_t (&wm)[kMaxWords])
 {
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
 #pragma unroll
-    for (int i = 0; i < kMaxScoreLoads; ++i)
-        if (sv[i] != 0.0f) {
-            const int e = (tid + i * kThreads) % a.E;
-            atomicOr(reinterpret_cast<unsigned long long *>(&sh.mask[e >> 6]), 1ull << (e & 63));
-        }
+    for (int w = 0; w < kMaxWords; ++w)
+        wm[w] = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxScoreLoads; ++i) {
+        const uint64_t b = __ballot(sv[i] != 0.0f);
+        const uint64_t m16 = (b | (b >> 16) | (b >> 32) | (b >> 48)) & 0xffffull;
+        wm[i / 4] |= m16 << (16 * (i % 4));
+    }
+    if (lane < kMaxWords)
+        sh.wmask[wave][lane] = wm[lane];
     __syncthreads();
-    const int W = (a.E + 63) >> 6;
     int cnt = 0;
-    for (int w = 0; w < W; ++w)
-        cnt += __popcll(sh.mask[w]);
+#pragma unroll
+    for (int w = 0; w < kMaxWords; ++w) {
+        uint64_t m = 0;
+#pragma unroll
+        for (int v = 0; v < kWaves; ++v)
+            m |= sh.wmask[v][w];
+        wm[w] = m;
+        cnt += __popcll(m);
+    }
     if (tid < a.E) {
         const int w = tid >> 6, bit = tid & 63;
-        const uint64_t word = sh.mask[w];
-        if ((word >> bit) & 1ull) {
-            int pos = __popcll(word & ((1ull << bit) - 1ull));
-            for (int v = 0; v < w; ++v)
-                pos += __popcll(sh.mask[v]);
-            sh.list[pos] = tid;
+        uint64_t word = 0;
+        int pos = 0;
+#pragma unroll
+        for (int v = 0; v < kMaxWords; ++v) {
+            if (v < w)
+                pos += __popcll(wm[v]);
+            if (v == w)
+                word = wm[v];
         }
+        if ((word >> bit) & 1ull)
+            sh.list[pos + __popcll(word & ((1ull << bit) - 1ull))] = tid;
     }
     __syncthreads();
     return cnt;
@@ -199,23 +217,26 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     const int nxl = kTileM * cpr / kThreads;
     bf16x8 xv[kMaxXLoads];
     int cnt;
+    uint64_t wm[kMaxWords];
     if constexpr (!ROUTER) {
         // Prologue loads, all unconditional (entries past a buffer's end read as zero) so
         // the compiler can wait for the scores alone: the union's scores first, then x.
         const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scores, (uint64_t)a.T * a.E * 4);
         float sv[kMaxScoreLoads];
+        {
+            const int tt = tid >> 4, sub = tid & 15;
 #pragma unroll
-        for (int i = 0; i < kMaxScoreLoads; ++i)
-            sv[i] = bload_f1<0>(rs, (uint32_t)((tid + i * kThreads) * 4));
+            for (int i = 0; i < kMaxScoreLoads; ++i) {
+                const int e = sub + 16 * i;
+                sv[i] = bload_f1<0>(rs, tt < a.T && e < a.E ? (uint32_t)((tt * a.E + e) * 4) : kOOB);
+            }
+        }
         // x, contiguous: 16-byte chunk q = i * 512 + tid of the 32 x d_h tile (token
         // q / cpr, chunk q % cpr); tokens past T read as zero.
 #pragma unroll
         for (int i = 0; i < kMaxXLoads; ++i)
             xv[i] = bload<0>(rx, (uint32_t)((i * kThreads + tid) * 16));
-        if (tid < kMaxWords)
-            sh.mask[tid] = 0;
-        __syncthreads();
-        cnt = union_from_scores(a, sh, sv);
+        cnt = union_of_tile(a, sh, sv, wm);
     } else {
         // x (every member stages all of it for the up phase) and this member's share of
         // the router: experts e0 .. e0 + EPM (EPM = ceil(E / P) <= 2). Wave w takes the
@@ -246,8 +267,6 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             bv[i] = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
         }
         const uint32_t repoch = 1u + ld_counter(&a.rflags[g * a.P + k]);
-        if (tid < kMaxWords)
-            sh.mask[tid] = 0;
 #pragma unroll
         for (int i = 0; i < kMaxXLoads; ++i)
             if (i < nxl) {
@@ -311,9 +330,11 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             }
         }
         __syncthreads();
+        float sv[kMaxScoreLoads];
         {
             // this thread's 4 logits from L2, then bias, ReLU, RMSNorm over the E experts,
-            // gain; the scores go to LDS [e][token] (pitch kRedPitch); tokens past T get 0
+            // gain; the scores go to LDS [e][token] (pitch kRedPitch) and to sv for the
+            // union; tokens past T get 0
             float lv[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -337,28 +358,30 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int e = sub + 16 * i;
+                const float sc = tt < a.T && e < a.E ? rv[i] * inv * gv[i] : 0.0f;
+                sv[i] = sc;
                 if (e < a.E) {
-                    const float sc = tt < a.T ? rv[i] * inv * gv[i] : 0.0f;
                     sh.red[e * kRedPitch + tt] = sc;
                     if (blockIdx.x == 0 && a.scores_out && tt < a.T)
                         a.scores_out[tt * a.E + e] = sc;
                 }
             }
-        }
-        __syncthreads();
-        float sv[kMaxScoreLoads];
 #pragma unroll
-        for (int i = 0; i < kMaxScoreLoads; ++i) {
-            const int idx = tid + i * kThreads;
-            sv[i] = idx < a.T * a.E ? sh.red[(idx % a.E) * kRedPitch + idx / a.E] : 0.0f;
+            for (int i = 4; i < kMaxScoreLoads; ++i)
+                sv[i] = 0.0f;
         }
-        cnt = union_from_scores(a, sh, sv);
+        cnt = union_of_tile(a, sh, sv, wm);
     }
 
     if (blockIdx.x == 0) {
         const int W = (a.E + 63) >> 6;
-        if (a.masks_out && tid < W)
-            a.masks_out[tid] = sh.mask[tid];
+        if (a.masks_out && tid < W) {
+            uint64_t m = wm[0];
+#pragma unroll
+            for (int w = 1; w < kMaxWords; ++w)
+                m = tid == w ? wm[w] : m;
+            a.masks_out[tid] = m;
+        }
         if (a.lists_out)
             for (int i = tid; i < a.E; i += kThreads)
                 a.lists_out[i] = i < cnt ? sh.list[i] : -1;
