@@ -18,9 +18,12 @@ distinct weight copies (>= 512 MiB in all) and the next of 16 mask draws, so the
 
 Prints ONE JSON line (see the keys below). `roofline` is for the dominant kernel: the
 one-launch layer kernel at the decode chunk (its duration is the step's), else the
-chunk-FFN launches: algorithmic bytes per call (the union experts' W1 and W2 slices,
-W_r when the router is inside, x and y) over its average duration, measured with HIP
-events around graph replays on the stream it runs on.
+chunk-FFN launches. For one chunk the bound is HBM: algorithmic bytes per call (the
+union experts' W1 and W2 slices, W_r when the router is inside, x and y) over its
+average duration. For several chunks the weights are shared by the chunks and stay in
+the caches, so the bound is the bf16 MFMA rate: the five expert products' flops of
+every (chunk, union expert) pair over the average duration. Durations are measured
+with HIP events around graph replays on the stream the kernels run on.
 """
 from __future__ import annotations
 
@@ -253,7 +256,27 @@ def main(argv=None):
     if args.cpu_seconds > 0:
         cpu = cpu_baseline(args, cfg, np, inputs)
 
-    traffic = read_traffic(args.workload)
+    traffic = read_traffic(args.workload, fused)
+    if C == 1:
+        # one chunk: the weight stream (each union expert's W1 and W2 read once) bounds it
+        roofline = {
+            "kernel": kernel_name, "bound": "hbm", "achieved": achieved_gbs,
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved_gbs / HBM_PEAK_GBS,
+            "traffic": traffic, "algorithmic_bytes_per_launch": kernel_bytes,
+            "avg_launch_ms": kernel_ms, "launch_timing": timing,
+            "mfma_frac": flops / (kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+        }
+    else:
+        # many chunks: every chunk's union experts are multiplied with its 32 tokens while
+        # the weights, shared by the chunks, stay in the caches; the products bound it
+        tflops = flops / (kernel_ms * 1e-3) / 1e12
+        roofline = {
+            "kernel": kernel_name, "bound": "mfma", "achieved": tflops,
+            "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s", "frac": tflops / BF16_PEAK_TFLOPS,
+            "traffic": traffic, "algorithmic_flops_per_launch": flops,
+            "avg_launch_ms": kernel_ms, "launch_timing": timing,
+            "effective_gbs_of_chunk_unions": achieved_gbs,
+        }
     activity = ("router activity following Markov masks at 80% TLS / 70% 8-token CLS "
                 "(orthonormal W_r, x drawn for the masks)" if args.workload != "e2e" else
                 "router with a logit shift for ~80% zeros, i.i.d. x")
@@ -280,19 +303,7 @@ def main(argv=None):
             "timing": f"hipGraph replays of {S} captured steps; eager Python-launched "
                       f"step {eager_ms:.4f} ms",
         },
-        "roofline": {
-            "kernel": kernel_name,
-            "bound": "hbm",
-            "achieved": achieved_gbs,
-            "peak": HBM_PEAK_GBS,
-            "unit": "GB/s",
-            "frac": achieved_gbs / HBM_PEAK_GBS,
-            "traffic": traffic,
-            "algorithmic_bytes_per_launch": kernel_bytes,
-            "avg_launch_ms": kernel_ms,
-            "launch_timing": timing,
-            "mfma_frac": flops / (kernel_ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
-        },
+        "roofline": roofline,
         "dense_ffn": dense,
         "extras": extras,
         "cpu_baseline": cpu,
@@ -515,12 +526,13 @@ def bench_backward(args, torch, np, bf, inputs, cfg, copies, xs, S_all, gain, ti
     return res
 
 
-def read_traffic(workload):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, if it was
-    taken on the current source of the measured kernel (the files its
-    `kernel_sources` line names); else None."""
+def read_traffic(workload, fused):
+    """HBM bytes per launch of the roofline kernel (the one-launch layer when fused,
+    else the chunk FFN) from the committed rocprofv3 counter summary, if it was taken
+    on the current source of that kernel (the files its `kernel_sources` line names);
+    else None."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"ffn_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{'layer' if fused else 'ffn'}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
