@@ -143,6 +143,12 @@ def main(argv=None):
     ws = bf.blockffn_chunk_ffn_workspace(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16, dev)
     router_ws = bf.blockffn_router_workspace(T, d_h, E, bf.BLOCKFFN_BF16, dev)
     fused = bf.blockffn_layer_forward_fused(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16)
+    if fused:
+        # the one-launch layer reads the expert weights in the tiled layout; each copy is
+        # packed once here, outside every timed region (as when weights are loaded)
+        for w in copies:
+            w["packed"] = bf.blockffn_pack_weights(w["w1"], w["w2"])
+        torch.cuda.synchronize()
     counts = [torch.zeros(C, dtype=torch.int32, device=dev) for _ in range(S)]
     scores = [torch.empty((T, E), dtype=torch.float32, device=dev) for _ in range(S)]
     nc, nd = len(copies), len(draws)
@@ -150,6 +156,15 @@ def main(argv=None):
     # step i uses weight copy i % nc and the x drawn for step i % S (S = lcm of the two
     # rotation lengths, so every replay of an S-step graph walks the same sequence)
     def step(i):
+        w, k = copies[i % nc], i % S
+        if fused:
+            bf.blockffn_layer_forward_packed(xs[k], w["w_r"], w["packed"], E, d_e, n, gain=gain,
+                                             bias=w["bias"], y=y, workspace=lws)
+        else:
+            bf.blockffn_layer_forward(xs[k], w["w_r"], w["w1"], w["w2"], n, gain=gain,
+                                      bias=w["bias"], y=y, workspace=lws)
+
+    def step_rowmajor(i):
         w, k = copies[i % nc], i % S
         bf.blockffn_layer_forward(xs[k], w["w_r"], w["w1"], w["w2"], n, gain=gain, bias=w["bias"],
                                   y=y, workspace=lws)
@@ -206,6 +221,13 @@ def main(argv=None):
     time_replays(g_sep, wreplays)
     sep_ms = time_replays(g_sep, replays) / nsteps
     del g_sep
+    # the one-launch layer on the row-major weights
+    rowmajor_ms = None
+    if fused:
+        g_rm = capture(step_rowmajor)
+        time_replays(g_rm, wreplays)
+        rowmajor_ms = time_replays(g_rm, replays) / nsteps
+        del g_rm
 
     # Python-launched steps, for comparison (host-bound at these sizes)
     eager_n = min(200, nsteps)
@@ -224,7 +246,8 @@ def main(argv=None):
     if fused:
         kernel_bytes = weight_bytes + act_bytes + E * d_h * 2       # + W_r
         kernel_ms = ms_per_step
-        kernel_name = "layer forward, router and chunk FFN in one launch (blockffn_layer_forward)"
+        kernel_name = ("layer forward, router and chunk FFN in one launch, tiled weights "
+                       "(blockffn_layer_forward_packed)")
         timing = "HIP events around graph replays of the steps (one launch each)"
     else:
         kernel_bytes = weight_bytes + act_bytes + T * E * 4         # + scores
@@ -251,6 +274,10 @@ def main(argv=None):
             "what": "blockffn_router + blockffn_chunk_ffn as two launches, same inputs",
             "ms_per_step": sep_ms, "tokens_per_s": T / (sep_ms * 1e-3),
             "chunk_ffn_ms": ffn_avg_ms}
+        if rowmajor_ms is not None:
+            extras["layer_rowmajor_weights"] = {
+                "what": "blockffn_layer_forward (one launch) on the row-major W1 and W2",
+                "ms_per_step": rowmajor_ms, "tokens_per_s": T / (rowmajor_ms * 1e-3)}
 
     cpu = None
     if args.cpu_seconds > 0:
@@ -328,8 +355,12 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws, 
 
     def layer_step(i):
         w, k = copies[i % nc], i % S
-        bf.blockffn_layer_forward(xs[k], w["w_r"], w["w1"], w["w2"], n, gain=gain, bias=w["bias"],
-                                  y=y, workspace=lws)
+        if "packed" in w:
+            bf.blockffn_layer_forward_packed(xs[k], w["w_r"], w["packed"], E, cfg["d_e"], n,
+                                             gain=gain, bias=w["bias"], y=y, workspace=lws)
+        else:
+            bf.blockffn_layer_forward(xs[k], w["w_r"], w["w1"], w["w2"], n, gain=gain,
+                                      bias=w["bias"], y=y, workspace=lws)
         bf.blockffn_add_layernorm(y, xs[k], ln_g, ln_b, out=out)
 
     g = capture(layer_step)
@@ -354,7 +385,7 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws, 
         return ms, sets
 
     res = {"layer_with_epilogue": {
-        "what": "blockffn_layer_forward + residual LayerNorm per step, same rotation as "
+        "what": "the layer step (as the headline) + residual LayerNorm, same rotation as "
                 "the headline step",
         "ms_per_step": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3)}}
 

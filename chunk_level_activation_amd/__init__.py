@@ -26,6 +26,7 @@ __all__ = [
     "blockffn_layer_backward", "blockffn_layer_backward_workspace_bytes",
     "blockffn_layer_forward", "blockffn_layer_forward_workspace_bytes",
     "blockffn_layer_forward_workspace", "blockffn_layer_forward_fused",
+    "blockffn_pack_weights_bytes", "blockffn_pack_weights", "blockffn_layer_forward_packed",
     "blockffn_last_error", "blockffn_version", "load_library",
 ]
 
@@ -88,6 +89,13 @@ def load_library():
     lib.blockffn_layer_forward.restype = I
     lib.blockffn_layer_forward_fused.argtypes = [I64, I64, I64, I64, I64, I, P]
     lib.blockffn_layer_forward_fused.restype = I
+    lib.blockffn_pack_weights_bytes.argtypes = [I64, I64, I64, I]
+    lib.blockffn_pack_weights_bytes.restype = ctypes.c_size_t
+    lib.blockffn_pack_weights.argtypes = [P, P, I64, I64, I64, I, P, P]
+    lib.blockffn_pack_weights.restype = I
+    lib.blockffn_layer_forward_packed.argtypes = [P, P, P, P, F, P, I64, I64, I64, I64, I64, I, P,
+                                                  P, P, ctypes.c_size_t, P]
+    lib.blockffn_layer_forward_packed.restype = I
     lib.blockffn_last_error.argtypes = []
     lib.blockffn_last_error.restype = ctypes.c_char_p
     lib.blockffn_version.argtypes = []
@@ -384,6 +392,59 @@ def blockffn_layer_forward(x, w_r, w1, w2, n: int, gain=None, bias=None, eps: fl
             _dev(scores, "scores", torch.float32), _dev(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)]
     _check(lib.blockffn_layer_forward(*args))
+    return y
+
+
+def blockffn_pack_weights_bytes(E: int, d_h: int, d_e: int, dtype: int) -> int:
+    return int(load_library().blockffn_pack_weights_bytes(E, d_h, d_e, dtype))
+
+
+def blockffn_pack_weights(w1, w2, *, packed=None, stream=None):
+    """The expert weights W1 [E, d_e, d_h] and W2 [E, d_h, d_e] (bf16) in the tiled
+    layout of blockffn_pack_weights (see blockffn.h): a flat bf16 tensor of
+    2*E*d_h*d_e elements."""
+    import torch
+    lib = load_library()
+    E, d_e, d_h = w1.shape
+    if tuple(w2.shape) != (E, d_h, d_e) or w2.dtype != w1.dtype:
+        raise ValueError("w2 must be [E, d_h, d_e] of w1's dtype")
+    code = _dtype_code(w1)
+    nbytes = blockffn_pack_weights_bytes(E, d_h, d_e, code)
+    if nbytes == 0:
+        raise BlockFFNError(1, "pack_weights: unsupported sizes or dtype")
+    if packed is None:
+        packed = torch.empty(nbytes // 2, dtype=w1.dtype, device=w1.device)
+    elif packed.numel() * packed.element_size() < nbytes:
+        raise ValueError("packed is too small")
+    _check(lib.blockffn_pack_weights(_dev(w1, "w1"), _dev(w2, "w2"), E, d_h, d_e, code,
+                                     _dev(packed, "packed"), _stream(stream)))
+    return packed
+
+
+def blockffn_layer_forward_packed(x, w_r, packed, E: int, d_e: int, n: int, gain=None,
+                                  bias=None, eps: float = FP32_EPS, *, y=None, scores=None,
+                                  workspace=None, stream=None):
+    """blockffn_layer_forward with W1 and W2 from blockffn_pack_weights (see blockffn.h)."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    if tuple(w_r.shape) != (E, d_h):
+        raise ValueError("w_r must be [E, d_h]")
+    if w_r.dtype != x.dtype or packed.dtype != x.dtype:
+        raise TypeError("x, w_r and packed must share a dtype")
+    code = _dtype_code(x)
+    if packed.numel() * packed.element_size() < blockffn_pack_weights_bytes(E, d_h, d_e, code):
+        raise ValueError("packed is too small for these sizes")
+    if y is None:
+        y = torch.empty_like(x)
+    if workspace is None:
+        workspace = blockffn_layer_forward_workspace(T, d_h, E, d_e, n, code, x.device)
+    args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
+            _dev(bias, "bias", torch.float32), float(eps), _dev(packed, "packed"),
+            T, d_h, E, d_e, int(n), code, _dev(y, "y", x.dtype),
+            _dev(scores, "scores", torch.float32), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    _check(lib.blockffn_layer_forward_packed(*args))
     return y
 
 

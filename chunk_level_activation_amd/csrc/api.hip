@@ -517,24 +517,28 @@ int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
                : 0;
 }
 
-blockffn_status_t blockffn_layer_forward(const void *x, const void *w_r, const float *gain,
-                                         const float *bias, float eps, const void *w1,
-                                         const void *w2, int64_t T, int64_t d_h, int64_t E,
-                                         int64_t d_e, int64_t n, int dtype, void *y, float *scores,
-                                         void *workspace, size_t workspace_bytes, void *stream)
+namespace {
+// Shared by blockffn_layer_forward (w1, w2 row-major; packed = NULL) and
+// blockffn_layer_forward_packed (w1 = w2 = NULL; packed in the tiled layout).
+blockffn_status_t layer_forward(const void *x, const void *w_r, const float *gain,
+                                const float *bias, float eps, const void *w1, const void *w2,
+                                const void *packed, int64_t T, int64_t d_h, int64_t E,
+                                int64_t d_e, int64_t n, int dtype, void *y, float *scores,
+                                void *workspace, size_t workspace_bytes, void *stream)
 {
     blockffn_status_t st = check_ffn_sizes(T, d_h, E, d_e, n, dtype);
     if (st != BLOCKFFN_OK)
         return st;
-    if (!x || !w_r || !w1 || !w2 || !y || !workspace)
-        return fail(BLOCKFFN_EINVAL, "x, w_r, w1, w2, y and workspace must not be NULL");
+    if (!x || !w_r || !(packed || (w1 && w2)) || !y || !workspace)
+        return fail(BLOCKFFN_EINVAL, packed ? "x, w_r, packed, y and workspace must not be NULL"
+                                            : "x, w_r, w1, w2, y and workspace must not be NULL");
     if (!(eps >= 0.0f))
         return fail(BLOCKFFN_EINVAL, "eps must be >= 0");
     const size_t ea = dtype == BLOCKFFN_BF16 ? 16 : 4;
-    if (!aligned(x, ea) || !aligned(w_r, ea) || !aligned(w1, ea) || !aligned(w2, ea) ||
-        !aligned(y, ea))
-        return fail(BLOCKFFN_EUNSUPPORTED, "x, w_r, w1, w2 and y must be " + std::to_string(ea) +
-                                               "-byte aligned");
+    if (!aligned(x, ea) || !aligned(w_r, ea) || (w1 && !aligned(w1, ea)) ||
+        (w2 && !aligned(w2, ea)) || (packed && !aligned(packed, ea)) || !aligned(y, ea))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x, w_r, the weights and y must be " +
+                                               std::to_string(ea) + "-byte aligned");
     if ((scores && !aligned(scores, 4)) || (gain && !aligned(gain, 4)) || (bias && !aligned(bias, 4)))
         return fail(BLOCKFFN_EUNSUPPORTED, "float arrays must be 4-byte aligned");
     if (!aligned(workspace, 256))
@@ -549,15 +553,20 @@ blockffn_status_t blockffn_layer_forward(const void *x, const void *w_r, const f
     if (p.decode && decode_grid(s, p, &xcds, &members) &&
         blockffn::layer_decode_supported(E, d_h, members)) {
         // one launch: the router computed by every workgroup from its staged x
+        const uint16_t *pw = static_cast<const uint16_t *>(packed);
         const hipError_t err = blockffn::launch_layer_bf16_decode(
             p, xcds, members, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_r),
-            gain, bias, eps, static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w2),
+            gain, bias, eps, packed ? pw : static_cast<const uint16_t *>(w1),
+            packed ? pw + E * d_e * d_h : static_cast<const uint16_t *>(w2), packed != nullptr,
             static_cast<uint16_t *>(y), scores, workspace, s);
         if (err != hipSuccess)
             return fail(BLOCKFFN_EHIP, std::string("layer launch failed: ") + hipGetErrorString(err));
         g_last_error.clear();
         return BLOCKFFN_OK;
     }
+    if (packed)
+        return fail(BLOCKFFN_EUNSUPPORTED,
+                    "packed weights need the one-launch layer (blockffn_layer_forward_fused)");
     char *base = static_cast<char *>(workspace);
     float *sc = scores ? scores : reinterpret_cast<float *>(base + L.scores);
     st = blockffn_router(x, w_r, gain, bias, eps, T, d_h, E, dtype, sc, nullptr, 1.0f, nullptr,
@@ -566,6 +575,59 @@ blockffn_status_t blockffn_layer_forward(const void *x, const void *w_r, const f
         return st;
     return blockffn_chunk_ffn(x, sc, w1, w2, T, d_h, E, d_e, n, dtype, y, workspace, L.scores,
                               nullptr, nullptr, nullptr, stream);
+}
+}  // namespace
+
+blockffn_status_t blockffn_layer_forward(const void *x, const void *w_r, const float *gain,
+                                         const float *bias, float eps, const void *w1,
+                                         const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                         int64_t d_e, int64_t n, int dtype, void *y, float *scores,
+                                         void *workspace, size_t workspace_bytes, void *stream)
+{
+    if (!w1 || !w2)
+        return fail(BLOCKFFN_EINVAL, "x, w_r, w1, w2, y and workspace must not be NULL");
+    return layer_forward(x, w_r, gain, bias, eps, w1, w2, nullptr, T, d_h, E, d_e, n, dtype, y,
+                         scores, workspace, workspace_bytes, stream);
+}
+
+size_t blockffn_pack_weights_bytes(int64_t E, int64_t d_h, int64_t d_e, int dtype)
+{
+    if (dtype != BLOCKFFN_BF16 || E < 1 || E > 256 || d_h < 32 || d_h % 32 != 0 || d_e < 32 ||
+        d_e % 32 != 0 || E * d_h * d_e > ((int64_t)1 << 30))
+        return 0;
+    return (size_t)(2 * E * d_h * d_e * 2);
+}
+
+blockffn_status_t blockffn_pack_weights(const void *w1, const void *w2, int64_t E, int64_t d_h,
+                                        int64_t d_e, int dtype, void *packed, void *stream)
+{
+    if (blockffn_pack_weights_bytes(E, d_h, d_e, dtype) == 0)
+        return fail(BLOCKFFN_EINVAL, "pack_weights: bf16 only, 1 <= E <= 256, d_h and d_e "
+                                     "positive multiples of 32, E*d_h*d_e <= 2^30");
+    if (!w1 || !w2 || !packed)
+        return fail(BLOCKFFN_EINVAL, "w1, w2 and packed must not be NULL");
+    if (!aligned(w1, 16) || !aligned(w2, 16) || !aligned(packed, 16))
+        return fail(BLOCKFFN_EUNSUPPORTED, "w1, w2 and packed must be 16-byte aligned");
+    const hipError_t err = blockffn::launch_pack_weights(
+        static_cast<const uint16_t *>(w1), static_cast<const uint16_t *>(w2), E, d_h, d_e,
+        static_cast<uint16_t *>(packed), static_cast<hipStream_t>(stream));
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("pack launch failed: ") + hipGetErrorString(err));
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
+blockffn_status_t blockffn_layer_forward_packed(const void *x, const void *w_r, const float *gain,
+                                                const float *bias, float eps, const void *packed,
+                                                int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                                int64_t n, int dtype, void *y, float *scores,
+                                                void *workspace, size_t workspace_bytes,
+                                                void *stream)
+{
+    if (!packed)
+        return fail(BLOCKFFN_EINVAL, "x, w_r, packed, y and workspace must not be NULL");
+    return layer_forward(x, w_r, gain, bias, eps, nullptr, nullptr, packed, T, d_h, E, d_e, n,
+                         dtype, y, scores, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

@@ -191,7 +191,12 @@ __device__ __forceinline__ uint32_t hid_offset(int g, int lu, int t)
 // logits back and applies bias, ReLU, RMSNorm over the E experts and the gain itself
 // (tokens past T get zero scores). The union and the score columns then come from LDS,
 // and the separate router launch and the scores' round trip through memory disappear.
-template <bool ROUTER>
+//
+// PACKED = true: W1 and W2 are in the tiled layout blockffn_pack_weights writes (each
+// matrix as 16 x 32 tiles of 1 KB, rows and columns in order), so a wave's operand
+// load of 16 rows x 32 k is one contiguous 1 KB access (two runs when a piece's rows
+// do not start on a tile) instead of 16 separate 64-byte pieces.
+template <bool ROUTER, bool PACKED>
 __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs a)
 {
     __shared__ Shared sh;
@@ -413,10 +418,17 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         const int sl = fs + (gu >= fsu ? 1 : 0);
         const int e = vr ? sh.list[sl] : 0;
         const int unit = gu - sl * a.d_e;
-        const uint32_t base = (uint32_t)(((e * a.d_e + unit) * a.d_h + kq0 + kgrp * 8) * 2);
+        // element (unit u, k) of the expert's W1: row-major, or in the tiled layout
+        // tile (u / 16, k / 32) of 16 x 32, row-major inside
+        const uint32_t base =
+            PACKED ? (uint32_t)((e * a.d_e * a.d_h + ((unit >> 4) * (a.d_h >> 5) + (kq0 >> 5)) * 512 +
+                                 (unit & 15) * 32 + kgrp * 8) *
+                                2)
+                   : (uint32_t)(((e * a.d_e + unit) * a.d_h + kq0 + kgrp * 8) * 2);
+        const uint32_t kstride = PACKED ? 1024u : 64u;
 #pragma unroll
         for (int ks = 0; ks < kMaxKSteps; ++ks)
-            wa[ks] = rh * 16 < nrows && ks < KSU ? bload<kNT>(rw1, vr ? base + ks * 64 : kOOB)
+            wa[ks] = rh * 16 < nrows && ks < KSU ? bload<kNT>(rw1, vr ? base + ks * kstride : kOOB)
                                                   : zero_bf16x8();
     }
 
@@ -437,7 +449,8 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     if (lane < kMaxDnSteps && lane < nsw) {
         const int gu = G0 + (st0 + lane) * 32;
         const int sl = gu / a.d_e;
-        sbase = sh.list[sl] * a.d_h * a.d_e + (gu - sl * a.d_e);
+        const int unit = gu - sl * a.d_e;
+        sbase = sh.list[sl] * a.d_h * a.d_e + (PACKED ? (unit >> 5) * 512 : unit);
     }
 
     // the member's score columns, zero past T
@@ -481,7 +494,10 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     // this wave is done with its W1: its share of the W2 half of the stream follows
     bf16x8 wb[kMaxDnSteps];
     {
-        const int lo = (jt * kDnCols + ct * 16 + l16) * a.d_e + kgrp * 8;
+        // element (column j, unit u) of the expert's W2: row-major, or tile (j / 16,
+        // u / 32) of the tiled layout (columns come in 16-aligned groups here)
+        const int lo = PACKED ? ((jt * 4 + ct) * (a.d_e >> 5)) * 512 + l16 * 32 + kgrp * 8
+                              : (jt * kDnCols + ct * 16 + l16) * a.d_e + kgrp * 8;
 #pragma unroll
         for (int i = 0; i < kMaxDnSteps; ++i)
             wb[i] = has_dn && i < nsw
@@ -619,7 +635,41 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     }
 }
 
+// The tiled weight layout: a row-major R x C bf16 matrix as (R/16) x (C/32) tiles of
+// 16 rows x 32 columns, tiles in row-major order, each tile row-major (1 KB). Thread
+// -> one 16-byte piece of the output (8 columns of one tile row); the source piece is
+// contiguous too. E matrices per launch, R % 16 == 0, C % 32 == 0.
+__global__ void __launch_bounds__(256) pack_tiles_kernel(const uint16_t *__restrict__ src,
+                                                          uint16_t *__restrict__ dst,
+                                                          int64_t pieces, int R, int C)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (q >= pieces)
+        return;
+    const int64_t per = (int64_t)R * C / 8;           // pieces per matrix
+    const int64_t m = q / per;
+    const int r8 = (int)(q - m * per);                // piece within the matrix
+    const int tile = r8 >> 6, in = r8 & 63;           // 64 pieces per 16 x 32 tile
+    const int tr = tile / (C >> 5), tc = tile - tr * (C >> 5);
+    const int row = tr * 16 + (in >> 2), col = tc * 32 + (in & 3) * 8;
+    const uint16_t *s = src + m * R * C + (int64_t)row * C + col;
+    uint16_t *d = dst + m * R * C + (int64_t)r8 * 8;
+    *reinterpret_cast<u32x4 *>(d) = *reinterpret_cast<const u32x4 *>(s);
+}
+
 }  // namespace
+
+hipError_t launch_pack_weights(const uint16_t *w1, const uint16_t *w2, int64_t E, int64_t d_h,
+                               int64_t d_e, uint16_t *packed, hipStream_t stream)
+{
+    const int64_t pieces = E * d_e * d_h / 8;
+    const unsigned blocks = (unsigned)((pieces + 255) / 256);
+    hipLaunchKernelGGL(pack_tiles_kernel, dim3(blocks), dim3(256), 0, stream, w1, packed, pieces,
+                       (int)d_e, (int)d_h);
+    hipLaunchKernelGGL(pack_tiles_kernel, dim3(blocks), dim3(256), 0, stream, w2,
+                       packed + E * d_e * d_h, pieces, (int)d_h, (int)d_e);
+    return hipGetLastError();
+}
 
 bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds, int members)
 {
@@ -648,12 +698,16 @@ size_t decode_scratch_bytes(int64_t d_h, int64_t d_e)
 int decode_blocks_per_cu()
 {
     int nb = 0, nr = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ffn_bf16_decode_kernel<false>, kThreads, 0) !=
-            hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nr, ffn_bf16_decode_kernel<true>, kThreads, 0) !=
-            hipSuccess)
+    int np = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ffn_bf16_decode_kernel<false, false>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nr, ffn_bf16_decode_kernel<true, false>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&np, ffn_bf16_decode_kernel<true, true>,
+                                                     kThreads, 0) != hipSuccess)
         return 0;
-    return nb < nr ? nb : nr;
+    const int m = nb < nr ? nb : nr;
+    return m < np ? m : np;
 }
 
 bool layer_decode_supported(int64_t E, int64_t d_h, int members)
@@ -703,7 +757,7 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
     a.masks_out = masks_out;
     a.lists_out = lists_out;
     a.counts_out = counts_out;
-    hipLaunchKernelGGL(ffn_bf16_decode_kernel<false>, dim3((unsigned)(xcds * members)),
+    hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false>), dim3((unsigned)(xcds * members)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -711,7 +765,8 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
 hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, const uint16_t *x,
                                     const uint16_t *w_r, const float *gain, const float *bias,
                                     float eps, const uint16_t *w1, const uint16_t *w2,
-                                    uint16_t *y, float *scores_out, void *ws, hipStream_t stream)
+                                    bool packed, uint16_t *y, float *scores_out, void *ws,
+                                    hipStream_t stream)
 {
     DecodeArgs a = decode_args(p, xcds, members, x, w1, w2, y, ws);
     a.w_r = w_r;
@@ -719,8 +774,12 @@ hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, con
     a.bias = bias;
     a.eps = eps;
     a.scores_out = scores_out;
-    hipLaunchKernelGGL(ffn_bf16_decode_kernel<true>, dim3((unsigned)(xcds * members)),
-                       dim3(kThreads), 0, stream, a);
+    if (packed)
+        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, true>), dim3((unsigned)(xcds * members)),
+                           dim3(kThreads), 0, stream, a);
+    else
+        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, false>), dim3((unsigned)(xcds * members)),
+                           dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
 

@@ -118,13 +118,19 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
                                   uint16_t *y, void *ws, uint64_t *masks_out,
                                   int32_t *lists_out, int32_t *counts_out, hipStream_t stream);
 // The same schedule with the router computed inside the launch (E <= 64 and at most
-// two experts per member, d_h % 64 == 0, on top of the decode sizes); scores_out [T][E]
-// is written when given.
+// two experts per member, d_h % 256 == 0 and <= 2048, on top of the decode sizes);
+// scores_out [T][E] is written when given. packed: w1 and w2 are in the tiled layout
+// of launch_pack_weights.
 bool layer_decode_supported(int64_t E, int64_t d_h, int members);
 hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, const uint16_t *x,
                                     const uint16_t *w_r, const float *gain, const float *bias,
                                     float eps, const uint16_t *w1, const uint16_t *w2,
-                                    uint16_t *y, float *scores_out, void *ws, hipStream_t stream);
+                                    bool packed, uint16_t *y, float *scores_out, void *ws,
+                                    hipStream_t stream);
+// W1 [E][d_e][d_h] and W2 [E][d_h][d_e] (bf16) into packed = [W1 tiles][W2 tiles], each
+// matrix as 16 x 32 tiles of 1 KB in row-major tile order, row-major inside a tile.
+hipError_t launch_pack_weights(const uint16_t *w1, const uint16_t *w2, int64_t E, int64_t d_h,
+                               int64_t d_e, uint16_t *packed, hipStream_t stream);
 // Four launches: union, per-expert tile lists, expert-grouped up-projection,
 // tile-pair x column-tile down-projection.
 hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const float *scores,

@@ -178,6 +178,40 @@ int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
                                  int dtype, void *stream);
 
 /*
+ * Bytes of a packed copy of the expert weights (2*E*d_h*d_e bf16 elements), or 0 when
+ * the sizes or dtype are not supported (bf16 only; 1 <= E <= 256; d_h and d_e positive
+ * multiples of 32; E*d_h*d_e <= 2^30).
+ */
+size_t blockffn_pack_weights_bytes(int64_t E, int64_t d_h, int64_t d_e, int dtype);
+
+/*
+ * Rewrites W1 [E, d_e, d_h] and W2 [E, d_h, d_e] (bf16, row-major, the experts of the
+ * skill page's "Architecture Overview") into packed (caller-owned device memory of
+ * blockffn_pack_weights_bytes(...) bytes, 16-byte aligned): W1's tiles, then W2's.
+ * Every matrix is cut into tiles of 16 rows x 32 columns (1 KB), stored in row-major
+ * tile order, each tile row-major. The values are copied exactly. This is a one-time
+ * layout change for weights that stay resident: it lets the one-launch layer read each
+ * 16 x 32 operand fragment as one contiguous access. Asynchronous on stream;
+ * BLOCKFFN_EINVAL for unsupported sizes or NULL pointers.
+ */
+blockffn_status_t blockffn_pack_weights(const void *w1, const void *w2, int64_t E, int64_t d_h,
+                                        int64_t d_e, int dtype, void *packed, void *stream);
+
+/*
+ * blockffn_layer_forward with the expert weights given as blockffn_pack_weights wrote
+ * them (same values, same result bits as the call with row-major W1 and W2). Only for
+ * sizes where blockffn_layer_forward_fused(...) is 1; otherwise BLOCKFFN_EUNSUPPORTED
+ * and nothing is enqueued. Other arguments, workspace and errors as in
+ * blockffn_layer_forward.
+ */
+blockffn_status_t blockffn_layer_forward_packed(const void *x, const void *w_r, const float *gain,
+                                                const float *bias, float eps, const void *packed,
+                                                int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                                int64_t n, int dtype, void *y, float *scores,
+                                                void *workspace, size_t workspace_bytes,
+                                                void *stream);
+
+/*
  * Residual + LayerNorm of the layer output (skill page, "Full BlockFFN Layer with
  * Combined Losses": the layer returns nn.LayerNorm(d_h) of the expert output plus
  * the layer input):

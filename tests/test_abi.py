@@ -227,3 +227,54 @@ def test_layer_backward_workspace_query(lib):
     assert f(2048, 2048, 64, 128, 32, 0) == 0      # bf16 only
     assert f(2048, 2048, 64, 64, 32, 1) == 0       # d_e % 128
     assert f(0, 2048, 64, 128, 32, 1) == 0
+
+
+def layer(lib, x=FAKE, w_r=FAKE, gain=None, bias=None, eps=1e-6, w1=FAKE, w2=FAKE, T=32,
+          d_h=2048, E=64, d_e=128, n=32, dtype=1, y=FAKE, scores=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.blockffn_layer_forward(x, w_r, gain, bias, eps, w1, w2, T, d_h, E, d_e, n, dtype,
+                                      y, scores, ws, ws_bytes, None)
+
+
+def layer_packed(lib, x=FAKE, w_r=FAKE, gain=None, bias=None, eps=1e-6, packed=FAKE, T=32,
+                 d_h=2048, E=64, d_e=128, n=32, dtype=1, y=FAKE, scores=None, ws=FAKE,
+                 ws_bytes=1 << 40):
+    return lib.blockffn_layer_forward_packed(x, w_r, gain, bias, eps, packed, T, d_h, E, d_e, n,
+                                             dtype, y, scores, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(w_r=None), 1), (dict(w1=None), 1), (dict(w2=None), 1),
+    (dict(y=None), 1), (dict(ws=None), 1), (dict(T=0), 1), (dict(n=0), 1), (dict(dtype=9), 1),
+    (dict(eps=-1.0), 1), (dict(E=257), 2), (dict(x=FAKE_ODD), 2), (dict(w_r=FAKE + 8), 2),
+    (dict(ws=FAKE + 16), 2), (dict(ws_bytes=1000), 3),
+])
+def test_layer_forward_rejects(lib, kw, status):
+    assert layer(lib, **kw) == status
+    assert bf.blockffn_last_error() != ""
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(packed=None), 1), (dict(x=None), 1), (dict(y=None), 1), (dict(T=0), 1),
+    (dict(packed=FAKE_ODD), 2), (dict(ws_bytes=1000), 3),
+    # sizes the one-launch layer never takes (E > 64, several chunks): nothing runs
+    (dict(E=128), 2), (dict(T=256), 2),
+])
+def test_layer_forward_packed_rejects(lib, kw, status):
+    assert layer_packed(lib, **kw) == status
+    assert bf.blockffn_last_error() != ""
+
+
+def test_pack_weights_query_and_rejects(lib):
+    f = lib.blockffn_pack_weights_bytes
+    assert f(64, 2048, 128, 1) == 2 * 64 * 2048 * 128 * 2
+    assert f(64, 2048, 128, 0) == 0            # bf16 only
+    assert f(64, 2048, 100, 1) == 0            # d_e % 32
+    assert f(64, 2050, 128, 1) == 0            # d_h % 32
+    assert f(0, 2048, 128, 1) == 0
+    assert f(300, 2048, 128, 1) == 0
+    p = lib.blockffn_pack_weights
+    assert p(FAKE, FAKE, 64, 2048, 128, 0, FAKE, None) == 1
+    assert p(None, FAKE, 64, 2048, 128, 1, FAKE, None) == 1
+    assert p(FAKE, FAKE, 64, 2048, 128, 1, None, None) == 1
+    assert p(FAKE, FAKE_ODD, 64, 2048, 128, 1, FAKE, None) == 2
+    assert bf.blockffn_last_error() != ""

@@ -106,3 +106,52 @@ def test_layer_forward_deterministic_and_graph_replays():
         torch.cuda.synchronize()
         for y, ref in zip(ys, eager):
             assert np.array_equal(host(y), ref), rep
+
+
+# ---------------------------------------------------------------- packed weights
+
+def _tiles(m):
+    """numpy reference of the tiled layout: [..., R, C] -> [..., R/16, C/32, 16, 32], flat."""
+    *lead, R, C = m.shape
+    t = m.reshape(*lead, R // 16, 16, C // 32, 32)
+    t = np.swapaxes(t, -3, -2)
+    return t.reshape(-1)
+
+
+@pytest.mark.parametrize("E,d_h,d_e", [(64, 2048, 128), (3, 96, 64), (1, 32, 32)])
+def test_pack_weights_layout(E, d_h, d_e):
+    rng = np.random.default_rng(40 + E)
+    w1 = (rng.standard_normal((E, d_e, d_h)) * 8).astype(np.float32)
+    w2 = (rng.standard_normal((E, d_h, d_e)) * 8).astype(np.float32)
+    w1_16, w2_16 = dev(w1, b16), dev(w2, b16)
+    packed = bf.blockffn_pack_weights(w1_16, w2_16)
+    torch.cuda.synchronize()
+    got = packed.view(torch.int16).cpu().numpy()
+    ref = np.concatenate([_tiles(w1_16.view(torch.int16).cpu().numpy()),
+                          _tiles(w2_16.view(torch.int16).cpu().numpy())])
+    assert np.array_equal(got, ref)
+
+
+@pytest.mark.parametrize("idx", range(7), ids=[c[0] for c in CASES[:7]])
+def test_layer_forward_packed(idx):
+    """Packed weights: the same bits as row-major weights, and the oracle's bar."""
+    label, seed, T, d_h, E, d_e, n, gain, bias = CASES[idx]
+    inp, g, b = _draw(seed, T, d_h, E, d_e, n, gain, bias)
+    y_ref, s_ref = _run(inp, g, b, n)
+    w1, w2 = dev(inp.w1, b16), dev(inp.w2, b16)
+    packed = bf.blockffn_pack_weights(w1, w2)
+    sc = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    y = bf.blockffn_layer_forward_packed(dev(inp.x, b16), dev(inp.w_r, b16), packed, E, d_e, n,
+                                         gain=None if g is None else dev(g),
+                                         bias=None if b is None else dev(b), scores=sc)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(y), y_ref)
+    assert np.array_equal(sc.cpu().numpy(), s_ref)
+    _check(inp, g, b, n, host(y), sc.cpu().numpy())
+
+
+def test_layer_forward_packed_rejects_unfused_sizes():
+    inp, g, b = _draw(7, 32, 2048, 128, 128, 32)
+    packed = bf.blockffn_pack_weights(dev(inp.w1, b16), dev(inp.w2, b16))
+    with pytest.raises(bf.BlockFFNError):
+        bf.blockffn_layer_forward_packed(dev(inp.x, b16), dev(inp.w_r, b16), packed, 128, 128, 32)
