@@ -70,6 +70,16 @@ __device__ __forceinline__ float dpp_f32(float v)
     return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL,
                                                               0xf, 0xf, false));
 }
+// Sum over each 16-lane row of the wave, returned in every lane of the row (the same
+// bits in all of them: every step adds two values in either order).
+__device__ __forceinline__ float row16_sum_f32(float v)
+{
+    v += dpp_f32<0xb1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_f32<0x4e>(v);    // quad_perm [2,3,0,1]
+    v += dpp_f32<0x141>(v);   // row_half_mirror
+    v += dpp_f32<0x140>(v);   // row_mirror
+    return v;
+}
 __device__ __forceinline__ float wave_sum_f32(float v)
 {
     v += dpp_f32<0xb1>(v);    // quad_perm [1,0,3,2]

@@ -110,6 +110,7 @@ struct Shared {
     // [2 step halves][64 columns][32 tokens]
     alignas(16) float red[2 * kDnCols * kRedPitch];
     alignas(16) uint16_t xs[kTileM * kMaxDh];   // x, 16-byte chunk c of token t at chunk c ^ (t & 15)
+    alignas(16) uint16_t wr[2 * kMaxDh];        // the member's (at most 2) W_r rows (router)
 };
 
 // Union of the experts active in the chunk, ascending list in LDS; returns |U| and
@@ -253,14 +254,12 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         const int EPM = (a.E + a.P - 1) / a.P;
         const int e0 = k * EPM;
         const int KS8 = a.d_h / 256;              // 32-wide k steps per eighth (<= 8)
-        bf16x8 wrv[8];
+        // the member's W_r rows, contiguous: thread -> one 16-byte chunk of the (at most
+        // 2) rows, rows past E read zero; staged in LDS with x
+        bf16x8 wrc;
         {
             const __amdgpu_buffer_rsrc_t rwr = make_rsrc(a.w_r, (uint64_t)a.E * a.d_h * 2);
-            const bool vr = l16 < EPM && e0 + l16 < a.E;
-            const uint32_t base = (uint32_t)(((e0 + l16) * a.d_h + wave * (a.d_h / 8) + kgrp * 8) * 2);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                wrv[j] = bload<0>(rwr, vr && j < KS8 ? base + j * 64 : kOOB);
+            wrc = bload<0>(rwr, tid < EPM * cpr ? (uint32_t)((e0 * a.d_h + tid * 8) * 2) : kOOB);
         }
         // this thread's epilogue entries: token tt, experts sub + 16 i
         const int tt = tid >> 4, sub = tid & 15;
@@ -278,6 +277,8 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                 const int q = i * kThreads + tid;
                 *reinterpret_cast<bf16x8 *>(&sh.xs[xs_chunk(q / cpr, q % cpr, cpr) * 8]) = xv[i];
             }
+        if (tid < 2 * cpr)
+            *reinterpret_cast<bf16x8 *>(&sh.wr[tid * 8]) = wrc;
         __syncthreads();
         float *part = sh.red;                     // [8 k eighths][2 experts][32 tokens]
         {
@@ -288,8 +289,11 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                     const int c = (wave * (a.d_h / 8) + j * 32) / 8 + kgrp;
                     const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
                     const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wrv[j], b0, acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wrv[j], b1, acc1, 0, 0, 0);
+                    // A: rows 0 and 1 of the 16-row block are the member's W_r rows
+                    const bf16x8 wa_r = l16 < 2 ? *reinterpret_cast<const bf16x8 *>(&sh.wr[l16 * a.d_h + c * 8])
+                                                : zero_bf16x8();
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa_r, b0, acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa_r, b1, acc1, 0, 0, 0);
                 }
             // element i: row (expert) kgrp*4 + i, token l16 (+16); rows 0 and 1 are kept
             if (kgrp == 0) {
@@ -355,10 +359,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                 rv[i] = (e < a.E && l > 0.0f) ? l : 0.0f;
                 sumsq = fmaf(rv[i], rv[i], sumsq);
             }
-            sumsq += __shfl_xor(sumsq, 1);
-            sumsq += __shfl_xor(sumsq, 2);
-            sumsq += __shfl_xor(sumsq, 4);
-            sumsq += __shfl_xor(sumsq, 8);
+            sumsq = row16_sum_f32(sumsq);     // the 16 threads of token tt
             const float inv = 1.0f / sqrtf(sumsq / (float)a.E + a.eps);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -396,11 +397,11 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     // The N = |U| * d_e hidden units of the union (slot-major) are split evenly: group
     // g takes the 32-unit-aligned range [G0, G1), member k of it the even-sized piece
     // [M0, M0 + nrows). A member's piece spans at most 2 slots (nrows <= 32 <= d_e).
-    const int nblk = cnt * (a.d_e / 32);
-    const int G0 = 32 * (int)((int64_t)g * nblk / a.X);
-    const int ng = 32 * (int)((int64_t)(g + 1) * nblk / a.X) - G0;
-    const int M0 = G0 + 2 * (int)((int64_t)k * (ng / 2) / a.P);
-    const int nrows = G0 + 2 * (int)((int64_t)(k + 1) * (ng / 2) / a.P) - M0;
+    const int nblk = cnt * (a.d_e / 32);     // <= 1024 blocks: 32-bit products suffice
+    const int G0 = 32 * (g * nblk / a.X);
+    const int ng = 32 * ((g + 1) * nblk / a.X) - G0;
+    const int M0 = G0 + 2 * (k * (ng / 2) / a.P);
+    const int nrows = G0 + 2 * ((k + 1) * (ng / 2) / a.P) - M0;
     const int fs = M0 / a.d_e;              // the member's first slot
     const int fsu = (fs + 1) * a.d_e;       // first unit of the next slot
 
