@@ -99,7 +99,7 @@ struct DecodeArgs {
 };
 
 struct Shared {
-    uint64_t wmask[kWaves][kMaxWords];
+    alignas(16) uint64_t wmask[kMaxWords][kWaves];   // per-wave union bits, word-major
     int list[256];
     int flag;
     int rflag;
@@ -132,15 +132,22 @@ __device__ int union_of_tile(const DecodeArgs &a, Shared &sh, const float (&sv)[
         wm[i / 4] |= m16 << (16 * (i % 4));
     }
     if (lane < kMaxWords)
-        sh.wmask[wave][lane] = wm[lane];
+        sh.wmask[lane][wave] = wm[lane];
     __syncthreads();
+    // word w of the 8 waves: 64 contiguous bytes, four 16-byte reads
+    const int W = (a.E + 63) >> 6;
     int cnt = 0;
 #pragma unroll
     for (int w = 0; w < kMaxWords; ++w) {
         uint64_t m = 0;
+        if (w < W) {
+            typedef unsigned long long u64x2 __attribute__((ext_vector_type(2)));
 #pragma unroll
-        for (int v = 0; v < kWaves; ++v)
-            m |= sh.wmask[v][w];
+            for (int v = 0; v < kWaves; v += 2) {
+                const u64x2 p = *reinterpret_cast<const u64x2 *>(&sh.wmask[w][v]);
+                m |= p[0] | p[1];
+            }
+        }
         wm[w] = m;
         cnt += __popcll(m);
     }
