@@ -45,8 +45,6 @@ namespace blockffn {
 namespace {
 
 constexpr int kBT = 256;                  // threads per workgroup, 4 waves
-constexpr int kBK = 32;                   // k per staged step
-constexpr int kLP = kBK + 8;              // LDS pitch (bf16) of a [row][k] tile: 80 bytes
 constexpr int kTM = 128;                  // 128 x 128 output tiles
 constexpr int kXN = 256;                  // dx columns per workgroup
 constexpr int kPassTiles = 4;             // chunk tiles per expert-pass workgroup
@@ -108,6 +106,47 @@ __device__ __forceinline__ void mma_64x64(const uint16_t *As, const uint16_t *Bs
 __device__ __forceinline__ u32x4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+}
+
+// The k loop of a 128 x 128 output tile, k in steps of kPK = 64, with kDepth steps in
+// flight: the operands of step s + kDepth are requested while step s is multiplied, so
+// the memory latency is covered by kDepth steps of products instead of one. load(s,
+// ra, rb) fills this thread's four 16-byte pieces of A and of B of step s (piece i:
+// row (tid + 256 i) / 8, k (tid % 8) * 8 of the [128][64] tiles) and must read zeros
+// (out-of-range offsets) for s >= steps: the loop runs a multiple of kDepth steps so
+// that every thread always has the same loads in flight.
+constexpr int kPK = 64;
+constexpr int kPKP = kPK + 8;             // LDS pitch of the [row][k] tiles: 144 bytes
+// The weight-gradient kernel keeps k = one tile's 32 tokens per step with one step of
+// prefetch: its grid (E x 2 x 128-square tiles) already gives each CU several
+// workgroups, and the deeper loop's registers would cost that occupancy.
+constexpr int kWBK = 32;
+constexpr int kWLP = kWBK + 8;
+constexpr int kDepth = 3;
+template <typename Load>
+__device__ __forceinline__ void kloop_128x128(Load load, int steps, uint16_t *As, uint16_t *Bs,
+                                              f32x16 (&acc)[2][2], int tid, int wm, int wn,
+                                              int lane)
+{
+    u32x4 ra[kDepth][4], rb[kDepth][4];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+        load(d, ra[d], rb[d]);
+    for (int s0 = 0; s0 < steps; s0 += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int q = tid + i * kBT;
+                *reinterpret_cast<u32x4 *>(&As[(q >> 3) * kPKP + (q & 7) * 8]) = ra[d][i];
+                *reinterpret_cast<u32x4 *>(&Bs[(q >> 3) * kPKP + (q & 7) * 8]) = rb[d][i];
+            }
+            __syncthreads();
+            load(s0 + d + kDepth, ra[d], rb[d]);
+            mma_64x64<kPK>(As, Bs, acc, wm, wn, lane);
+            __syncthreads();
+        }
+    }
 }
 
 // ------------------------------------------------------------------ 1. tile transposes
@@ -178,8 +217,7 @@ struct PassArgs {
     Dims d;
 };
 
-constexpr int kPK = 64;                   // expert pass: k per staged step
-constexpr int kPP = kPK + 8;              // its LDS pitch (bf16): 144 bytes
+constexpr int kPP = kPKP;                 // the expert pass's LDS pitch (same k step)
 
 __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
 {
@@ -341,7 +379,7 @@ __global__ void __launch_bounds__(kBT, 2) wgrad_kernel(WgradArgs a)
     const int M = kind == 0 ? d.d_e : d.d_h, N = kind == 0 ? d.d_h : d.d_e;
     const int MT = M / kTM;
     const int mt = t2 % MT, nt = t2 / MT;
-    __shared__ alignas(16) uint16_t As[kTM * kLP], Bs[kTM * kLP];
+    __shared__ alignas(16) uint16_t As[kTM * kWLP], Bs[kTM * kWLP];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave & 1, wn = wave >> 1;
     const int cnt = a.tile_count[e];
@@ -387,13 +425,13 @@ __global__ void __launch_bounds__(kBT, 2) wgrad_kernel(WgradArgs a)
     for (int s = 0; s < cnt; ++s) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4 *>(&As[srow[i] * kLP + skv[i]]) = ra[i];
-            *reinterpret_cast<u32x4 *>(&Bs[srow[i] * kLP + skv[i]]) = rb[i];
+            *reinterpret_cast<u32x4 *>(&As[srow[i] * kWLP + skv[i]]) = ra[i];
+            *reinterpret_cast<u32x4 *>(&Bs[srow[i] * kWLP + skv[i]]) = rb[i];
         }
         __syncthreads();
         if (s + 1 < cnt)
             load_step(s + 1);
-        mma_64x64<kBK>(As, Bs, acc, wm, wn, lane);
+        mma_64x64<kWBK>(As, Bs, acc, wm, wn, lane);
         __syncthreads();
     }
     float *out = kind == 0 ? a.dw1 + (int64_t)e * d.d_e * d.d_h : a.dw2 + (int64_t)e * d.d_h * d.d_e;
@@ -430,7 +468,7 @@ __global__ void __launch_bounds__(kBT, 2) dx_kernel(DxArgs a)
 {
     const Dims &d = a.d;
     const int tg = blockIdx.x, nb = blockIdx.y * kTM, z = blockIdx.z;
-    __shared__ alignas(16) uint16_t As[kTM * kLP], Bs[kTM * kLP];
+    __shared__ alignas(16) uint16_t As[kTM * kPKP], Bs[kTM * kPKP];
     __shared__ uint64_t um[kXTiles][4];     // union masks of the 4 tiles' chunks
     __shared__ int elist[256];
     __shared__ int ecount;
@@ -455,49 +493,34 @@ __global__ void __launch_bounds__(kBT, 2) dx_kernel(DxArgs a)
     const int e_lo = (int)((int64_t)z * ne / a.splits), e_hi = (int)((int64_t)(z + 1) * ne / a.splits);
     const __amdgpu_buffer_rsrc_t rda = make_rsrc(a.da_tu, (uint64_t)d.CT * d.E * kTileM * d.d_e * 2);
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(a.w1t, (uint64_t)d.E * d.d_e * d.d_h * 2);
-    int srow[2], skv[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = tid + i * kBT;
-        srow[i] = q >> 2;
-        skv[i] = (q & 3) * 8;
-    }
     f32x16 acc[2][2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
             zero_acc(acc[i][j]);
-    const int US = d.d_e / kBK;
+    const int US = d.d_e / kPK;
     const int steps = (e_hi - e_lo) * US;
-    u32x4 ra[2], rb[2];
-    auto load_step = [&](int s) {
-        const int e = elist[e_lo + s / US];
-        const int u0 = (s % US) * kBK;
+    auto load = [&](int st, u32x4 (&ra)[4], u32x4 (&rb)[4]) {
+        // no branch here, so the compiler keeps every step's loads in flight: the list
+        // is read at a valid position even past the last step (masked to an expert
+        // index; such steps read zeros)
+        const uint32_t vmask = 0u - (uint32_t)(st < steps);   // all ones on a real step
+        const int e = elist[e_lo + (st < steps ? st / US : 0)] & 255;
+        const int u0 = (st % US) * kPK;
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = srow[i] / kTileM, tile = tg * kXTiles + q;
-            const bool use = tile < d.CT && ((um[q][e >> 6] >> (e & 63)) & 1ull);
-            ra[i] = load16(rda, use ? (uint32_t)(((((int64_t)tile * d.E + e) * kTileM + srow[i] % kTileM) * d.d_e +
-                                                  u0 + skv[i]) * 2)
-                                    : kOOB);
-            rb[i] = load16(rw1, (uint32_t)((((int64_t)e * d.d_h + nb + srow[i]) * d.d_e + u0 + skv[i]) * 2));
+        for (int i = 0; i < 4; ++i) {
+            const int q = tid + i * kBT, row = q >> 3, kk = (q & 7) * 8;
+            const int qt = row / kTileM, tile = tg * kXTiles + qt;
+            const uint64_t word = um[qt][e >> 6];               // (qt < 4 always)
+            const uint32_t umask = vmask & (0u - (uint32_t)((tile < d.CT) & (int)((word >> (e & 63)) & 1ull)));
+            const uint32_t ao = (uint32_t)(((((int64_t)tile * d.E + e) * kTileM + row % kTileM) * d.d_e + u0 + kk) * 2);
+            const uint32_t bo = (uint32_t)((((int64_t)e * d.d_h + nb + row) * d.d_e + u0 + kk) * 2);
+            ra[i] = load16(rda, (ao & umask) | (kOOB & ~umask));
+            rb[i] = load16(rw1, (bo & vmask) | (kOOB & ~vmask));
         }
     };
-    if (steps > 0)
-        load_step(0);
-    for (int s = 0; s < steps; ++s) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            *reinterpret_cast<u32x4 *>(&As[srow[i] * kLP + skv[i]]) = ra[i];
-            *reinterpret_cast<u32x4 *>(&Bs[srow[i] * kLP + skv[i]]) = rb[i];
-        }
-        __syncthreads();
-        if (s + 1 < steps)
-            load_step(s + 1);
-        mma_64x64<kBK>(As, Bs, acc, wm, wn, lane);
-        __syncthreads();
-    }
+    kloop_128x128(load, steps, As, Bs, acc, tid, wm, wn, lane);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
