@@ -15,8 +15,9 @@
 //   3. up_grouped_kernel: workgroup = (expert e, 4 of e's tiles): a 128 x d_e x d_h
 //      GEMM (x rows gathered, W1_e read once per workgroup and shared through the
 //      XCD's L2 by the workgroups of the same expert, which the grid places on one
-//      XCD), double-buffered through LDS, 32x32x16 bf16 MFMA, then Swish and the
-//      score; the bf16 hidden rows go to Ht[tile][e].
+//      XCD), double-buffered through LDS with kDepth k steps of loads in flight,
+//      32x32x16 bf16 MFMA, then Swish and the score; the bf16 hidden rows go to
+//      Ht[tile][e].
 //   4. down_grouped_kernel: workgroup = (2 chunk tiles, 256 output columns): a
 //      64 x 256 GEMM over k = the union of the two chunks' experts x d_e, ascending,
 //      with the hidden rows of a tile whose chunk does not use the expert read as
@@ -41,7 +42,9 @@ constexpr int kDnTiles = 2;               // chunk tiles per down workgroup
 constexpr int kDnRows = kDnTiles * kTileM;    // 64
 constexpr int kDnCols = 256;              // output columns per down workgroup
 constexpr int kMaxWords = 4;
-constexpr int kDepth = 4;                 // down: k steps whose loads are in flight ahead of use
+constexpr int kDepth = 4;                 // k steps whose loads are in flight ahead of use
+constexpr int kUpDepth = 2;               // up: the same, in 32 registers, so two workgroups fit a CU
+static_assert(kDepth % 2 == 0 && kUpDepth % 2 == 0, "the LDS double buffer alternates with the ring slot");
 // A buffer offset beyond every range used here: the load returns zero, no memory access.
 constexpr uint32_t kOutOfRange = 0x80000000u;
 
@@ -109,15 +112,15 @@ __global__ void __launch_bounds__(256) expert_tiles_kernel(GroupedArgs a)
 }
 
 // ------------------------------------------------------------------ up (grouped GEMM)
-__global__ void __launch_bounds__(kGThreads, 2) up_grouped_kernel(GroupedArgs a)
+__global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 {
     const int e = blockIdx.x % a.E;
     const int b = blockIdx.x / a.E;
     const int cnt = a.tile_count[e];
     if (b * kUpTiles >= cnt)
         return;
-    __shared__ uint16_t As[2][kUpRows * kPitch];   // x rows x 64 k
-    __shared__ uint16_t Bs[2][kUpCols * kPitch];   // W1 rows (hidden units) x 64 k
+    __shared__ alignas(16) uint16_t As[2][kUpRows * kPitch];   // x rows x 64 k
+    __shared__ alignas(16) uint16_t Bs[2][kUpCols * kPitch];   // W1 rows (hidden units) x 64 k
     __shared__ int64_t tok[kUpRows];
     __shared__ int tiles[kUpTiles];
 
@@ -159,37 +162,49 @@ __global__ void __launch_bounds__(kGThreads, 2) up_grouped_kernel(GroupedArgs a)
 #pragma unroll
             for (int v = 0; v < 16; ++v)
                 acc[j][v] = 0.0f;
-        bf16x8 ra[2], rb[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            ra[i] = av[i] ? bload<0>(rx, aoff[i]) : zero_bf16x8();
-            rb[i] = bload<0>(rw1, boff[i]);
-        }
-        for (int s = 0; s < KS; ++s) {
-            const int buf = s & 1;
+        // kUpDepth k steps of loads in flight, every load issued: rows without a token,
+        // and steps past KS, read zeros
+        bf16x8 ra[kUpDepth][2], rb[kUpDepth][2];
+        auto issue = [&](int st, int d) {
+            const uint32_t okm = 0u - (uint32_t)(st < KS);
+            const uint32_t kb = (uint32_t)(st * kKStep * 2);
 #pragma unroll
             for (int i = 0; i < 2; ++i) {
-                *reinterpret_cast<bf16x8 *>(&As[buf][lrow[i] * kPitch + lcol[i]]) = ra[i];
-                *reinterpret_cast<bf16x8 *>(&Bs[buf][lrow[i] * kPitch + lcol[i]]) = rb[i];
+                const uint32_t am = okm & (0u - (uint32_t)av[i]);
+                ra[d][i] = bload<0>(rx, ((aoff[i] + kb) & am) | (kOutOfRange & ~am));
+                rb[d][i] = bload<0>(rw1, ((boff[i] + kb) & okm) | (kOutOfRange & ~okm));
             }
-            __syncthreads();
-            if (s + 1 < KS) {
-                const uint32_t kb = (uint32_t)((s + 1) * kKStep * 2);
+        };
+        // issued in ring order (the scheduling barriers keep it) so that the wait before
+        // a slot's LDS store counts only the younger slots' loads
+#pragma unroll
+        for (int d = 0; d < kUpDepth; ++d) {
+            issue(d, d);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // whole turns of the ring: the steps past KS add zeros, and the loop has no exit
+        // that would leave the wait counts unknown
+        for (int s0 = 0; s0 < KS; s0 += kUpDepth) {
+#pragma unroll
+            for (int d = 0; d < kUpDepth; ++d) {
+                const int buf = d & 1;
 #pragma unroll
                 for (int i = 0; i < 2; ++i) {
-                    ra[i] = av[i] ? bload<0>(rx, aoff[i] + kb) : zero_bf16x8();
-                    rb[i] = bload<0>(rw1, boff[i] + kb);
+                    *reinterpret_cast<bf16x8 *>(&As[buf][lrow[i] * kPitch + lcol[i]]) = ra[d][i];
+                    *reinterpret_cast<bf16x8 *>(&Bs[buf][lrow[i] * kPitch + lcol[i]]) = rb[d][i];
                 }
-            }
+                __syncthreads();
+                issue(s0 + d + kUpDepth, d);
 #pragma unroll
-            for (int ks = 0; ks < kKStep / 16; ++ks) {
-                const bf16x8 fa =
-                    *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * 32 + col) * kPitch + ks * 16 + kg * 8]);
+                for (int ks = 0; ks < kKStep / 16; ++ks) {
+                    const bf16x8 fa =
+                        *reinterpret_cast<const bf16x8 *>(&As[buf][(wm * 32 + col) * kPitch + ks * 16 + kg * 8]);
 #pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
-                        &Bs[buf][(wn * 64 + j * 32 + col) * kPitch + ks * 16 + kg * 8]);
-                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
+                    for (int j = 0; j < 2; ++j) {
+                        const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
+                            &Bs[buf][(wn * 64 + j * 32 + col) * kPitch + ks * 16 + kg * 8]);
+                        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
+                    }
                 }
             }
         }
@@ -219,8 +234,8 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     const int NCT = a.d_h / kDnCols;
     const int ct = blockIdx.x % NCT;
     const int bt = blockIdx.x / NCT;
-    __shared__ uint16_t As[2][kDnRows * kPitch];   // hidden rows x 64 units
-    __shared__ uint16_t Bs[2][kDnCols * kPitch];   // W2 rows (output columns) x 64 units
+    __shared__ alignas(16) uint16_t As[2][kDnRows * kPitch];   // hidden rows x 64 units
+    __shared__ alignas(16) uint16_t Bs[2][kDnCols * kPitch];   // W2 rows (output columns) x 64 units
     __shared__ uint64_t m_tile[kDnTiles][kMaxWords];
     __shared__ int list[256];
     __shared__ int nlist;
@@ -297,15 +312,15 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
         }
     };
 #pragma unroll
-    for (int d = 0; d < kDepth; ++d)
+    for (int d = 0; d < kDepth; ++d) {
         issue(d, d);
+        __builtin_amdgcn_sched_barrier(0);
+    }
     for (int s0 = 0; s0 < steps; s0 += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             const int st = s0 + d;
-            if (st >= steps)
-                break;
-            const int buf = st & 1;
+            const int buf = d & 1;
             *reinterpret_cast<bf16x8 *>(&As[buf][arow * kPitch + acol]) = ra[d];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
