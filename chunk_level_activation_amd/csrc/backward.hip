@@ -158,21 +158,30 @@ struct PassArgs {
 };
 
 constexpr int kPP = kPKP;                 // the expert pass's LDS pitch (same k step)
+constexpr int kPassThreads = 2 * kBT;     // two 4-wave groups: X W1^T and DY W2
 
-__global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
+// Waves 0-3 multiply X by W1_e^T and waves 4-7 DY by W2_e (the same 128 x 128 tile
+// loop on their own LDS tiles, three k steps of loads in flight); the second group then
+// hands G to the first through LDS (each thread's accumulators to the thread with the
+// same position in the first group), which applies the epilogue.
+__global__ void __launch_bounds__(kPassThreads, 2) expert_pass_kernel(PassArgs a)
 {
     const Dims &d = a.d;
     const int e = blockIdx.x % d.E, grp = blockIdx.x / d.E;
     const int cnt = a.tile_count[e];
     if (grp * kPassTiles >= cnt)
         return;
-    __shared__ alignas(16) uint16_t As1[kTM * kPP], Bs1[kTM * kPP], As2[kTM * kPP], Bs2[kTM * kPP];
+    // operand tiles As1 Bs1 As2 Bs2, reused after the k loop for the hand-over of G
+    __shared__ alignas(16) uint16_t ops[4 * kTM * kPP];
+    static_assert(sizeof(ops) >= (size_t)kBT * 64 * sizeof(float), "G hand-over fits the operand tiles");
     __shared__ float red[kTM][65];
     __shared__ float dsacc[kTM], scol[kTM];
     __shared__ int64_t tok[kTM];
     __shared__ int tiles[kPassTiles];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave & 1, wn = wave >> 1;
+    const int g = __builtin_amdgcn_readfirstlane(wave >> 2);   // 0: X W1^T, 1: DY W2
+    const int gt = tid & (kBT - 1);                            // thread within the group
+    const int wm = wave & 1, wn = (wave >> 1) & 1;
     if (tid < kPassTiles)
         tiles[tid] = grp * kPassTiles + tid < cnt ? a.tile_list[(int64_t)e * d.CT + grp * kPassTiles + tid] : -1;
     __syncthreads();
@@ -184,110 +193,105 @@ __global__ void __launch_bounds__(kBT, 1) expert_pass_kernel(PassArgs a)
     }
     __syncthreads();
 
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)d.T * d.d_h * 2);
-    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, (uint64_t)d.T * d.d_h * 2);
-    const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
-    const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(a.w2t, (uint64_t)d.E * d.d_e * d.d_h * 2);
-    // staging: vector q = tid + 256 i (i < 4) is row q / 8, k offset (q % 8) * 8; all four
-    // operands are k-contiguous rows (x, dy: tokens; W1, W2^T: hidden units)
-    constexpr int kV = kTM * kPK / 8 / kBT;    // 4 vectors per thread per operand
-    int srow[kV], skv[kV];
-    uint32_t xoff[kV];
+    // the group's operands: token rows of x or dy, hidden-unit rows of W1 or W2^T (both
+    // [E][d_e][d_h], so the same offsets serve either)
+    const __amdgpu_buffer_rsrc_t rA =
+        make_rsrc(g ? a.dy : a.x, (uint64_t)d.T * d.d_h * 2);
+    const __amdgpu_buffer_rsrc_t rB =
+        make_rsrc(g ? a.w2t : a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
+    uint16_t *As = ops + (2 * g) * kTM * kPP, *Bs = ops + (2 * g + 1) * kTM * kPP;
+    // piece i of this thread: row (gt + 256 i) / 8, k offset (gt % 8) * 8
+    constexpr int kV = kTM * kPK / 8 / kBT;    // 4
+    uint32_t xoff[kV], xmask[kV];
 #pragma unroll
     for (int i = 0; i < kV; ++i) {
-        const int q = tid + i * kBT;
-        srow[i] = q >> 3;
-        skv[i] = (q & 7) * 8;
-        const int64_t t = tok[srow[i]];
-        xoff[i] = t >= 0 ? (uint32_t)((t * d.d_h + skv[i]) * 2) : kOOB;
+        const int q = gt + i * kBT;
+        const int64_t t = tok[q >> 3];
+        xmask[i] = 0u - (uint32_t)(t >= 0);
+        xoff[i] = t >= 0 ? (uint32_t)((t * d.d_h + (q & 7) * 8) * 2) : 0u;
     }
     const int KS = d.d_h / kPK;
+    float *gbuf = reinterpret_cast<float *>(ops);   // [64 values][256 threads]
     for (int u0 = 0; u0 < d.d_e; u0 += kTM) {
-        f32x16 acc1[2][2], acc2[2][2];
+        uint32_t woff[kV];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                zero_acc(acc1[i][j]);
-                zero_acc(acc2[i][j]);
-            }
-        u32x4 rxv[kV], rw1v[kV], rdyv[kV], rw2v[kV];
-        auto load_step = [&](int s) {
+        for (int i = 0; i < kV; ++i) {
+            const int q = gt + i * kBT;
+            woff[i] = (uint32_t)((((int64_t)e * d.d_e + u0 + (q >> 3)) * d.d_h + (q & 7) * 8) * 2);
+        }
+        auto load = [&](int s, u32x4(&ra)[4], u32x4(&rb)[4]) {
+            const uint32_t okm = 0u - (uint32_t)(s < KS);
             const uint32_t ko = (uint32_t)(s * kPK * 2);
 #pragma unroll
             for (int i = 0; i < kV; ++i) {
-                const uint32_t xo = xoff[i] == kOOB ? kOOB : xoff[i] + ko;
-                const uint32_t wo =
-                    (uint32_t)((((int64_t)e * d.d_e + u0 + srow[i]) * d.d_h + skv[i]) * 2) + ko;
-                rxv[i] = load16(rx, xo);
-                rdyv[i] = load16(rdy, xo);
-                rw1v[i] = load16(rw1, wo);
-                rw2v[i] = load16(rw2, wo);
+                const uint32_t am = okm & xmask[i];
+                ra[i] = load16(rA, ((xoff[i] + ko) & am) | (kOOB & ~am));
+                rb[i] = load16(rB, ((woff[i] + ko) & okm) | (kOOB & ~okm));
             }
         };
-        load_step(0);
-        for (int s = 0; s < KS; ++s) {
+        f32x16 acc[2][2];
+        tile::zero_acc(acc);
+        kloop_128x128(load, KS, As, Bs, acc, gt, wm, wn, lane);
+        // the k loop ended with a barrier: the operand tiles are free for G
+        if (g == 1) {
 #pragma unroll
-            for (int i = 0; i < kV; ++i) {
-                const int o = srow[i] * kPP + skv[i];
-                *reinterpret_cast<u32x4 *>(&As1[o]) = rxv[i];
-                *reinterpret_cast<u32x4 *>(&Bs1[o]) = rw1v[i];
-                *reinterpret_cast<u32x4 *>(&As2[o]) = rdyv[i];
-                *reinterpret_cast<u32x4 *>(&Bs2[o]) = rw2v[i];
-            }
-            __syncthreads();
-            if (s + 1 < KS)
-                load_step(s + 1);
-            mma_64x64<kPK>(As1, Bs1, acc1, wm, wn, lane);
-            mma_64x64<kPK>(As2, Bs2, acc2, wm, wn, lane);
-            __syncthreads();
+            for (int i = 0; i < 2; ++i)
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int v = 0; v < 16; ++v)
+                        gbuf[((i * 2 + j) * 16 + v) * kBT + gt] = acc[i][j][v];
         }
-        // epilogue: Swish, its slope, the score
-        float part[2][16];
+        __syncthreads();
+        if (g == 0) {
+            // epilogue: Swish, its slope, the score
+            float part[2][16];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                part[i][v] = 0.0f;
+                for (int v = 0; v < 16; ++v)
+                    part[i][v] = 0.0f;
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                const int unit = u0 + wn * 64 + j * 32 + (lane & 31);
+                for (int j = 0; j < 2; ++j) {
+                    const int unit = u0 + wn * 64 + j * 32 + (lane & 31);
 #pragma unroll
-                for (int vg = 0; vg < 4; ++vg) {
-                    uint32_t da_pk[2] = {0u, 0u}, sh_pk[2] = {0u, 0u};
-                    const int row0 = wm * 64 + i * 32 + acc_row(vg * 4, lane);   // 4 consecutive rows
-                    const int tile = tiles[row0 / kTileM];
+                    for (int vg = 0; vg < 4; ++vg) {
+                        uint32_t da_pk[2] = {0u, 0u}, sh_pk[2] = {0u, 0u};
+                        const int row0 = wm * 64 + i * 32 + acc_row(vg * 4, lane);   // 4 consecutive rows
+                        const int tile = tiles[row0 / kTileM];
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        const int v = vg * 4 + q, row = row0 + q;
-                        const float av = acc1[i][j][v], g = acc2[i][j][v], s = scol[row];
-                        const float sig = 1.0f / (1.0f + expf(-av));
-                        const float h = av * sig;
-                        part[i][v] += g * h;
-                        const float dA = s * g * (sig * (1.0f + av * (1.0f - sig)));
-                        const float sh = s * h;
-                        const uint32_t b_da = f32_to_bf16(dA), b_sh = f32_to_bf16(sh);
-                        da_pk[q >> 1] |= b_da << ((q & 1) * 16);
-                        sh_pk[q >> 1] |= b_sh << ((q & 1) * 16);
-                        if (tile >= 0)
-                            a.da_tu[(((int64_t)tile * d.E + e) * kTileM + row % kTileM) * d.d_e + unit] =
-                                (uint16_t)b_da;
-                    }
-                    if (tile >= 0) {
-                        const int64_t o = (((int64_t)tile * d.E + e) * d.d_e + unit) * kTileM + row0 % kTileM;
-                        *reinterpret_cast<uint64_t *>(&a.da_ut[o]) = (uint64_t)da_pk[0] | ((uint64_t)da_pk[1] << 32);
-                        *reinterpret_cast<uint64_t *>(&a.sh_ut[o]) = (uint64_t)sh_pk[0] | ((uint64_t)sh_pk[1] << 32);
+                        for (int q = 0; q < 4; ++q) {
+                            const int v = vg * 4 + q, row = row0 + q;
+                            const float av = acc[i][j][v], s = scol[row];
+                            const float gv = gbuf[((i * 2 + j) * 16 + v) * kBT + gt];
+                            const float sig = 1.0f / (1.0f + expf(-av));
+                            const float h = av * sig;
+                            part[i][v] += gv * h;
+                            const float dA = s * gv * (sig * (1.0f + av * (1.0f - sig)));
+                            const float sh = s * h;
+                            const uint32_t b_da = f32_to_bf16(dA), b_sh = f32_to_bf16(sh);
+                            da_pk[q >> 1] |= b_da << ((q & 1) * 16);
+                            sh_pk[q >> 1] |= b_sh << ((q & 1) * 16);
+                            if (tile >= 0)
+                                a.da_tu[(((int64_t)tile * d.E + e) * kTileM + row % kTileM) * d.d_e + unit] =
+                                    (uint16_t)b_da;
+                        }
+                        if (tile >= 0) {
+                            const int64_t o = (((int64_t)tile * d.E + e) * d.d_e + unit) * kTileM + row0 % kTileM;
+                            *reinterpret_cast<uint64_t *>(&a.da_ut[o]) = (uint64_t)da_pk[0] | ((uint64_t)da_pk[1] << 32);
+                            *reinterpret_cast<uint64_t *>(&a.sh_ut[o]) = (uint64_t)sh_pk[0] | ((uint64_t)sh_pk[1] << 32);
+                        }
                     }
                 }
-            }
-        // ds: per-lane row partials -> LDS [row][64 columns] -> summed in column order
+            // ds: per-lane row partials -> LDS [row][64 columns] -> summed in column order
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+            for (int i = 0; i < 2; ++i)
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                red[wm * 64 + i * 32 + acc_row(v, lane)][wn * 32 + (lane & 31)] = part[i][v];
+                for (int v = 0; v < 16; ++v)
+                    red[wm * 64 + i * 32 + acc_row(v, lane)][wn * 32 + (lane & 31)] = part[i][v];
+        }
         __syncthreads();
         if (tid < kTM) {
             float sum = 0.0f;
@@ -854,7 +858,7 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     pa.sh_ut = reinterpret_cast<uint16_t *>(at(L.sh_ut));
     pa.d = d;
     const int64_t pass_blocks = b.E * ((p.CT + kPassTiles - 1) / kPassTiles);
-    hipLaunchKernelGGL(expert_pass_kernel, dim3((unsigned)pass_blocks), dim3(kBT), 0, stream, pa);
+    hipLaunchKernelGGL(expert_pass_kernel, dim3((unsigned)pass_blocks), dim3(kPassThreads), 0, stream, pa);
 
     WgradArgs wa;
     wa.xt = xt;
