@@ -228,6 +228,26 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
 
     const int cpr = a.d_h / 8;
     const int nxl = kTileM * cpr / kThreads;
+    // x goes to LDS without registers: LDS chunk slot q = i * 512 + tid (token q / cpr,
+    // slot q % cpr) takes the chunk the swizzled order puts there, (q % cpr) ^ (token &
+    // 15); tokens past T read as zero. The (token, slot) of q steps by 512 slots per
+    // load without a division.
+    auto stage_x = [&]() {
+        const int dt = kThreads / cpr, dp = kThreads % cpr;
+        int t = tid / cpr, p = tid % cpr;
+#pragma unroll
+        for (int i = 0; i < kMaxXLoads; ++i) {
+            if (i < nxl)
+                bload_lds16<0>(rx, &sh.xs[(i * kThreads + wave * kWave) * 8],
+                               (uint32_t)((t * cpr + (p ^ (t & 15))) * 16));
+            p += dp;
+            t += dt;
+            if (p >= cpr) {
+                p -= cpr;
+                ++t;
+            }
+        }
+    };
     bf16x8 xv[kMaxXLoads];
     int cnt;
     uint64_t wm[kMaxWords];
@@ -244,8 +264,10 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                 sv[i] = bload_f1<0>(rs, tt < a.T && e < a.E ? (uint32_t)((tt * a.E + e) * 4) : kOOB);
             }
         }
-        // x, contiguous: 16-byte chunk q = i * 512 + tid of the 32 x d_h tile (token
-        // q / cpr, chunk q % cpr); tokens past T read as zero.
+        // x, contiguous, through registers (staged in LDS after the union: loads straight
+        // into LDS would make the union's barriers wait for them): 16-byte chunk q = i *
+        // 512 + tid of the 32 x d_h tile (token q / cpr, chunk q % cpr); tokens past T
+        // read as zero.
 #pragma unroll
         for (int i = 0; i < kMaxXLoads; ++i)
             xv[i] = bload<0>(rx, (uint32_t)((i * kThreads + tid) * 16));
@@ -255,9 +277,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         // the router: experts e0 .. e0 + EPM (EPM = ceil(E / P) <= 2). Wave w takes the
         // d_h eighth [w * d_h / 8, +d_h / 8): A = the member's W_r rows (16-row block,
         // rows past EPM read zero) straight from memory, B = x from LDS, 16x16x32 MFMA.
-#pragma unroll
-        for (int i = 0; i < kMaxXLoads; ++i)
-            xv[i] = bload<0>(rx, (uint32_t)((i * kThreads + tid) * 16));
+        stage_x();
         const int EPM = (a.E + a.P - 1) / a.P;
         const int e0 = k * EPM;
         const int KS8 = a.d_h / 256;              // 32-wide k steps per eighth (<= 8)
@@ -278,12 +298,6 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             bv[i] = (a.bias && e < a.E) ? a.bias[e] : 0.0f;
         }
         const uint32_t repoch = 1u + ld_counter(&a.rflags[g * a.P + k]);
-#pragma unroll
-        for (int i = 0; i < kMaxXLoads; ++i)
-            if (i < nxl) {
-                const int q = i * kThreads + tid;
-                *reinterpret_cast<bf16x8 *>(&sh.xs[xs_chunk(q / cpr, q % cpr, cpr) * 8]) = xv[i];
-            }
         if (tid < 2 * cpr)
             *reinterpret_cast<bf16x8 *>(&sh.wr[tid * 8]) = wrc;
         __syncthreads();

@@ -30,6 +30,16 @@ __device__ __forceinline__ bf16x8 bload(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, AUX));
 }
+// 16 bytes per lane from buffer offset off straight into LDS, without registers: lane
+// l's bytes land at dst + 16 l (dst must be the same for the whole wave); an offset past
+// the range stores zeros. The data is in LDS once the wave's vector-memory count covers
+// the load.
+typedef __attribute__((address_space(3))) void lds_void;
+template <int AUX>
+__device__ __forceinline__ void bload_lds16(__amdgpu_buffer_rsrc_t r, void *dst, uint32_t off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void *)dst, 16, off, 0, 0, AUX);
+}
 template <int AUX>
 __device__ __forceinline__ float4 bload_f4(__amdgpu_buffer_rsrc_t r, uint32_t off)
 {
