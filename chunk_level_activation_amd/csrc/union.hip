@@ -24,7 +24,7 @@ union_kernel(const float *__restrict__ scores, int64_t T, int E, int64_t n, int 
              int32_t *__restrict__ counts, uint64_t *__restrict__ masks_out,
              int32_t *__restrict__ lists_out, int32_t *__restrict__ counts_out)
 {
-    constexpr int kBatch = 16;    // tokens whose score loads are in flight together
+    constexpr int kBatch = 32;    // tokens whose score loads are in flight together (one n = 32 chunk)
     const int64_t c = blockIdx.x;
     const int lane = threadIdx.x;
     const int64_t t0 = c * n;
@@ -35,13 +35,15 @@ union_kernel(const float *__restrict__ scores, int64_t T, int E, int64_t n, int 
         bool active = false;
         if (e < E) {
             for (int64_t tb = t0; tb < t1; tb += kBatch) {
+                // every load issued (tokens past the chunk re-read its last token and are
+                // masked out): a load under a branch would be waited for on its own
                 float v[kBatch];
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i)
-                    v[i] = tb + i < t1 ? scores[(tb + i) * E + e] : 0.0f;
+                    v[i] = scores[(tb + i < t1 ? tb + i : t1 - 1) * E + e];
 #pragma unroll
                 for (int i = 0; i < kBatch; ++i)
-                    active |= v[i] != 0.0f;
+                    active |= tb + i < t1 && v[i] != 0.0f;
             }
         }
         const uint64_t word = __ballot(active);
