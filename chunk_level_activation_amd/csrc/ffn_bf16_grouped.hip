@@ -122,6 +122,7 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
     __shared__ alignas(16) uint16_t As[2][kUpRows * kPitch];   // x rows x 64 k
     __shared__ alignas(16) uint16_t Bs[2][kUpCols * kPitch];   // W1 rows (hidden units) x 64 k
     __shared__ int64_t tok[kUpRows];
+    __shared__ float scol[kUpRows];   // score of (row's token, e), zero for rows without one
     __shared__ int tiles[kUpTiles];
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
@@ -131,8 +132,11 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
         tiles[tid] = b * kUpTiles + tid < cnt ? a.tile_list[(int64_t)e * a.CT + b * kUpTiles + tid]
                                               : -1;
     __syncthreads();
-    if (tid < kUpRows)
-        tok[tid] = tile_token(a, tiles[tid / kTileM], tid % kTileM);
+    if (tid < kUpRows) {
+        const int64_t t = tile_token(a, tiles[tid / kTileM], tid % kTileM);
+        tok[tid] = t;
+        scol[tid] = t >= 0 ? a.scores[t * a.E + e] : 0.0f;
+    }
     __syncthreads();
 
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)a.T * a.d_h * 2);
@@ -217,9 +221,7 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) {
                     const int r = acc_row(v, lane);
-                    const int64_t t = tok[wm * 32 + r];
-                    const float sc = t >= 0 ? a.scores[t * a.E + e] : 0.0f;
-                    const float h = swish_fast(acc[j][v]) * sc;
+                    const float h = swish_fast(acc[j][v]) * scol[wm * 32 + r];
                     a.hidden[(((int64_t)tile * a.E + e) * kTileM + r) * a.d_e + unit] = f32_to_bf16(h);
                 }
             }
