@@ -583,14 +583,29 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         return;
 
     // ---- down: B = the hidden rows (32 units x 16 tokens): lane (token l16 (+16),
-    // k group kgrp) holds units 32 (st0 + i) + 8 kgrp .. +8 of the group's range, from
-    // L2; in the fragment order each of these loads is one contiguous 1 KB access
+    // k group kgrp) holds units 32 (st0 + i) + 8 kgrp .. +8 of the group's range. In the
+    // fragment order the group's block is ng / 16 fragments of 1 KB, each lane-contiguous:
+    // it is copied once into LDS over the x tile (which the up products are done with) by
+    // loads that write LDS, and the four column-quarter waves that use each fragment read
+    // it from there instead of each loading it from L2.
+    char *hs = reinterpret_cast<char *>(sh.xs);
+    static_assert(kGroupUnitsMax / 16 * 1024 <= (int)sizeof(sh.xs), "the group's hidden block fits the x tile");
+    {
+        const int nfrag = (ng / 32) * 2;
+        const uint32_t gb = (uint32_t)(g * (kGroupUnitsMax / 32) * 2) * 1024u;
+#pragma unroll
+        for (int j = 0; j < kGroupUnitsMax / 16 / kWaves; ++j) {
+            const int f = j * kWaves + wave;
+            bload_lds16<kSC0>(rhid, hs + f * 1024, f < nfrag ? gb + (uint32_t)f * 1024u + lane * 16u : kOOB);
+        }
+    }
+    __syncthreads();
     bf16x8 hv[kMaxDnSteps][2];
 #pragma unroll
     for (int i = 0; i < kMaxDnSteps; ++i)
 #pragma unroll
         for (int th = 0; th < 2; ++th)
-            hv[i][th] = i < nsw ? bload<kSC0>(rhid, hid_offset(g, (st0 + i) * 32 + kgrp * 8, th * 16 + l16))
+            hv[i][th] = i < nsw ? *reinterpret_cast<const bf16x8 *>(hs + ((st0 + i) * 2 + th) * 1024 + lane * 16)
                                 : zero_bf16x8();
     acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
     acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
