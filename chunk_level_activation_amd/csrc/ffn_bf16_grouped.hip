@@ -15,9 +15,10 @@
 //   3. up_grouped_kernel: workgroup = (expert e, 4 of e's tiles): a 128 x d_e x d_h
 //      GEMM (x rows gathered, W1_e read once per workgroup and shared through the
 //      XCD's L2 by the workgroups of the same expert, which the grid places on one
-//      XCD), double-buffered through LDS with kDepth k steps of loads in flight,
-//      32x32x16 bf16 MFMA, then Swish and the score; the bf16 hidden rows go to
-//      Ht[tile][e].
+//      XCD), double-buffered through LDS with kUpDepth k steps of loads in flight
+//      (few enough registers for two 8-wave workgroups per CU), 32x32x16 bf16 MFMA,
+//      then Swish and the score (staged in LDS with the rows' tokens); the bf16 hidden
+//      rows go to Ht[tile][e].
 //   4. down_grouped_kernel: workgroup = (2 chunk tiles, 256 output columns): a
 //      64 x 256 GEMM over k = the union of the two chunks' experts x d_e, ascending,
 //      with the hidden rows of a tile whose chunk does not use the expert read as
@@ -112,6 +113,7 @@ __global__ void __launch_bounds__(256) expert_tiles_kernel(GroupedArgs a)
 }
 
 // ------------------------------------------------------------------ up (grouped GEMM)
+// At least 4 waves per SIMD (at most 128 registers): two 8-wave workgroups per CU.
 __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 {
     const int e = blockIdx.x % a.E;
