@@ -312,7 +312,7 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
             const int r = q >> 3, c8 = (q & 7) * 8;
             const uint32_t boffs =
                 (uint32_t)(((e * a.d_h + ct * kDnCols + r) * a.d_e + k0 + c8) * 2);
-            rb[d][i] = bload<kNT>(rw2, ok ? boffs : kOutOfRange);
+            rb[d][i] = bload<0>(rw2, ok ? boffs : kOutOfRange);
         }
     };
 #pragma unroll
