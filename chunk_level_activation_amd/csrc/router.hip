@@ -28,7 +28,7 @@ namespace blockffn {
 // order.
 constexpr int kRouterThreads = 512;
 constexpr int kRouterWaves = kRouterThreads / kWave;
-constexpr int64_t kRouterTargetBlocks = 128;   // split the d_h sum until about this many
+constexpr int64_t kRouterTargetBlocks = 256;   // split the d_h sum until about this many (one per CU)
 constexpr int kRouterMaxSplits = 8;
 
 // LOCAL: the S splits of a tile run on one XCD (the caller verified round-robin
