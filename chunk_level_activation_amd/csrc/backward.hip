@@ -524,6 +524,15 @@ constexpr int kRtPer = 256 / kWave;       // experts per lane (E <= 256)
 // union, plus the probability term), the RMSNorm and ReLU backward -> dl, and the gain
 // term; then dx[t] += W_r^T dl for the workgroup's tokens, each W_r row loaded once for
 // all of them (experts in order, eight rows in flight).
+// p[0 .. n) = 0 (the recomputed router's arrival counters: this workspace is not
+// zero-filled by the caller)
+__global__ void __launch_bounds__(kBT) zero_words_kernel(uint32_t *p, int64_t n)
+{
+    const int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x;
+    if (i < n)
+        p[i] = 0u;
+}
+
 __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
 {
     const Dims &d = a.d;
@@ -728,6 +737,7 @@ struct BwdLayout {
     size_t masks, lists, counts, tile_list, tile_count;
     size_t logits, scores, ds, dl, gt;
     size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, w1t, w2t, dx_part;
+    size_t router;        // the forward router's split workspace (0 bytes when it takes none)
     int dx_splits;
     size_t total;
 };
@@ -773,6 +783,7 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
     L.da_ut = take(2 * p.CT * E * kTileM * d_e);
     L.sh_ut = take(2 * p.CT * E * kTileM * d_e);
     L.rp_part = take(4 * (size_t)router_param_splits(T, d_h, E) * E * d_h);
+    L.router = take(router_workspace_bytes(T, d_h, E));
     L.w1t = take(2 * (size_t)E * d_e * d_h);
     L.w2t = take(2 * (size_t)E * d_e * d_h);
     L.dx_splits = dx_splits(p.CT, d_h, E);
@@ -810,8 +821,17 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     auto at = [&](size_t off) { return base + off; };
     float *logits = reinterpret_cast<float *>(at(L.logits));
     float *scores = reinterpret_cast<float *>(at(L.scores));
+    // the forward router with its d_h split when it takes one (few tokens): its arrival
+    // counters are cleared first
+    void *rws = nullptr;
+    if (router_workspace_bytes(b.T, b.d_h, b.E) > 0) {
+        rws = at(L.router);
+        const int64_t tiles = (b.T + kTileM - 1) / kTileM;
+        hipLaunchKernelGGL(zero_words_kernel, dim3((unsigned)((tiles + kBT - 1) / kBT)), dim3(kBT), 0, stream,
+                           static_cast<uint32_t *>(rws), tiles);
+    }
     hipError_t err = launch_router_bf16(b.x, b.w_r, b.gain, b.bias, b.eps, b.T, b.d_h, b.E, scores,
-                                        logits, 1.0f, nullptr, nullptr, 0, stream);
+                                        logits, 1.0f, nullptr, rws, 0, stream);
     if (err != hipSuccess)
         return err;
     if ((err = launch_union(p, scores, ws, nullptr, nullptr, nullptr, stream)) != hipSuccess)
