@@ -17,13 +17,15 @@
 //                 dgain_e = sum_t ds r inv
 //
 // Kernels, in stream order (all products on 32x32x16 bf16 MFMA, fp32 accumulation):
-//   0. the forward router (recomputed: logits and scores), the chunk unions and the
-//      per-expert tile lists (the forward's kernels);
+//   0. the forward router (recomputed: logits and scores, with its d_h split when it
+//      takes one), the chunk unions and the per-expert tile lists (the forward's
+//      kernels);
 //   1. transpose_tiles_kernel: x and dy copied per 32-token chunk tile as
 //      [tile][d_h][32 tokens], so the weight-gradient products, whose k is the token,
 //      read k-contiguous operands;
-//   2. expert_pass_kernel, workgroup = (expert e, 4 of its tiles): a = X W1_e^T and
-//      G = DY W2_e over d_h (B = W2^T rows), then ds, and dA and SH in bf16 in both
+//   2. expert_pass_kernel, workgroup = (expert e, 4 of its tiles), 8 waves: a = X W1_e^T
+//      on waves 0-3 and G = DY W2_e on waves 4-7 over d_h (B = W2^T rows), both on the
+//      128 x 128 tile loop of tile_gemm.h; then ds, and dA and SH in bf16 in both
 //      [token][unit] and [unit][token] order;
 //   3. wgrad_kernel, workgroup = (expert, dW1 or dW2, 128 x 128 output tile): k over the
 //      expert's tiles' tokens; every output element is owned by one workgroup (an
