@@ -1,7 +1,6 @@
-// The 128 x 128 bf16 output tile shared by the grouped expert products (prefill up
-// projection, backward expert gradients): 256 threads = 4 waves, each wave a 64 x 64
-// block of 2 x 2 32x32x16 MFMA accumulators, operands staged through LDS as [row][k]
-// tiles of 64 k.
+// The 128 x 128 bf16 output tile of the backward's expert-pass and dx products: 256
+// threads = 4 waves, each wave a 64 x 64 block of 2 x 2 32x32x16 MFMA accumulators,
+// operands staged through LDS as [row][k] tiles of 64 k.
 //
 // A 64 x 64 wave block reads 16 KB of LDS per 64-wide k step for 512 KFLOP (32 flops
 // per byte), twice the ratio of a 32 x 64 block: with LDS delivering about 150 bytes
