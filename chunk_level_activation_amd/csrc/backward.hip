@@ -696,22 +696,38 @@ __global__ void __launch_bounds__(kBT) router_param_reduce_kernel(RouterArgs a, 
 {
     const Dims &d = a.d;
     const int e0 = blockIdx.x * kRpE, j = blockIdx.y * kBT + threadIdx.x, tid = threadIdx.x;
+    // the kRpE experts' partials of up to 16 splits requested together, then added in
+    // split order (experts past E and splits past `splits` read zero and are not added)
+    const __amdgpu_buffer_rsrc_t rpp = make_rsrc(part, (uint64_t)splits * d.E * d.d_h * 4);
+    for (int z0 = 0; z0 < splits; z0 += 16) {
+        float pv[16][kRpE];
 #pragma unroll
-    for (int q = 0; q < kRpE; ++q)
-        if (e0 + q < d.E) {
-            float sum = 0.0f;
-#pragma unroll 8
-            for (int z = 0; z < splits; ++z)
-                sum += part[((int64_t)z * d.E + e0 + q) * d.d_h + j];
-            a.dw_r[(int64_t)(e0 + q) * d.d_h + j] = sum;
-        }
+        for (int z = 0; z < 16; ++z)
+#pragma unroll
+            for (int q = 0; q < kRpE; ++q) {
+                const bool ok = z0 + z < splits && e0 + q < d.E;
+                pv[z][q] = __builtin_bit_cast(
+                    float, __builtin_amdgcn_raw_buffer_load_b32(
+                               rpp, ok ? (int)((((int64_t)(z0 + z) * d.E + e0 + q) * d.d_h + j) * 4) : (int)kOOB, 0, 0));
+            }
+#pragma unroll
+        for (int q = 0; q < kRpE; ++q)
+            if (e0 + q < d.E) {
+                float sum = z0 == 0 ? 0.0f : a.dw_r[(int64_t)(e0 + q) * d.d_h + j];
+#pragma unroll
+                for (int z = 0; z < 16; ++z)
+                    if (z0 + z < splits)
+                        sum += pv[z][q];
+                a.dw_r[(int64_t)(e0 + q) * d.d_h + j] = sum;
+            }
+    }
     if (blockIdx.y != 0)
         return;
     __shared__ float pg[kBT], pb[kBT];
     const int q = tid % kRpE, sl = tid / kRpE;
     float sg = 0.0f, sb = 0.0f;
     if (e0 + q < d.E) {
-#pragma unroll 8
+#pragma unroll 16
         for (int64_t t = sl; t < d.T; t += kBT / kRpE) {
             sg += a.gt[t * d.E + e0 + q];
             sb += a.dl[t * d.E + e0 + q];
