@@ -1,0 +1,107 @@
+"""Parity of the exact path the benchmark times, on the inputs it times it on.
+
+bench.py times blockffn_layer_forward_packed (router and chunk FFN in one launch, expert
+weights in the tiled layout) on the decode chunk: d_h=2048, E=64, d_e=128, T = n = 32,
+bf16. Its inputs make the router's activity follow per-expert Markov on/off masks at
+80% token-level / 70% 8-token chunk-level sparsity (W_r with orthonormal rows, each
+token built so that W_r x_t has the mask's signs with a 0.1 margin), so the chunk
+union is sparse (about 35 of 64 experts). The inputs here come from bench.py's own
+construction (make_inputs), with fewer weight copies.
+
+Bars (skill page "BlockFFN: Sparse Mixture-of-Experts Optimized for End-Device
+Deployment", "Core Concept" and "Architecture Overview"): y within
+max|dy| / max|y_ref| <= 1e-2 of the oracle's router feeding the oracle's chunk FFN;
+the union of the fused call's scores bit-exact against the oracle's union (every
+logit is at least 0.1 from zero, so no activity decision is ill-conditioned); the
+scores within 1e-4 of max|s_ref|.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bench
+import chunk_level_activation_amd as bf
+import oracle
+from chunk_level_activation_amd import inputs
+from gpu_helpers import DEV, TOL_BF16, host, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def bench_inputs():
+    args = bench.parse_args(["--rotate-mib", "1", "--draws", "6", "--seed", "3"])
+    cfg, copies, draws, xs, S = bench.make_inputs(args, torch, np, inputs)
+    for w in copies:
+        w["packed"] = bf.blockffn_pack_weights(w["w1"], w["w2"])
+    torch.cuda.synchronize()
+    return cfg, copies, draws, xs, S
+
+
+def _oracle_step(x, w):
+    x_h, w_r = host(x), host(w["w_r"])
+    logits, s_ref = oracle.router(x_h, w_r)
+    y_ref = oracle.chunk_ffn(x_h, s_ref.astype(np.float32), host(w["w1"]), host(w["w2"]), 32)
+    return logits, s_ref, y_ref
+
+
+def test_bench_path_matches_oracle(bench_inputs):
+    cfg, copies, draws, xs, S = bench_inputs
+    T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
+    assert (T, d_h, E, d_e, n) == (32, 2048, 64, 128, 32)
+    assert bf.blockffn_layer_forward_fused(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16)
+    gain = torch.ones(E, dtype=torch.float32, device=DEV)
+    lws = bf.blockffn_layer_forward_workspace(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16, DEV)
+    sizes = []
+    for i in range(S):
+        w, x = copies[i % len(copies)], xs[i % S]
+        sc = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        y = bf.blockffn_layer_forward_packed(x, w["w_r"], w["packed"], E, d_e, n, gain=gain,
+                                             bias=w["bias"], scores=sc, workspace=lws)
+        sc_rm = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        y_rm = bf.blockffn_layer_forward(x, w["w_r"], w["w1"], w["w2"], n, gain=gain,
+                                         bias=w["bias"], scores=sc_rm, workspace=lws)
+        torch.cuda.synchronize()
+        logits, s_ref, y_ref = _oracle_step(x, w)
+        s = sc.cpu().numpy()
+        # activity is decided everywhere: the logits keep the mask's 0.1 margin
+        assert np.abs(logits).min() > 0.05
+        m_ref, l_ref, c_ref = oracle.chunk_union(s_ref.astype(np.float32), n)
+        m_got, l_got, c_got = oracle.chunk_union(s, n)
+        assert np.array_equal(m_got, m_ref) and np.array_equal(l_got, l_ref), i
+        assert np.array_equal(c_got, c_ref)
+        # the mask the inputs were built for is the router's activity
+        act = draws[i % len(draws)]["act"]
+        assert np.array_equal(s != 0, act), i
+        assert rel_err(s, s_ref) <= 1e-4
+        assert rel_err(host(y), y_ref) <= TOL_BF16, i
+        # packed and row-major weights give the same bits
+        assert torch.equal(y, y_rm) and torch.equal(sc, sc_rm)
+        sizes.append(int(c_ref[0]))
+    # the configuration the headline runs in: sparse unions, not near-full ones
+    assert all(20 <= c <= 52 for c in sizes), sizes
+    assert 28 <= np.mean(sizes) <= 44, sizes
+
+
+def test_bench_path_union_outputs_of_chunk_ffn(bench_inputs):
+    """blockffn_chunk_ffn on the fused call's scores reports exactly the oracle's union
+    (masks, ascending list, count), and its y agrees with the fused call's."""
+    cfg, copies, draws, xs, S = bench_inputs
+    T, d_h, E, d_e, n = cfg["T"], cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
+    gain = torch.ones(E, dtype=torch.float32, device=DEV)
+    for i in range(min(S, 3)):
+        w, x = copies[i % len(copies)], xs[i % S]
+        sc = torch.empty((T, E), dtype=torch.float32, device=DEV)
+        y = bf.blockffn_layer_forward_packed(x, w["w_r"], w["packed"], E, d_e, n, gain=gain,
+                                             scores=sc)
+        masks = torch.empty((1, 1), dtype=torch.int64, device=DEV)
+        lists = torch.empty((1, E), dtype=torch.int32, device=DEV)
+        counts = torch.empty((1,), dtype=torch.int32, device=DEV)
+        y2 = bf.blockffn_chunk_ffn(x, sc, w["w1"], w["w2"], n, union_masks=masks,
+                                   expert_lists=lists, union_counts=counts)
+        torch.cuda.synchronize()
+        m_ref, l_ref, c_ref = oracle.chunk_union(sc.cpu().numpy(), n)
+        assert np.array_equal(masks.cpu().numpy().view(np.uint64), m_ref)
+        assert np.array_equal(lists.cpu().numpy(), l_ref)
+        assert np.array_equal(counts.cpu().numpy(), c_ref)
+        assert rel_err(host(y), host(y2)) <= 1e-2
