@@ -110,8 +110,20 @@ struct Shared {
     // [2 step halves][64 columns][32 tokens]
     alignas(16) float red[2 * kDnCols * kRedPitch];
     alignas(16) uint16_t xs[kTileM * kMaxDh];   // x, 16-byte chunk c of token t at chunk c ^ (t & 15)
-    alignas(16) uint16_t wr[2 * kMaxDh];        // the member's (at most 2) W_r rows (router)
+    // the member's (at most 2) W_r rows for the router products; after the router, the
+    // chunk's scores [E][32 tokens] (fp32, the same bytes: kMaxLayerE * 32 * 4)
+    alignas(16) uint16_t wr[2 * kMaxDh];
 };
+
+// Workgroup barrier that waits for this wave's LDS accesses only, not for its loads
+// from memory still in flight (which __syncthreads would wait for).
+__device__ __forceinline__ void lds_barrier()
+{
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0); vmcnt and expcnt left alone
+    __builtin_amdgcn_s_barrier();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
 // Union of the experts active in the chunk, ascending list in LDS; returns |U| and
 // leaves the mask words in wm. Thread tid holds in sv[i] the score of token tid / 16
@@ -208,6 +220,8 @@ template <bool ROUTER, bool PACKED>
 __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs a)
 {
     __shared__ Shared sh;
+    static_assert(kMaxLayerE * kTileM * 4 <= (int)sizeof(sh.wr), "the scores fit the W_r rows' region");
+    float *const scol_lds = reinterpret_cast<float *>(sh.wr);
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int l16 = lane & 15, kgrp = lane >> 4;
@@ -388,7 +402,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                 const float sc = tt < a.T && e < a.E ? rv[i] * inv * gv[i] : 0.0f;
                 sv[i] = sc;
                 if (e < a.E) {
-                    sh.red[e * kRedPitch + tt] = sc;
+                    scol_lds[e * kTileM + tt] = sc;
                     if (blockIdx.x == 0 && a.scores_out && tt < a.T)
                         a.scores_out[tt * a.E + e] = sc;
                 }
@@ -426,6 +440,24 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     const int fs = M0 / a.d_e;              // the member's first slot
     const int fsu = (fs + 1) * a.d_e;       // first unit of the next slot
 
+    // the member's score columns, zero past T: requested before W1 (so that scores given
+    // as an input do not arrive behind W1) and put in LDS after the up products (by then
+    // they have arrived; the Swish epilogue reads them after the next barrier)
+    float scv = 0.0f;
+    {
+        const int j = (tid / kTileM) & 1, t = tid % kTileM;
+        const bool ok = tid < 2 * kTileM && nrows > 0 && fs + j < cnt;
+        const int e = sh.list[ok ? fs + j : 0];
+        if constexpr (ROUTER) {
+            if (ok)
+                scv = scol_lds[e * kTileM + t];
+        } else {
+            // every thread issues the load (past T or outside the columns it reads zero),
+            // so the loads that follow keep exact wait counts
+            const __amdgpu_buffer_rsrc_t rs = make_rsrc(a.scores, (uint64_t)a.T * a.E * 4);
+            scv = bload_f1<0>(rs, ok && t < a.T ? (uint32_t)((t * a.E + e) * 4) : kOOB);
+        }
+    }
     // W1 as the A operand (16 rows x 32 k): wave (row half rh, k quarter kq); lane
     // (row l16, k group kgrp) holds row rh*16 + l16 of the member's piece (unit
     // M0 + row of the union) at k = kq*d_h/4 + 32 ks + 8 kgrp .. +8.
@@ -448,10 +480,17 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                                 2)
                    : (uint32_t)(((e * a.d_e + unit) * a.d_h + kq0 + kgrp * 8) * 2);
         const uint32_t kstride = PACKED ? 1024u : 64u;
+        // Only the lanes of rows inside the piece issue loads (lanes of absent rows are
+        // switched off and keep zeros), so a block with a few rows costs the CU's load
+        // path only those rows; steps past d_h read zero without touching memory.
 #pragma unroll
         for (int ks = 0; ks < kMaxKSteps; ++ks)
-            wa[ks] = rh * 16 < nrows && ks < KSU ? bload<kNT>(rw1, vr ? base + ks * kstride : kOOB)
-                                                  : zero_bf16x8();
+            wa[ks] = zero_bf16x8();
+        if (rh * 16 < nrows && vr) {
+#pragma unroll
+            for (int ks = 0; ks < kMaxKSteps; ++ks)
+                wa[ks] = bload<kNT>(rw1, ks < KSU ? base + ks * kstride : kOOB);
+        }
     }
 
     // W2 as the A operand of the down products (16 columns x 32 units): wave (column
@@ -475,19 +514,6 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         sbase = sh.list[sl] * a.d_h * a.d_e + (PACKED ? (unit >> 5) * 512 : unit);
     }
 
-    // the member's score columns, zero past T
-    if (tid < 2 * kTileM) {
-        const int j = tid / kTileM, t = tid % kTileM;
-        float v = 0.0f;
-        if (nrows > 0 && fs + j < cnt) {
-            const int e = sh.list[fs + j];
-            if constexpr (ROUTER)
-                v = sh.red[e * kRedPitch + t];
-            else
-                v = t < a.T ? a.scores[t * a.E + e] : 0.0f;
-        }
-        sh.s_col[j][t] = v;
-    }
     if constexpr (!ROUTER) {
 #pragma unroll
         for (int i = 0; i < kMaxXLoads; ++i)
@@ -496,24 +522,29 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                 *reinterpret_cast<bf16x8 *>(&sh.xs[xs_chunk(q / cpr, q % cpr, cpr) * 8]) = xv[i];
             }
     }
-    __syncthreads();
 
     // ---- up: pre-activations of the member's rows over this wave's k quarter.
     // B = x^T (32 k x 16 tokens): lane (token l16 (+16), k group kgrp).
+    // x in LDS: staged from registers above when the scores are an input (the fused
+    // router staged it long ago); the score columns are read only after the next barrier
+    if constexpr (!ROUTER)
+        lds_barrier();
     f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-    if (rh * 16 < nrows) {
 #pragma unroll
-        for (int ks = 0; ks < kMaxKSteps; ++ks)
-            if (ks < KSU) {
-                const int c = (kq0 + ks * 32) / 8 + kgrp;
-                const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
-                const bf16x8 b1 =
-                    *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b0, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b1, acc1, 0, 0, 0);
-            }
-    }
+    for (int ks = 0; ks < kMaxKSteps; ++ks)
+        if (ks < KSU) {
+            const int c = (kq0 + ks * 32) / 8 + kgrp;
+            const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
+            const bf16x8 b1 =
+                *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b0, acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b1, acc1, 0, 0, 0);
+        }
+    if (tid < 2 * kTileM)
+        sh.s_col[tid / kTileM][tid % kTileM] = scv;
     // this wave is done with its W1: its share of the W2 half of the stream follows
+    // (requested together with W1 instead, W2 takes the CU's load path from W1 and the
+    // up products finish later). A step past the wave's range issues nothing.
     bf16x8 wb[kMaxDnSteps];
     {
         // element (column j, unit u) of the expert's W2: row-major, or tile (j / 16,
@@ -521,10 +552,11 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         const int lo = PACKED ? ((jt * 4 + ct) * (a.d_e >> 5)) * 512 + l16 * 32 + kgrp * 8
                               : (jt * kDnCols + ct * 16 + l16) * a.d_e + kgrp * 8;
 #pragma unroll
-        for (int i = 0; i < kMaxDnSteps; ++i)
-            wb[i] = has_dn && i < nsw
-                        ? bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2))
-                        : zero_bf16x8();
+        for (int i = 0; i < kMaxDnSteps; ++i) {
+            wb[i] = zero_bf16x8();
+            if (has_dn && i < nsw)
+                wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2));
+        }
     }
     // 16x16 accumulator layout: element i of a lane is row (lane/16)*4 + i of column
     // lane%16 (here: W1 row, token)
