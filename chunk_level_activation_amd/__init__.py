@@ -27,7 +27,8 @@ __all__ = [
     "blockffn_layer_forward", "blockffn_layer_forward_workspace_bytes",
     "blockffn_layer_forward_workspace", "blockffn_layer_forward_fused",
     "blockffn_pack_weights_bytes", "blockffn_pack_weights", "blockffn_layer_forward_packed",
-    "blockffn_last_error", "blockffn_version", "load_library",
+    "blockffn_init", "blockffn_workspace_check", "blockffn_last_error", "blockffn_version",
+    "load_library",
 ]
 
 BLOCKFFN_F32 = 0
@@ -35,7 +36,8 @@ BLOCKFFN_BF16 = 1
 # torch.nn.RMSNorm's default eps for fp32 (torch.finfo(torch.float32).eps).
 FP32_EPS = 1.1920928955078125e-07
 
-STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP"}
+STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EHIP",
+                5: "ETIMEOUT"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libblockffn.so")
@@ -96,12 +98,30 @@ def load_library():
     lib.blockffn_layer_forward_packed.argtypes = [P, P, P, P, F, P, I64, I64, I64, I64, I64, I, P,
                                                   P, P, ctypes.c_size_t, P]
     lib.blockffn_layer_forward_packed.restype = I
+    lib.blockffn_init.argtypes = [P]
+    lib.blockffn_init.restype = I
+    lib.blockffn_workspace_check.argtypes = [P, ctypes.c_size_t, P]
+    lib.blockffn_workspace_check.restype = I
     lib.blockffn_last_error.argtypes = []
     lib.blockffn_last_error.restype = ctypes.c_char_p
     lib.blockffn_version.argtypes = []
     lib.blockffn_version.restype = ctypes.c_char_p
     _lib = lib
     return lib
+
+
+def blockffn_init(stream=None) -> None:
+    """Probe the current device for the one-launch schedules (see blockffn.h); optional,
+    and to be called outside graph capture."""
+    _check(load_library().blockffn_init(_stream(stream)))
+
+
+def blockffn_workspace_check(workspace, stream=None) -> None:
+    """Raise BlockFFNError (status ETIMEOUT) if a kernel that used this workspace timed
+    out in one of its bounded waits; synchronises the stream (see blockffn.h)."""
+    _check(load_library().blockffn_workspace_check(
+        _dev(workspace, "workspace"), workspace.numel() * workspace.element_size(),
+        _stream(stream)))
 
 
 def blockffn_last_error() -> str:

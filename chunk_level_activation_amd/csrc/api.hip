@@ -15,7 +15,7 @@ namespace {
 
 thread_local std::string g_last_error;
 
-// Per-device facts some schedules depend on, found on first use.
+// Per-device facts some schedules depend on, found on first use (or by blockffn_init).
 struct DeviceInfo {
     bool probed = false;
     int xcds = 0;          // XCDs, when round-robin workgroup placement was verified
@@ -25,9 +25,34 @@ constexpr int kMaxDevices = 64;
 std::mutex g_device_mutex;
 DeviceInfo g_devices[kMaxDevices];
 
+// Probes the current device on `stream` (one small launch into a static device array,
+// then a synchronisation of `stream`). Caller holds g_device_mutex.
+hipError_t probe_device(int dev, hipStream_t stream, DeviceInfo &d)
+{
+    int nxcd = 0, cus = 0;
+    bool round_robin = false;
+    hipError_t err = hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev);
+    if (err == hipSuccess)
+        err = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (err != hipSuccess)
+        return err;
+    if (nxcd > 1 && nxcd <= blockffn::kMaxGroups && cus % nxcd == 0) {
+        err = blockffn::probe_xcd_placement(nxcd, stream, &round_robin);
+        if (err != hipSuccess)
+            return err;
+        if (round_robin) {
+            d.xcds = nxcd;
+            d.cus = cus;
+        }
+    }
+    d.probed = true;
+    return hipSuccess;
+}
+
 // Number of XCDs X of the current device if workgroup b of a launch is verified to
-// run on XCD b % X, else 0. The first call probes; the probe synchronises, so it is
-// skipped (and retried on a later call) while the stream is being captured into a
+// run on XCD b % X, else 0. The first call on a device probes it on the caller's
+// stream (see probe_device) unless blockffn_init did; the probe synchronises, so it
+// is skipped (and retried on a later call) while the stream is being captured into a
 // graph, and the call answers 0 meanwhile.
 const DeviceInfo *device_info(hipStream_t stream)
 {
@@ -41,17 +66,7 @@ const DeviceInfo *device_info(hipStream_t stream)
         if (hipStreamIsCapturing(stream, &cs) != hipSuccess ||
             cs != hipStreamCaptureStatusNone)
             return nullptr;
-        int nxcd = 0, cus = 0;
-        bool round_robin = false;
-        if (hipDeviceGetAttribute(&nxcd, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess &&
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) ==
-                hipSuccess &&
-            nxcd > 1 && nxcd <= blockffn::kMaxGroups && cus % nxcd == 0 &&
-            blockffn::probe_xcd_placement(nxcd, &round_robin) == hipSuccess && round_robin) {
-            d.xcds = nxcd;
-            d.cus = cus;
-        }
-        d.probed = true;
+        (void)probe_device(dev, stream, d);
     }
     return &d;
 }
@@ -175,7 +190,58 @@ extern "C" {
 
 const char *blockffn_last_error(void) { return g_last_error.c_str(); }
 
-const char *blockffn_version(void) { return "blockffn-gfx950 0.1.0"; }
+const char *blockffn_version(void) { return "blockffn-gfx950 0.2.0"; }
+
+blockffn_status_t blockffn_init(void *stream)
+{
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("no current device: ") + hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BLOCKFFN_EUNSUPPORTED, "device index beyond the library's table");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(s, &cs) != hipSuccess || cs != hipStreamCaptureStatusNone)
+        return fail(BLOCKFFN_EINVAL, "blockffn_init synchronises its stream: call it outside "
+                                     "graph capture");
+    {
+        std::lock_guard<std::mutex> lock(g_device_mutex);
+        DeviceInfo &d = g_devices[dev];
+        if (!d.probed && (err = probe_device(dev, s, d)) != hipSuccess)
+            return fail(BLOCKFFN_EHIP, std::string("placement probe failed: ") +
+                                           hipGetErrorString(err));
+    }
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
+
+blockffn_status_t blockffn_workspace_check(const void *workspace, size_t workspace_bytes,
+                                           void *stream)
+{
+    if (!workspace)
+        return fail(BLOCKFFN_EINVAL, "workspace must not be NULL");
+    if (!aligned(workspace, 256))
+        return fail(BLOCKFFN_EUNSUPPORTED, "workspace needs 256-byte alignment");
+    if (workspace_bytes < blockffn::kControlBytes)
+        return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                             " bytes, less than its control block (" +
+                                             std::to_string(blockffn::kControlBytes) + ")");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    uint32_t word = 0;
+    const uint32_t *src = static_cast<const uint32_t *>(workspace) + blockffn::kStatusWord;
+    hipError_t err = hipMemcpyAsync(&word, src, sizeof(word), hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess)
+        err = hipStreamSynchronize(s);
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("reading the status word: ") + hipGetErrorString(err));
+    if (word != 0)
+        return fail(BLOCKFFN_ETIMEOUT,
+                    "a kernel that used this workspace timed out waiting for other workgroups "
+                    "(its outputs are NaN); zero-fill the workspace before using it again");
+    g_last_error.clear();
+    return BLOCKFFN_OK;
+}
 
 size_t blockffn_router_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int dtype)
 {

@@ -315,31 +315,36 @@ ffn_bf16_down_kernel(FfnArgs a)
     down_item(a, item, s_list, cnt);
 }
 
-// Workgroup-to-XCD placement probe: records the XCD each workgroup ran on.
+// Workgroup-to-XCD placement probe: records the XCD each workgroup ran on, into a
+// static device array (each device holds its own copy for the life of the process; the
+// library allocates nothing for it).
+constexpr int kProbeBlocks = 4096;
+__device__ uint32_t g_xcd_probe[kProbeBlocks];
+
 __global__ void xcd_probe_kernel(uint32_t *out)
 {
     if (threadIdx.x == 0)
         out[blockIdx.x] = __builtin_amdgcn_s_getreg((31 << 11) | 20);   // HW_REG_XCC_ID
 }
 
-hipError_t probe_xcd_placement(int nxcd, bool *round_robin)
+hipError_t probe_xcd_placement(int nxcd, hipStream_t stream, bool *round_robin)
 {
-    constexpr int kBlocks = 4096;
-    uint32_t *buf = nullptr;
     *round_robin = false;
-    hipError_t err = hipMalloc(&buf, kBlocks * sizeof(uint32_t));
+    uint32_t *buf = nullptr;
+    hipError_t err = hipGetSymbolAddress(reinterpret_cast<void **>(&buf), HIP_SYMBOL(g_xcd_probe));
     if (err != hipSuccess)
         return err;
-    hipLaunchKernelGGL(xcd_probe_kernel, dim3(kBlocks), dim3(64), 0, 0, buf);
+    hipLaunchKernelGGL(xcd_probe_kernel, dim3(kProbeBlocks), dim3(64), 0, stream, buf);
     err = hipGetLastError();
-    static uint32_t host[kBlocks];
+    static uint32_t host[kProbeBlocks];
     if (err == hipSuccess)
-        err = hipMemcpy(host, buf, sizeof(host), hipMemcpyDeviceToHost);
-    (void)hipFree(buf);
+        err = hipMemcpyAsync(host, buf, sizeof(host), hipMemcpyDeviceToHost, stream);
+    if (err == hipSuccess)
+        err = hipStreamSynchronize(stream);
     if (err != hipSuccess)
         return err;
     bool ok = nxcd > 0;
-    for (int b = 0; b < kBlocks && ok; ++b)
+    for (int b = 0; b < kProbeBlocks && ok; ++b)
         ok = (int)(host[b] & 0xF) == b % nxcd;
     *round_robin = ok;
     return hipSuccess;

@@ -34,8 +34,9 @@
 // follows the group's size: one workgroup per up item where possible).
 // A down workgroup waits only on up workgroups of its own XCD with smaller indices,
 // which the in-order dispatcher has placed first, so every wait ends (it is bounded
-// anyway: on time-out the outputs of the tile become NaN). The cross-XCD sum and the
-// k-slice sum are done by whichever workgroup arrives last, which never waits. All
+// anyway: on time-out the outputs of the tile become NaN and the workspace's status
+// word is set). The cross-XCD sum and the k-slice sum are done by whichever workgroup
+// arrives last, which never waits. All
 // counters return to zero before the kernel ends; they live in the workspace's fixed
 // control block.
 #include "common.h"
@@ -67,6 +68,7 @@ struct Chunk1Args {
     uint32_t *up_done;      // [E]     finished hidden tiles per slot
     uint32_t *cons_done;    // [X]     down items done with the group's hidden rows
     uint32_t *dn_arrive;    // [JT]    group tiles stored per output tile
+    uint32_t *status;       // the workspace's status word: set when a wait times out
     uint64_t *masks_out;
     int32_t *lists_out;
     int32_t *counts_out;
@@ -282,6 +284,8 @@ __device__ void down_item(const Chunk1Args &a, const Rsrc &r, Shared &sh, int g,
     }
     __syncthreads();
     const bool timed_out = sh.flag != 0;
+    if (timed_out && tid == 0)
+        __hip_atomic_fetch_or(a.status, kStatusTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -489,6 +493,7 @@ hipError_t launch_ffn_bf16_chunk1(const FfnPlan &p, int xcds, int wg_per_xcd,
     a.up_done = a.up_arrive + p.E * a.RT;
     a.cons_done = a.up_done + p.E;
     a.dn_arrive = a.cons_done + kMaxGroups;
+    a.status = control + kStatusWord;
     a.masks_out = masks_out;
     a.lists_out = lists_out;
     a.counts_out = counts_out;

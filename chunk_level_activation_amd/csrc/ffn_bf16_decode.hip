@@ -40,7 +40,8 @@
 //   * The X group tiles of an output tile come from different XCDs: they go to
 //     memory with device-scope stores, and the last of the X to arrive (an atomic
 //     counter) adds them in group order and writes y.
-// Every wait is bounded: on time-out the affected outputs become NaN. Waits are on the
+// Every wait is bounded: on time-out the affected outputs become NaN and the
+// workspace's status word is set. Waits are on the
 // members of one group, which are all resident at once (one workgroup per CU, as many
 // members as the XCD has CUs). The group barrier uses per-member epoch flags that all
 // advance by one per call (from zero), the cross-XCD sum an arrival counter that
@@ -84,6 +85,7 @@ struct DecodeArgs {
     uint32_t *rflags;       // [X][P] per member: calls whose router logits it has stored
     float *logits;          // [X][E][32] router logits, one copy per group
     uint32_t *dn_arrive;    // [JT] group tiles stored per output tile
+    uint32_t *status;       // the workspace's status word: set when a wait times out
     uint64_t *masks_out;
     int32_t *lists_out;
     int32_t *counts_out;
@@ -611,6 +613,8 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     }
     __syncthreads();
     const bool timed_out = sh.flag != 0 || (ROUTER && sh.rflag != 0);
+    if (timed_out && tid == 0)
+        __hip_atomic_fetch_or(a.status, kStatusTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (!has_dn)
         return;
 
@@ -802,6 +806,9 @@ DecodeArgs decode_args(const FfnPlan &p, int xcds, int members, const uint16_t *
     a.dn_arrive = ctrl;
     a.flags = ctrl + kDecodeMaxJT;
     a.rflags = a.flags + kMaxGroups * kMaxMembers;
+    static_assert(kDecodeMaxJT + 2 * kMaxGroups * kMaxMembers == kDecodeControlEnd - kDecodeControlWord,
+                  "the control-block layout in plan.h");
+    a.status = reinterpret_cast<uint32_t *>(base) + kStatusWord;
     const size_t part = align_up((size_t)(p.d_h / kDnCols) * kMaxGroups * kTileM * kDnCols * 4, 256);
     a.logits = reinterpret_cast<float *>(base + p.off_partials + hidden + part);
     a.T = (int)p.T;

@@ -7,13 +7,24 @@
 
 namespace blockffn {
 
-// The workspace starts with a control block of fixed size. The one-launch bf16
-// kernel keeps its arrival counters there; every call returns the counters it used
-// to zero, so the block is all-zero between calls whatever sizes the calls have, and
-// a workspace zero-filled once stays valid. Scratch data always lies after the block.
+// The workspace starts with a control block of fixed size (64 KB of 32-bit words),
+// in three disjoint regions:
+//   words [0, kDecodeControlWord): the single-chunk schedule's arrival counters
+//       (ffn_bf16_chunk.hip); every call returns the ones it used to zero;
+//   words [kDecodeControlWord, kStatusWord): the decode schedule's arrival counters,
+//       which return to zero, and its per-member epoch flags, which count the calls
+//       made with this workspace and only ever increase (a zero-filled workspace
+//       starts them at a consistent state; the first word past them is
+//       kDecodeControlEnd);
+//   word kStatusWord: set to a non-zero value by a kernel whose bounded wait timed
+//       out (its outputs are then NaN); only zero-filling the workspace clears it.
+// A workspace zero-filled once therefore stays valid across calls of any sizes until
+// a wait times out. Scratch data always lies after the block.
 constexpr size_t kControlBytes = 64 * 1024;
 constexpr int64_t kControlWords = kControlBytes / sizeof(uint32_t);
-constexpr int64_t kMaxGroups = 16;   // XCDs the one-launch kernel may spread groups over
+constexpr int64_t kMaxGroups = 16;   // XCDs the one-launch kernels may spread groups over
+constexpr int64_t kStatusWord = kControlWords - 1;
+constexpr uint32_t kStatusTimedOut = 1u;
 
 // One-launch bf16 schedule for a single chunk tile (defined in ffn_bf16_chunk.hip).
 bool chunk1_supported(int64_t CT, int64_t d_h, int64_t d_e);
@@ -23,8 +34,17 @@ int chunk1_blocks_per_cu();
 // One-launch bf16 decode schedule, one workgroup per CU (ffn_bf16_decode.hip).
 // decode_shape(): sizes that may use it on some device (the workspace is sized for
 // it); decode_supported(): sizes usable with `xcds` groups of `members` workgroups.
-// Its counters start at this word of the control block.
+// Its counters and flags occupy words [kDecodeControlWord, kDecodeControlEnd) of the
+// control block: 32 output-tile counters, then two flag arrays of kMaxGroups x 64
+// members.
 constexpr int64_t kDecodeControlWord = kControlWords / 2;
+constexpr int64_t kDecodeControlEnd = kDecodeControlWord + 32 + 2 * kMaxGroups * 64;
+static_assert(kDecodeControlEnd <= kStatusWord, "the decode flags stay below the status word");
+// Words the single-chunk schedule uses for E experts of width d_e and d_h columns.
+inline int64_t chunk1_control_words(int64_t E, int64_t d_h, int64_t d_e)
+{
+    return E * (d_e / 128) + E + kMaxGroups + d_h / 64;
+}
 inline bool decode_shape(int dtype, int64_t CT, int64_t d_h, int64_t d_e)
 {
     return dtype == 1 && CT == 1 && d_h % 128 == 0 && d_h <= 2048 && d_e % 64 == 0 &&
@@ -72,7 +92,7 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     p.W = (E + 63) / 64;
     p.JT = (d_h + 31) / 32;
     p.chunk1 = dtype == 1 && chunk1_supported(p.CT, d_h, d_e) &&
-               E * (d_e / 64 + 1) + kMaxGroups + d_h / 64 <= kControlWords;
+               chunk1_control_words(E, d_h, d_e) <= kDecodeControlWord;
     p.decode = decode_shape(dtype, p.CT, d_h, d_e);
     p.grouped = dtype == 1 && grouped_supported(T, p.CT, d_h, E, d_e);
     const size_t helem = dtype == 1 ? 2 : 4;   // hidden activations: bf16 or fp32
@@ -156,8 +176,10 @@ hipError_t launch_router_bf16(const uint16_t *x, const uint16_t *w_r, const floa
                               const float *bias, float eps, int64_t T, int64_t d_h,
                               int64_t E, float *scores, float *logits, float sharpness,
                               float *probs, void *ws, int xcds, hipStream_t stream);
-// Checks that workgroup b of a launch runs on XCD b % nxcd (round-robin dispatch).
-hipError_t probe_xcd_placement(int nxcd, bool *round_robin);
+// Checks that workgroup b of a launch runs on XCD b % nxcd (round-robin dispatch): one
+// probe launch on `stream` into a static device array, then a synchronisation of that
+// stream. Allocates nothing.
+hipError_t probe_xcd_placement(int nxcd, hipStream_t stream, bool *round_robin);
 hipError_t launch_router_f32(const float *x, const float *w_r, const float *gain,
                              const float *bias, float eps, int64_t T, int64_t d_h,
                              int64_t E, float *scores, float *logits, float sharpness,

@@ -15,7 +15,14 @@
  *
  * Conventions shared by every call:
  *  - All array pointers are DEVICE pointers (hipMalloc / torch CUDA memory) owned by
- *    the caller. The library allocates, frees and retains nothing.
+ *    the caller. The library never allocates or frees device or pinned memory and
+ *    retains no caller pointer. It holds small static device arrays of its own (one
+ *    copy per device, for the life of the process) and, per device, the result of a
+ *    one-time probe of workgroup placement: blockffn_init() runs that probe
+ *    explicitly; otherwise the first call on a device runs it on the caller's stream
+ *    and synchronises that stream (skipped while the stream is being captured into a
+ *    graph: such calls then take the schedules that need no placement facts, and a
+ *    later call probes).
  *  - Arrays are dense, row-major, C-contiguous. Weights use the nn.Linear layout
  *    [out_features, in_features], stacked over experts.
  *  - `dtype` selects the element type of x, W_r, W1, W2 and y: BLOCKFFN_F32 (float)
@@ -46,7 +53,8 @@ typedef enum {
     BLOCKFFN_EINVAL = 1,        /* NULL required pointer, size <= 0, unknown dtype   */
     BLOCKFFN_EUNSUPPORTED = 2,  /* valid but outside the supported sizes/alignment   */
     BLOCKFFN_EWORKSPACE = 3,    /* workspace smaller than the query call returned    */
-    BLOCKFFN_EHIP = 4           /* the HIP runtime reported an error at launch       */
+    BLOCKFFN_EHIP = 4,          /* the HIP runtime reported an error                 */
+    BLOCKFFN_ETIMEOUT = 5       /* blockffn_workspace_check: a kernel's wait timed out */
 } blockffn_status_t;
 
 typedef enum { BLOCKFFN_F32 = 0, BLOCKFFN_BF16 = 1 } blockffn_dtype_t;
@@ -121,14 +129,21 @@ size_t blockffn_chunk_ffn_workspace_bytes(int64_t T, int64_t d_h, int64_t E,
  *                   second product and y is rounded to bf16 (nearest even).
  *   workspace, workspace_bytes: device scratch of at least
  *                   blockffn_chunk_ffn_workspace_bytes(...) bytes, ZERO-FILLED before
- *                   its first use (e.g. hipMemset or torch.zeros). It holds arrival
- *                   counters that every call returns to zero, so a zeroed workspace
- *                   stays valid across calls of any sizes; the rest of it is scratch.
- *                   Calls that may run concurrently need separate workspaces. A call
- *                   whose kernel times out waiting on its own work items (which only
- *                   a broken device or a workspace that was not zeroed can cause)
- *                   writes NaN to the affected rows of y; zero the workspace again
- *                   before reusing it.
+ *                   its first use (e.g. hipMemset or torch.zeros). Its first 64 KB
+ *                   are a control block: arrival counters that every call returns to
+ *                   zero, per-workgroup epoch flags that count the calls made with
+ *                   the workspace, and a status word; a zero-filled workspace stays
+ *                   valid across calls of any sizes. The rest of it is scratch.
+ *                   Calls that may run concurrently need separate workspaces.
+ *                   The single-chunk schedules (one launch whose workgroups hand work
+ *                   to each other) wait on workgroups of the same launch, which must
+ *                   all be resident at once (one per CU). A wait is bounded: if it
+ *                   times out, the affected rows of y become NaN and the workspace's
+ *                   status word is set, which blockffn_workspace_check reports. Causes:
+ *                   a workspace that was not zero-filled (or was reused after such a
+ *                   time-out), kernels of other streams or processes holding CUs so
+ *                   that the launch's workgroups are not co-resident, or a faulty
+ *                   device. After a time-out zero-fill the workspace before reusing it.
  *   union_masks_out   [C][ceil(E/64)] uint64 or NULL: bit e%64 of word e/64 set when
  *                   e is in U_c (C = ceil(T/n))
  *   expert_lists_out  [C][E] int32 or NULL: U_c in ascending expert id, then -1
@@ -154,7 +169,8 @@ size_t blockffn_layer_forward_workspace_bytes(int64_t T, int64_t d_h, int64_t E,
  * s = blockffn_router(x, W_r, gain, bias, eps). Arguments as in those two calls;
  * scores [T, E] float or NULL receives s. The workspace (at least
  * blockffn_layer_forward_workspace_bytes(...), 256-byte aligned) must be ZERO-FILLED
- * before its first use; every call returns its counters to zero. For one chunk of at
+ * before its first use; its control block then stays consistent across calls (as in
+ * blockffn_chunk_ffn, including the time-out behaviour and blockffn_workspace_check). For one chunk of at
  * most 32 tokens in bf16 with E <= 64 and d_h a multiple of 256 up to 2048 (and the
  * chunk FFN's single-chunk schedule available) the router runs inside the FFN launch:
  * the workgroups that share an XCD split the E logits between them (fp32 sums of bf16
@@ -310,6 +326,26 @@ blockffn_status_t blockffn_layer_backward(const void *x, const void *w_r, const 
                                           float *dw_r, float *dgain, float *dbias, float *dw1,
                                           float *dw2, void *workspace, size_t workspace_bytes,
                                           void *stream);
+
+/*
+ * Probes the current device for the facts some schedules need (workgroup-to-XCD
+ * placement: one small kernel launch on `stream` into a static device array, then a
+ * synchronisation of `stream`). Optional: without it the first call on a device does
+ * the same. Call it before capturing graphs, so that captured calls can use the
+ * one-launch schedules. BLOCKFFN_EINVAL while `stream` is being captured,
+ * BLOCKFFN_EHIP if the probe fails.
+ */
+blockffn_status_t blockffn_init(void *stream);
+
+/*
+ * Reports whether a kernel that used `workspace` (a chunk-FFN or layer-forward
+ * workspace, at least 64 KB) timed out in one of its bounded waits: synchronises
+ * `stream`, reads the workspace's status word and returns BLOCKFFN_OK (no time-out)
+ * or BLOCKFFN_ETIMEOUT (outputs of that call are NaN; zero-fill the workspace before
+ * using it again). Call it on the stream the workspace's calls ran on.
+ */
+blockffn_status_t blockffn_workspace_check(const void *workspace, size_t workspace_bytes,
+                                           void *stream);
 
 /* Message describing the calling thread's last non-OK status ("" if none). */
 const char *blockffn_last_error(void);

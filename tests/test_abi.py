@@ -278,3 +278,60 @@ def test_pack_weights_query_and_rejects(lib):
     assert p(FAKE, FAKE, 64, 2048, 128, 1, None, None) == 1
     assert p(FAKE, FAKE_ODD, 64, 2048, 128, 1, FAKE, None) == 2
     assert bf.blockffn_last_error() != ""
+
+
+def test_workspace_check_rejects_before_touching_the_device(lib):
+    assert lib.blockffn_workspace_check(None, 1 << 20, None) == 1          # EINVAL
+    assert lib.blockffn_workspace_check(FAKE_ODD, 1 << 20, None) == 2      # EUNSUPPORTED
+    assert lib.blockffn_workspace_check(FAKE, 4096, None) == 3             # EWORKSPACE
+    assert "control block" in bf.blockffn_last_error()
+    assert bf.STATUS_NAMES[5] == "ETIMEOUT"
+
+
+CONTROL_PROBE = r"""
+#include <cstdio>
+#include "plan.h"
+using namespace blockffn;
+int main()
+{
+    static_assert(kDecodeControlWord < kDecodeControlEnd && kDecodeControlEnd <= kStatusWord &&
+                  kStatusWord < kControlWords, "control regions in order");
+    const long Es[] = {1, 2, 16, 40, 64, 100, 128, 200, 250, 256};
+    const long des[] = {16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 65536};
+    const long dhs[] = {32, 128, 512, 1024, 2048, 4096, 8192, 16384};
+    const long Ts[] = {1, 32};
+    long checked = 0, chunk1 = 0;
+    for (long E : Es) for (long de : des) for (long dh : dhs) for (long T : Ts) {
+        const FfnPlan p = make_plan(T, dh, E, de, 32, 1);
+        ++checked;
+        if (p.chunk1) {
+            ++chunk1;
+            // the single-chunk schedule's counters stay below the decode region
+            if (chunk1_control_words(E, dh, de) > kDecodeControlWord) {
+                std::printf("overlap E=%ld d_e=%ld d_h=%ld\n", E, de, dh);
+                return 1;
+            }
+        }
+    }
+    std::printf("ok %ld %ld\n", checked, chunk1);
+    return 0;
+}
+"""
+
+
+def test_control_block_regions_are_disjoint(tmp_path):
+    """Every size the single-chunk schedule takes keeps its counters below the decode
+    schedule's flags, whose region ends below the status word (plan.h)."""
+    import subprocess
+    src = tmp_path / "control_probe.hip"
+    src.write_text(CONTROL_PROBE)
+    exe = tmp_path / "control_probe"
+    csrc = os.path.join(ROOT, "chunk_level_activation_amd", "csrc")
+    libdir = os.path.dirname(bf.library_path)
+    cmd = ["/opt/rocm/bin/hipcc", "--offload-arch=gfx950", "-O1", "-std=c++17", f"-I{csrc}",
+           str(src), "-o", str(exe), f"-L{libdir}", "-lblockffn", f"-Wl,-rpath,{libdir}"]
+    subprocess.run(cmd, check=True, capture_output=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert out.returncode == 0, out.stdout + out.stderr
+    checked, chunk1 = map(int, out.stdout.split()[1:3])
+    assert checked > 1000 and chunk1 > 0
