@@ -27,7 +27,7 @@ __all__ = [
     "blockffn_layer_forward", "blockffn_layer_forward_workspace_bytes",
     "blockffn_layer_forward_workspace", "blockffn_layer_forward_fused",
     "blockffn_pack_weights_bytes", "blockffn_pack_weights", "blockffn_layer_forward_packed",
-    "blockffn_init", "blockffn_workspace_check", "blockffn_last_error", "blockffn_version",
+    "blockffn_layer_forward_noalloc", "blockffn_init", "blockffn_workspace_check", "blockffn_last_error", "blockffn_version",
     "load_library",
 ]
 
@@ -98,6 +98,9 @@ def load_library():
     lib.blockffn_layer_forward_packed.argtypes = [P, P, P, P, F, P, I64, I64, I64, I64, I64, I, P,
                                                   P, P, ctypes.c_size_t, P]
     lib.blockffn_layer_forward_packed.restype = I
+    lib.blockffn_layer_forward_noalloc.argtypes = [P, P, P, P, F, P, P, I64, I64, I64, I64, I64,
+                                                   I, P, P, P]
+    lib.blockffn_layer_forward_noalloc.restype = I
     lib.blockffn_init.argtypes = [P]
     lib.blockffn_init.restype = I
     lib.blockffn_workspace_check.argtypes = [P, ctypes.c_size_t, P]
@@ -412,6 +415,29 @@ def blockffn_layer_forward(x, w_r, w1, w2, n: int, gain=None, bias=None, eps: fl
             _dev(scores, "scores", torch.float32), _dev(workspace, "workspace"),
             workspace.numel() * workspace.element_size(), _stream(stream)]
     _check(lib.blockffn_layer_forward(*args))
+    return y
+
+
+def blockffn_layer_forward_noalloc(x, w_r, w1, w2, n: int, gain=None, bias=None,
+                                   eps: float = FP32_EPS, *, y=None, scores=None, stream=None):
+    """blockffn_layer_forward with the library's own scratch array instead of a workspace,
+    for callers that cannot allocate (see blockffn.h); y must then be given by such
+    callers (it is allocated here only when omitted)."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    E, d_e, _ = w1.shape
+    if tuple(w_r.shape) != (E, d_h) or tuple(w2.shape) != (E, d_h, d_e):
+        raise ValueError("w_r must be [E, d_h], w2 [E, d_h, d_e]")
+    if w_r.dtype != x.dtype or w1.dtype != x.dtype or w2.dtype != x.dtype:
+        raise TypeError("x, w_r, w1 and w2 must share a dtype")
+    if y is None:
+        y = torch.empty_like(x)
+    args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
+            _dev(bias, "bias", torch.float32), float(eps), _dev(w1, "w1"), _dev(w2, "w2"),
+            T, d_h, E, d_e, int(n), _dtype_code(x), _dev(y, "y", x.dtype),
+            _dev(scores, "scores", torch.float32), _stream(stream)]
+    _check(lib.blockffn_layer_forward_noalloc(*args))
     return y
 
 

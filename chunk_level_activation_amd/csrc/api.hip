@@ -49,6 +49,42 @@ hipError_t probe_device(int dev, hipStream_t stream, DeviceInfo &d)
     return hipSuccess;
 }
 
+// The allocation-free entry point's scratch: one file-scope device array (each device
+// holds its own copy until the process ends). Host code uses only the per-device
+// address hipGetSymbolAddress returns for it, never the array's name. It starts
+// zero-filled (a static device array), which is the state the workspace protocol needs.
+constexpr size_t kNoallocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+void *g_scratch_ptr[kMaxDevices];
+
+// Resolves `scratch` on device `dev` (which must be current); once per device. Caller
+// holds g_device_mutex.
+hipError_t noalloc_scratch_init(int dev)
+{
+    if (g_scratch_ptr[dev])
+        return hipSuccess;
+    void *p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err == hipSuccess)
+        g_scratch_ptr[dev] = p;
+    return err;
+}
+
+// Before each allocation-free call: if an earlier call's bounded wait timed out (status
+// word set), the control block's flags are inconsistent, so it is zero-filled again
+// (counters, flags and status word). One workgroup; the word is read before any thread
+// writes.
+__global__ void __launch_bounds__(1024) scratch_recover_kernel(uint32_t *control)
+{
+    const uint32_t status = __hip_atomic_load(control + blockffn::kStatusWord, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    __syncthreads();
+    if (status == 0)
+        return;
+    for (int i = threadIdx.x; i < (int)blockffn::kControlWords; i += blockDim.x)
+        control[i] = 0u;
+}
+
 // Number of XCDs X of the current device if workgroup b of a launch is verified to
 // run on XCD b % X, else 0. The first call on a device probes it on the caller's
 // stream (see probe_device) unless blockffn_init did; the probe synchronises, so it
@@ -210,6 +246,9 @@ blockffn_status_t blockffn_init(void *stream)
         DeviceInfo &d = g_devices[dev];
         if (!d.probed && (err = probe_device(dev, s, d)) != hipSuccess)
             return fail(BLOCKFFN_EHIP, std::string("placement probe failed: ") +
+                                           hipGetErrorString(err));
+        if ((err = noalloc_scratch_init(dev)) != hipSuccess)
+            return fail(BLOCKFFN_EHIP, std::string("scratch array address: ") +
                                            hipGetErrorString(err));
     }
     g_last_error.clear();
@@ -694,6 +733,58 @@ blockffn_status_t blockffn_layer_forward_packed(const void *x, const void *w_r, 
         return fail(BLOCKFFN_EINVAL, "x, w_r, packed, y and workspace must not be NULL");
     return layer_forward(x, w_r, gain, bias, eps, nullptr, nullptr, packed, T, d_h, E, d_e, n,
                          dtype, y, scores, workspace, workspace_bytes, stream);
+}
+
+blockffn_status_t blockffn_layer_forward_noalloc(const void *x, const void *w_r, const float *gain,
+                                                 const float *bias, float eps, const void *w1,
+                                                 const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                                 int64_t d_e, int64_t n, int dtype, void *y,
+                                                 float *scores, void *stream)
+{
+    if (!w1 || !w2)
+        return fail(BLOCKFFN_EINVAL, "x, w_r, w1, w2 and y must not be NULL");
+    blockffn_status_t st = check_ffn_sizes(T, d_h, E, d_e, n, dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    const size_t need = layer_ws(T, d_h, E, d_e, n, dtype).total;
+    if (need > kNoallocScratchBytes)
+        return fail(BLOCKFFN_EUNSUPPORTED,
+                    "these sizes need " + std::to_string(need) + " bytes of scratch, more than "
+                    "the library's array of " + std::to_string(kNoallocScratchBytes) +
+                    " bytes; use blockffn_layer_forward with a workspace");
+    int dev = 0;
+    hipError_t err = hipGetDevice(&dev);
+    if (err != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("no current device: ") + hipGetErrorString(err));
+    if (dev < 0 || dev >= kMaxDevices)
+        return fail(BLOCKFFN_EUNSUPPORTED, "device index beyond the library's table");
+    void *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(g_device_mutex);
+        if ((err = noalloc_scratch_init(dev)) != hipSuccess)
+            return fail(BLOCKFFN_EHIP, std::string("scratch array address: ") +
+                                           hipGetErrorString(err));
+        ptr = g_scratch_ptr[dev];
+    }
+    // validate everything the workspace call checks before enqueueing anything
+    if (!x || !w_r || !y)
+        return fail(BLOCKFFN_EINVAL, "x, w_r, w1, w2 and y must not be NULL");
+    if (!(eps >= 0.0f))
+        return fail(BLOCKFFN_EINVAL, "eps must be >= 0");
+    const size_t ea = dtype == BLOCKFFN_BF16 ? 16 : 4;
+    if (!aligned(x, ea) || !aligned(w_r, ea) || !aligned(w1, ea) || !aligned(w2, ea) ||
+        !aligned(y, ea))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x, w_r, the weights and y must be " +
+                                               std::to_string(ea) + "-byte aligned");
+    if ((scores && !aligned(scores, 4)) || (gain && !aligned(gain, 4)) || (bias && !aligned(bias, 4)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "float arrays must be 4-byte aligned");
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipLaunchKernelGGL(scratch_recover_kernel, dim3(1), dim3(1024), 0, s,
+                       static_cast<uint32_t *>(ptr));
+    if ((err = hipGetLastError()) != hipSuccess)
+        return fail(BLOCKFFN_EHIP, std::string("scratch check launch failed: ") + hipGetErrorString(err));
+    return layer_forward(x, w_r, gain, bias, eps, w1, w2, nullptr, T, d_h, E, d_e, n, dtype, y,
+                         scores, ptr, kNoallocScratchBytes, stream);
 }
 
 }  // extern "C"

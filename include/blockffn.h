@@ -194,6 +194,26 @@ int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
                                  int dtype, void *stream);
 
 /*
+ * blockffn_layer_forward without a caller workspace, for callers that cannot allocate
+ * device memory (code under graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc). Same arguments, kernels and results as blockffn_layer_forward; the
+ * workspace is a file-scope device array of the library, 16 MiB, one per device (held
+ * until the process ends; its address is resolved by blockffn_init or by this call's
+ * first use on a device). Sizes whose blockffn_layer_forward_workspace_bytes(...)
+ * exceed 16 MiB are rejected with BLOCKFFN_EUNSUPPORTED before anything is enqueued
+ * (the decode chunk, d_h=2048 E=64 d_e=128 T=32 bf16, needs 8.7 MiB). Allocates and
+ * frees nothing. Each call first enqueues a one-workgroup kernel that zero-fills the
+ * array's control block if an earlier call's bounded wait timed out. Every call on a
+ * device shares that device's array: calls that may overlap on one device (other
+ * streams, other threads) race and must not be issued.
+ */
+blockffn_status_t blockffn_layer_forward_noalloc(const void *x, const void *w_r, const float *gain,
+                                                 const float *bias, float eps, const void *w1,
+                                                 const void *w2, int64_t T, int64_t d_h, int64_t E,
+                                                 int64_t d_e, int64_t n, int dtype, void *y,
+                                                 float *scores, void *stream);
+
+/*
  * Bytes of a packed copy of the expert weights (2*E*d_h*d_e bf16 elements), or 0 when
  * the sizes or dtype are not supported (bf16 only; 1 <= E <= 256; d_h and d_e positive
  * multiples of 32; E*d_h*d_e <= 2^30).
