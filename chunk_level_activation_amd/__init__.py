@@ -40,7 +40,10 @@ STATUS_NAMES = {0: "OK", 1: "EINVAL", 2: "EUNSUPPORTED", 3: "EWORKSPACE", 4: "EH
                 5: "ETIMEOUT"}
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-library_path = os.path.join(_HERE, "libblockffn.so")
+# BLOCKFFN_SANITIZE=1 selects the build whose host code runs under the address and
+# undefined-behaviour sanitizers (build_lib.py --sanitize); the kernels are the same.
+library_path = os.path.join(_HERE, "libblockffn_san.so" if os.environ.get("BLOCKFFN_SANITIZE") == "1"
+                            else "libblockffn.so")
 _lib = None
 
 

@@ -45,6 +45,26 @@ def build(verbose: bool = False, src: str = _SRC, out: str = _LIB_PATH) -> str:
     return out
 
 
+# A build with the address and undefined-behaviour sanitizers (clang, so that one
+# sanitizer runtime serves this library and the HIP library's host code in the same
+# process). Selected by BLOCKFFN_SANITIZE=1; see chunk_level_activation_amd.build_lib.
+_SAN_LIB_PATH = os.path.join(_HERE, "liboracle_san.so")
+_CLANG = "/opt/rocm/lib/llvm/bin/clang"
+
+
+def build_sanitized(verbose: bool = False, src: str = _SRC, out: str = _SAN_LIB_PATH) -> str:
+    """The same C file with -fsanitize=address,undefined (no recovery), for host-side
+    checking of the oracle's memory accesses and arithmetic."""
+    cmd = [_CLANG, "-O1", "-g", "-ffp-contract=off", "-fno-fast-math", "-fopenmp",
+           "-std=c11", "-Wall", "-Wextra", "-fsanitize=address,undefined",
+           "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-shared-libasan",
+           "-shared", "-fPIC", src, "-o", out, "-lm"]
+    if verbose:
+        print(" ".join(cmd))
+    subprocess.run(cmd, check=True)
+    return out
+
+
 _lib = None
 
 
@@ -60,6 +80,11 @@ def use_library(path: str | None):
 def _load():
     if _lib is not None:
         return _lib
+    if os.environ.get("BLOCKFFN_SANITIZE") == "1":
+        if not os.path.exists(_SAN_LIB_PATH) or (
+                os.path.getmtime(_SAN_LIB_PATH) < os.path.getmtime(_SRC)):
+            build_sanitized()
+        return _bind(ctypes.CDLL(_SAN_LIB_PATH))
     if not os.path.exists(_LIB_PATH) or (
             os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC)):
         build()
