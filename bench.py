@@ -545,7 +545,18 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws, 
     ln_b = torch.zeros(d_h, dtype=torch.float32, device=dev)
     out = torch.empty((T, d_h), dtype=torch.bfloat16, device=dev)
 
-    def layer_step(i):
+    probs = torch.empty((T, E), dtype=torch.float32, device=dev)
+    fws = bf.blockffn_layer_forward_full_workspace(T, d_h, E, cfg["d_e"], n, bf.BLOCKFFN_BF16, dev)
+
+    def layer_full(i):
+        w, k = copies[i % nc], i % S
+        wk = (dict(packed=w["packed"], E=E, d_e=cfg["d_e"]) if "packed" in w else
+              dict(w1=w["w1"], w2=w["w2"]))
+        bf.blockffn_layer_forward_full(xs[k], w["w_r"], n, gain=gain, bias=w["bias"],
+                                       ln_gamma=ln_g, ln_beta=ln_b, out=out, probs=probs,
+                                       sharpness=2.0, workspace=fws, **wk)
+
+    def layer_then_ln(i):
         w, k = copies[i % nc], i % S
         if "packed" in w:
             bf.blockffn_layer_forward_packed(xs[k], w["w_r"], w["packed"], E, cfg["d_e"], n,
@@ -555,10 +566,19 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws, 
                                       bias=w["bias"], y=y, workspace=lws)
         bf.blockffn_add_layernorm(y, xs[k], ln_g, ln_b, out=out)
 
-    g = capture(layer_step)
-    time_replays(g, wreplays)
-    layer_ms = time_replays(g, replays) / (replays * S)
-    del g
+    res = {}
+    for name, body, what in (
+            ("layer_with_epilogue", layer_full,
+             "blockffn_layer_forward_full: the layer step (as the headline) with the residual "
+             "LayerNorm and the router probabilities, fused into the one launch at the decode "
+             "chunk; same rotation as the headline step"),
+            ("layer_then_add_layernorm", layer_then_ln,
+             "the headline layer step followed by blockffn_add_layernorm (two launches)")):
+        g = capture(body)
+        time_replays(g, wreplays)
+        ms = time_replays(g, replays) / (replays * S)
+        del g
+        res[name] = {"what": what, "ms_per_step": ms, "tokens_per_s": T / (ms * 1e-3)}
 
     def rotating_ms(make, launch, bytes_per_set, launches=256):
         """Average duration of one launch over rotating input sets (>= 512 MiB)."""
@@ -575,11 +595,6 @@ def bench_extras(args, torch, np, bf, inputs, cfg, copies, xs, S, gain, y, lws, 
         del gr, data
         torch.cuda.empty_cache()
         return ms, sets
-
-    res = {"layer_with_epilogue": {
-        "what": "the layer step (as the headline) + residual LayerNorm, same rotation as "
-                "the headline step",
-        "ms_per_step": layer_ms, "tokens_per_s": T / (layer_ms * 1e-3)}}
 
     # residual + LayerNorm at the end-to-end token count
     T_ln = 4096

@@ -27,7 +27,8 @@ __all__ = [
     "blockffn_layer_forward", "blockffn_layer_forward_workspace_bytes",
     "blockffn_layer_forward_workspace", "blockffn_layer_forward_fused",
     "blockffn_pack_weights_bytes", "blockffn_pack_weights", "blockffn_layer_forward_packed",
-    "blockffn_layer_forward_noalloc", "blockffn_init", "blockffn_workspace_check", "blockffn_last_error", "blockffn_version",
+    "blockffn_layer_forward_full", "blockffn_layer_forward_full_workspace_bytes",
+    "blockffn_layer_forward_full_workspace", "blockffn_layer_forward_noalloc", "blockffn_init", "blockffn_workspace_check", "blockffn_last_error", "blockffn_version",
     "load_library",
 ]
 
@@ -101,6 +102,11 @@ def load_library():
     lib.blockffn_layer_forward_packed.argtypes = [P, P, P, P, F, P, I64, I64, I64, I64, I64, I, P,
                                                   P, P, ctypes.c_size_t, P]
     lib.blockffn_layer_forward_packed.restype = I
+    lib.blockffn_layer_forward_full_workspace_bytes.argtypes = [I64, I64, I64, I64, I64, I]
+    lib.blockffn_layer_forward_full_workspace_bytes.restype = ctypes.c_size_t
+    lib.blockffn_layer_forward_full.argtypes = [P, P, P, P, F, P, P, P, I64, I64, I64, I64, I64, I,
+                                                P, P, F, P, F, P, P, P, P, ctypes.c_size_t, P]
+    lib.blockffn_layer_forward_full.restype = I
     lib.blockffn_layer_forward_noalloc.argtypes = [P, P, P, P, F, P, P, I64, I64, I64, I64, I64,
                                                    I, P, P, P]
     lib.blockffn_layer_forward_noalloc.restype = I
@@ -419,6 +425,58 @@ def blockffn_layer_forward(x, w_r, w1, w2, n: int, gain=None, bias=None, eps: fl
             workspace.numel() * workspace.element_size(), _stream(stream)]
     _check(lib.blockffn_layer_forward(*args))
     return y
+
+
+def blockffn_layer_forward_full_workspace_bytes(T: int, d_h: int, E: int, d_e: int, n: int,
+                                                dtype: int) -> int:
+    nbytes = load_library().blockffn_layer_forward_full_workspace_bytes(T, d_h, E, d_e, n, dtype)
+    if nbytes == 0:
+        raise BlockFFNError(1, blockffn_last_error())
+    return int(nbytes)
+
+
+def blockffn_layer_forward_full_workspace(T: int, d_h: int, E: int, d_e: int, n: int,
+                                          dtype: int, device="cuda"):
+    """A zero-filled workspace for blockffn_layer_forward_full."""
+    import torch
+    return torch.zeros(blockffn_layer_forward_full_workspace_bytes(T, d_h, E, d_e, n, dtype),
+                       dtype=torch.uint8, device=device)
+
+
+def blockffn_layer_forward_full(x, w_r, n: int, *, w1=None, w2=None, packed=None, E=None,
+                                d_e=None, gain=None, bias=None, eps: float = FP32_EPS,
+                                ln_gamma=None, ln_beta=None, ln_eps: float = 1e-5, out=None,
+                                sharpness: float = 1.0, probs=None, y=None, scores=None,
+                                workspace=None, stream=None):
+    """out [T, d_h] = LayerNorm(layer FFN output + x), and probs = sigmoid(sharpness *
+    scores) when `probs` is given (see blockffn.h). Weights: w1/w2 row-major, or packed
+    (from blockffn_pack_weights) with E and d_e given."""
+    import torch
+    lib = load_library()
+    T, d_h = x.shape
+    if packed is None:
+        E, d_e, _ = w1.shape
+        if tuple(w2.shape) != (E, d_h, d_e):
+            raise ValueError("w2 must be [E, d_h, d_e]")
+    elif E is None or d_e is None:
+        raise ValueError("packed weights need E and d_e")
+    if tuple(w_r.shape) != (E, d_h):
+        raise ValueError("w_r must be [E, d_h]")
+    code = _dtype_code(x)
+    if out is None:
+        out = torch.empty_like(x)
+    if workspace is None:
+        workspace = blockffn_layer_forward_full_workspace(T, d_h, E, d_e, n, code, x.device)
+    args = [_dev(x, "x"), _dev(w_r, "w_r"), _dev(gain, "gain", torch.float32),
+            _dev(bias, "bias", torch.float32), float(eps), _dev(w1, "w1"), _dev(w2, "w2"),
+            _dev(packed, "packed"), T, d_h, E, d_e, int(n), code,
+            _dev(ln_gamma, "ln_gamma", torch.float32), _dev(ln_beta, "ln_beta", torch.float32),
+            float(ln_eps), _dev(out, "out", x.dtype), float(sharpness),
+            _dev(probs, "probs", torch.float32), _dev(y, "y", x.dtype),
+            _dev(scores, "scores", torch.float32), _dev(workspace, "workspace"),
+            workspace.numel() * workspace.element_size(), _stream(stream)]
+    _check(lib.blockffn_layer_forward_full(*args))
+    return out
 
 
 def blockffn_layer_forward_noalloc(x, w_r, w1, w2, n: int, gain=None, bias=None,

@@ -601,6 +601,14 @@ LayerWs layer_ws(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n, int 
 }
 }  // namespace
 
+namespace {
+// The full layer's y region (after the layer workspace) when the caller does not keep y.
+size_t layer_y_bytes(int64_t T, int64_t d_h, int dtype)
+{
+    return blockffn::align_up((size_t)T * (size_t)d_h * (dtype == BLOCKFFN_BF16 ? 2 : 4), 256);
+}
+}  // namespace
+
 size_t blockffn_layer_forward_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
                                               int64_t n, int dtype)
 {
@@ -623,25 +631,28 @@ int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
 }
 
 namespace {
-// Shared by blockffn_layer_forward (w1, w2 row-major; packed = NULL) and
-// blockffn_layer_forward_packed (w1 = w2 = NULL; packed in the tiled layout).
+// Shared by blockffn_layer_forward (w1, w2 row-major; packed = NULL),
+// blockffn_layer_forward_packed (w1 = w2 = NULL; packed in the tiled layout) and
+// blockffn_layer_forward_full (ep != NULL: the epilogue, validated by the caller; y may
+// then be NULL, and the workspace holds a y region after the layer's own part).
 blockffn_status_t layer_forward(const void *x, const void *w_r, const float *gain,
                                 const float *bias, float eps, const void *w1, const void *w2,
                                 const void *packed, int64_t T, int64_t d_h, int64_t E,
                                 int64_t d_e, int64_t n, int dtype, void *y, float *scores,
-                                void *workspace, size_t workspace_bytes, void *stream)
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                const blockffn::LayerEpilogue *ep = nullptr)
 {
     blockffn_status_t st = check_ffn_sizes(T, d_h, E, d_e, n, dtype);
     if (st != BLOCKFFN_OK)
         return st;
-    if (!x || !w_r || !(packed || (w1 && w2)) || !y || !workspace)
+    if (!x || !w_r || !(packed || (w1 && w2)) || !(y || ep) || !workspace)
         return fail(BLOCKFFN_EINVAL, packed ? "x, w_r, packed, y and workspace must not be NULL"
                                             : "x, w_r, w1, w2, y and workspace must not be NULL");
     if (!(eps >= 0.0f))
         return fail(BLOCKFFN_EINVAL, "eps must be >= 0");
     const size_t ea = dtype == BLOCKFFN_BF16 ? 16 : 4;
     if (!aligned(x, ea) || !aligned(w_r, ea) || (w1 && !aligned(w1, ea)) ||
-        (w2 && !aligned(w2, ea)) || (packed && !aligned(packed, ea)) || !aligned(y, ea))
+        (w2 && !aligned(w2, ea)) || (packed && !aligned(packed, ea)) || (y && !aligned(y, ea)))
         return fail(BLOCKFFN_EUNSUPPORTED, "x, w_r, the weights and y must be " +
                                                std::to_string(ea) + "-byte aligned");
     if ((scores && !aligned(scores, 4)) || (gain && !aligned(gain, 4)) || (bias && !aligned(bias, 4)))
@@ -649,9 +660,10 @@ blockffn_status_t layer_forward(const void *x, const void *w_r, const float *gai
     if (!aligned(workspace, 256))
         return fail(BLOCKFFN_EUNSUPPORTED, "workspace needs 256-byte alignment");
     const LayerWs L = layer_ws(T, d_h, E, d_e, n, dtype);
-    if (workspace_bytes < L.total)
+    const size_t need = ep ? L.total + layer_y_bytes(T, d_h, dtype) : L.total;
+    if (workspace_bytes < need)
         return fail(BLOCKFFN_EWORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                             " bytes, needs " + std::to_string(L.total));
+                                             " bytes, needs " + std::to_string(need));
     hipStream_t s = static_cast<hipStream_t>(stream);
     const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
     int xcds = 0, members = 0;
@@ -663,7 +675,7 @@ blockffn_status_t layer_forward(const void *x, const void *w_r, const float *gai
             p, xcds, members, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(w_r),
             gain, bias, eps, packed ? pw : static_cast<const uint16_t *>(w1),
             packed ? pw + E * d_e * d_h : static_cast<const uint16_t *>(w2), packed != nullptr,
-            static_cast<uint16_t *>(y), scores, workspace, s);
+            static_cast<uint16_t *>(y), scores, workspace, ep, s);
         if (err != hipSuccess)
             return fail(BLOCKFFN_EHIP, std::string("layer launch failed: ") + hipGetErrorString(err));
         g_last_error.clear();
@@ -674,12 +686,18 @@ blockffn_status_t layer_forward(const void *x, const void *w_r, const float *gai
                     "packed weights need the one-launch layer (blockffn_layer_forward_fused)");
     char *base = static_cast<char *>(workspace);
     float *sc = scores ? scores : reinterpret_cast<float *>(base + L.scores);
-    st = blockffn_router(x, w_r, gain, bias, eps, T, d_h, E, dtype, sc, nullptr, 1.0f, nullptr,
-                         base + L.router, workspace_bytes - L.router, stream);
+    st = blockffn_router(x, w_r, gain, bias, eps, T, d_h, E, dtype, sc, nullptr,
+                         ep ? ep->sharpness : 1.0f, ep ? ep->probs : nullptr, base + L.router,
+                         L.total - L.router, stream);
     if (st != BLOCKFFN_OK)
         return st;
-    return blockffn_chunk_ffn(x, sc, w1, w2, T, d_h, E, d_e, n, dtype, y, workspace, L.scores,
-                              nullptr, nullptr, nullptr, stream);
+    void *yb = y ? y : base + L.total;
+    st = blockffn_chunk_ffn(x, sc, w1, w2, T, d_h, E, d_e, n, dtype, yb, workspace, L.scores,
+                            nullptr, nullptr, nullptr, stream);
+    if (st != BLOCKFFN_OK || !ep)
+        return st;
+    return blockffn_add_layernorm(yb, x, ep->ln_gamma, ep->ln_beta, ep->ln_eps, T, d_h, dtype,
+                                  ep->ln_out, stream);
 }
 }  // namespace
 
@@ -733,6 +751,65 @@ blockffn_status_t blockffn_layer_forward_packed(const void *x, const void *w_r, 
         return fail(BLOCKFFN_EINVAL, "x, w_r, packed, y and workspace must not be NULL");
     return layer_forward(x, w_r, gain, bias, eps, nullptr, nullptr, packed, T, d_h, E, d_e, n,
                          dtype, y, scores, workspace, workspace_bytes, stream);
+}
+
+size_t blockffn_layer_forward_full_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                                   int64_t n, int dtype)
+{
+    if (check_ffn_sizes(T, d_h, E, d_e, n, dtype) != BLOCKFFN_OK)
+        return 0;
+    return layer_ws(T, d_h, E, d_e, n, dtype).total + layer_y_bytes(T, d_h, dtype);
+}
+
+blockffn_status_t blockffn_layer_forward_full(const void *x, const void *w_r, const float *gain,
+                                              const float *bias, float eps, const void *w1,
+                                              const void *w2, const void *packed, int64_t T,
+                                              int64_t d_h, int64_t E, int64_t d_e, int64_t n,
+                                              int dtype, const float *ln_gamma,
+                                              const float *ln_beta, float ln_eps, void *out,
+                                              float sharpness, float *probs, void *y,
+                                              float *scores, void *workspace,
+                                              size_t workspace_bytes, void *stream)
+{
+    blockffn_status_t st = check_ffn_sizes(T, d_h, E, d_e, n, dtype);
+    if (st != BLOCKFFN_OK)
+        return st;
+    if (!out)
+        return fail(BLOCKFFN_EINVAL, "out must not be NULL");
+    if ((packed != nullptr) == (w1 != nullptr || w2 != nullptr))
+        return fail(BLOCKFFN_EINVAL, "give either w1 and w2 (row-major) or packed, not both");
+    if (!(ln_eps >= 0.0f) || !std::isfinite(ln_eps))
+        return fail(BLOCKFFN_EINVAL, "ln_eps must be finite and >= 0");
+    if (probs && !std::isfinite(sharpness))
+        return fail(BLOCKFFN_EINVAL, "sharpness must be finite");
+    const int64_t vec = dtype == BLOCKFFN_BF16 ? 8 : 4;
+    if (d_h % vec != 0)
+        return fail(BLOCKFFN_EUNSUPPORTED, "d_h must be a multiple of " + std::to_string(vec));
+    if (!aligned(out, 16) || (ln_gamma && !aligned(ln_gamma, 16)) ||
+        (ln_beta && !aligned(ln_beta, 16)) || (probs && !aligned(probs, 4)) ||
+        !aligned(x, 16) || (y && !aligned(y, 16)))
+        return fail(BLOCKFFN_EUNSUPPORTED, "x, y, out, ln_gamma and ln_beta must be 16-byte "
+                                           "aligned, probs 4-byte aligned");
+    const size_t elem = dtype == BLOCKFFN_BF16 ? 2 : 4;
+    const size_t obytes = (size_t)T * (size_t)d_h * elem, pbytes = (size_t)T * (size_t)E * 4;
+    if (overlap(out, obytes, x, obytes) || (y && overlap(out, obytes, y, obytes)) ||
+        (scores && overlap(out, obytes, scores, pbytes)) ||
+        (probs && overlap(out, obytes, probs, pbytes)) ||
+        (probs && scores && overlap(probs, pbytes, scores, pbytes)))
+        return fail(BLOCKFFN_EINVAL, "out, probs and scores must not overlap x, y or each other");
+    blockffn::LayerEpilogue ep{ln_gamma, ln_beta, ln_eps, static_cast<uint16_t *>(out),
+                               sharpness, probs};
+    if (packed) {
+        hipStream_t s = static_cast<hipStream_t>(stream);
+        const blockffn::FfnPlan p = blockffn::make_plan(T, d_h, E, d_e, n, dtype);
+        int xcds = 0, members = 0;
+        if (!(p.decode && decode_grid(s, p, &xcds, &members) &&
+              blockffn::layer_decode_supported(E, d_h, members)))
+            return fail(BLOCKFFN_EUNSUPPORTED,
+                        "packed weights need the one-launch layer (blockffn_layer_forward_fused)");
+    }
+    return layer_forward(x, w_r, gain, bias, eps, w1, w2, packed, T, d_h, E, d_e, n, dtype, y,
+                         scores, workspace, workspace_bytes, stream, &ep);
 }
 
 blockffn_status_t blockffn_layer_forward_noalloc(const void *x, const void *w_r, const float *gain,

@@ -86,6 +86,17 @@ struct DecodeArgs {
     float *logits;          // [X][E][32] router logits, one copy per group
     uint32_t *dn_arrive;    // [JT] group tiles stored per output tile
     uint32_t *status;       // the workspace's status word: set when a wait times out
+    // fused epilogue (LN = true): ln_out = LayerNorm(bf16(y) + x) over d_h with ln_gamma,
+    // ln_beta (NULL = 1, 0) and ln_eps; y itself is written only when y != NULL
+    const float *ln_gamma, *ln_beta;
+    float ln_eps;
+    uint16_t *ln_out;
+    float *ln_stats;        // [JT][32 tokens][2]: each output tile's mean and squared deviations
+    uint32_t *ln_arrive;    // output tiles whose statistics are stored
+    uint32_t *ln_depart;    // output tiles done reading them (the last resets both to zero)
+    // router probabilities (ROUTER = true): probs_out [T][E] = sigmoid(sharpness * s)
+    float sharpness;
+    float *probs_out;
     uint64_t *masks_out;
     int32_t *lists_out;
     int32_t *counts_out;
@@ -202,6 +213,105 @@ __device__ __forceinline__ uint32_t hid_offset(int g, int lu, int t)
     return (uint32_t)((((g * (kGroupUnitsMax / 32) * 2 + frag) * kWave + ln) * 8 + (lu & 7)) * 2);
 }
 
+// Residual + LayerNorm of the layer output fused into the last step (skill page, "Full
+// BlockFFN Layer with Combined Losses": the layer returns LayerNorm(output + x) over
+// d_h). The owner of output tile jt (64 columns; the last group to arrive there) holds,
+// per thread, token tt and columns c0 .. c0 + 3 of y (rounded to bf16, as the unfused
+// layer stores it) and of x (xw, loaded with the group tiles). v = y + x; the 16 threads of a token reduce the tile's mean and sum
+// of squared deviations exactly (two passes over its 64 values) and store them; once the
+// statistics of all JT tiles are stored (a device-scope arrival count), each owner
+// combines the JT pairs of its tokens (equal-size parts: mean of the means, and the
+// squared deviations plus 64 times the squared offsets of the tile means), normalises
+// its columns and writes ln_out; the last owner to have read the statistics returns both
+// counters to zero. All JT owners are resident at once (the schedule's one workgroup
+// per CU), and the wait is bounded like the others (on time-out the columns become NaN
+// and the status word is set).
+__device__ void layernorm_tail(const DecodeArgs &a, int jt, int tt, int c0, const uint16_t (&yb)[4],
+                               const unsigned int (&xw)[2], bool timed_out)
+{
+    const __amdgpu_buffer_rsrc_t rst = make_rsrc(a.ln_stats, (uint64_t)a.JT * kTileM * 2 * 4);
+    const int col = jt * kDnCols + c0;
+    float v[4];
+    v[0] = bf16_to_f32(yb[0]) + bf16_to_f32((uint16_t)(xw[0] & 0xffffu));
+    v[1] = bf16_to_f32(yb[1]) + bf16_to_f32((uint16_t)(xw[0] >> 16));
+    v[2] = bf16_to_f32(yb[2]) + bf16_to_f32((uint16_t)(xw[1] & 0xffffu));
+    v[3] = bf16_to_f32(yb[3]) + bf16_to_f32((uint16_t)(xw[1] >> 16));
+    // the tile's statistics of token tt (16 threads x 4 columns)
+    const float tmean = row16_sum_f32((v[0] + v[1]) + (v[2] + v[3])) * (1.0f / kDnCols);
+    float m2 = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        m2 = fmaf(v[i] - tmean, v[i] - tmean, m2);
+    m2 = row16_sum_f32(m2);
+    if ((threadIdx.x & 15) == 0)
+        __builtin_amdgcn_raw_buffer_store_b64(
+            __builtin_bit_cast(unsigned int __attribute__((ext_vector_type(2))), make_float2(tmean, m2)),
+            rst, (int)((jt * kTileM + tt) * 2 * 4), 0, kSC1);
+    drain_memory();
+    __syncthreads();
+    __shared__ int ln_flag;
+    if (threadIdx.x == 0) {
+        add_counter(a.ln_arrive, 1u);
+        uint32_t spins = 0;
+        bool ready = false;
+        while (!ready && spins < kSpinLimit) {
+            ready = ld_counter(a.ln_arrive) >= (uint32_t)a.JT;
+            if (!ready) {
+                ++spins;
+                __builtin_amdgcn_s_sleep(1);
+            }
+        }
+        ln_flag = !ready;
+        if (!ready)
+            __hip_atomic_fetch_or(a.status, kStatusTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    __syncthreads();
+    // combine the JT tiles' statistics of token tt: thread (tt, i) loads tile i (and
+    // i + 16), the 16 threads of the token meet by row sums
+    const int i0 = threadIdx.x & 15;
+    float2 st[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int q = i0 + 16 * h;
+        st[h] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
+                                               rst, q < a.JT ? (int)((q * kTileM + tt) * 2 * 4) : (int)kOOB,
+                                               0, kSC1));
+    }
+    const float rjt = 1.0f / (float)a.JT;
+    const float mean = row16_sum_f32(st[0].x + st[1].x) * rjt;
+    float dev = 0.0f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+        if (i0 + 16 * h < a.JT) {
+            const float dm = st[h].x - mean;
+            dev += st[h].y + (float)kDnCols * dm * dm;
+        }
+    const float var = row16_sum_f32(dev) / (float)a.d_h;
+    const float inv = 1.0f / sqrtf(var + a.ln_eps);
+    const bool bad = timed_out || ln_flag != 0;
+    // every thread has its statistics (used above): depart
+    __syncthreads();
+    if (threadIdx.x == 0 && !bad) {
+        const uint32_t prev = add_counter(a.ln_depart, 1u);
+        if (prev == (uint32_t)(a.JT - 1)) {
+            st_counter(a.ln_arrive, 0u);
+            st_counter(a.ln_depart, 0u);
+        }
+    }
+    uint16_t o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float g = a.ln_gamma ? a.ln_gamma[col + i] : 1.0f;
+        const float b = a.ln_beta ? a.ln_beta[col + i] : 0.0f;
+        o[i] = f32_to_bf16(bad ? __builtin_nanf("") : (v[i] - mean) * inv * g + b);
+    }
+    if (tt < a.T) {
+        const uint64_t packed = (uint64_t)o[0] | ((uint64_t)o[1] << 16) | ((uint64_t)o[2] << 32) |
+                                ((uint64_t)o[3] << 48);
+        *reinterpret_cast<uint64_t *>(a.ln_out + (int64_t)tt * a.d_h + col) = packed;
+    }
+}
+
 // ROUTER = false: the scores are an input. ROUTER = true: the launch first computes
 // the router for the chunk itself (skill page, "Architecture Overview" and "Router
 // Architecture Setup": l = W_r x, s = RMSNorm_E(ReLU(l)) * gain), from the x every
@@ -218,7 +328,7 @@ __device__ __forceinline__ uint32_t hid_offset(int g, int lu, int t)
 // matrix as 16 x 32 tiles of 1 KB, rows and columns in order), so a wave's operand
 // load of 16 rows x 32 k is one contiguous 1 KB access (two runs when a piece's rows
 // do not start on a tile) instead of 16 separate 64-byte pieces.
-template <bool ROUTER, bool PACKED>
+template <bool ROUTER, bool PACKED, bool LN>
 __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs a)
 {
     __shared__ Shared sh;
@@ -407,6 +517,8 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                     scol_lds[e * kTileM + tt] = sc;
                     if (blockIdx.x == 0 && a.scores_out && tt < a.T)
                         a.scores_out[tt * a.E + e] = sc;
+                    if (blockIdx.x == 0 && a.probs_out && tt < a.T)
+                        a.probs_out[tt * a.E + e] = 1.0f / (1.0f + expf(-a.sharpness * sc));
                 }
             }
 #pragma unroll
@@ -684,7 +796,17 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     __syncthreads();
     if (!sh.last)
         return;
-    // last group tile of this output tile: add the X tiles in group order
+    // last group tile of this output tile: add the X tiles in group order (with the
+    // fused LayerNorm, the residual's x values are requested first, alongside)
+    unsigned int xw[2] = {0u, 0u};
+    if constexpr (LN) {
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)a.T * a.d_h * 2);
+        const int col = jt * kDnCols + c0;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            xw[h] = __builtin_amdgcn_raw_buffer_load_b32(
+                rx, tt < a.T ? (int)((tt * a.d_h + col + 2 * h) * 2) : (int)kOOB, 0, 0);
+    }
     float4 pv[kMaxGroups];
 #pragma unroll
     for (int q = 0; q < kMaxGroups; ++q)
@@ -700,12 +822,15 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             sum.z += pv[q].z;
             sum.w += pv[q].w;
         }
-    if (tt < a.T) {
-        const uint64_t packed = (uint64_t)f32_to_bf16(sum.x) | ((uint64_t)f32_to_bf16(sum.y) << 16) |
-                                ((uint64_t)f32_to_bf16(sum.z) << 32) |
-                                ((uint64_t)f32_to_bf16(sum.w) << 48);
+    const uint16_t yb[4] = {f32_to_bf16(sum.x), f32_to_bf16(sum.y), f32_to_bf16(sum.z),
+                            f32_to_bf16(sum.w)};
+    if (tt < a.T && (!LN || a.y)) {
+        const uint64_t packed = (uint64_t)yb[0] | ((uint64_t)yb[1] << 16) | ((uint64_t)yb[2] << 32) |
+                                ((uint64_t)yb[3] << 48);
         *reinterpret_cast<uint64_t *>(a.y + (int64_t)tt * a.d_h + jt * kDnCols + c0) = packed;
     }
+    if constexpr (LN)
+        layernorm_tail(a, jt, tt, c0, yb, xw, timed_out);
 }
 
 // The tiled weight layout: a row-major R x C bf16 matrix as (R/16) x (C/32) tiles of
@@ -765,22 +890,29 @@ size_t decode_scratch_bytes(int64_t d_h, int64_t d_e)
     const size_t hidden = (size_t)kMaxGroups * kGroupUnitsMax * kTileM * 2;
     const size_t part = (size_t)(d_h / kDnCols) * kMaxGroups * kTileM * kDnCols * 4;
     const size_t logits = (size_t)kMaxGroups * kMaxLayerE * kTileM * 4;
-    return align_up(hidden, 256) + align_up(part, 256) + logits;
+    const size_t ln_stats = (size_t)kDecodeMaxJT * kTileM * 2 * 4;
+    return align_up(hidden, 256) + align_up(part, 256) + align_up(logits, 256) + ln_stats;
 }
 
 int decode_blocks_per_cu()
 {
-    int nb = 0, nr = 0;
-    int np = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, ffn_bf16_decode_kernel<false, false>,
+    // every variant must fit one workgroup per CU
+    int occ[5] = {0, 0, 0, 0, 0};
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[0], ffn_bf16_decode_kernel<false, false, false>,
                                                      kThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&nr, ffn_bf16_decode_kernel<true, false>,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[1], ffn_bf16_decode_kernel<true, false, false>,
                                                      kThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&np, ffn_bf16_decode_kernel<true, true>,
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[2], ffn_bf16_decode_kernel<true, true, false>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[3], ffn_bf16_decode_kernel<true, false, true>,
+                                                     kThreads, 0) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[4], ffn_bf16_decode_kernel<true, true, true>,
                                                      kThreads, 0) != hipSuccess)
         return 0;
-    const int m = nb < nr ? nb : nr;
-    return m < np ? m : np;
+    int m = occ[0];
+    for (int i = 1; i < 5; ++i)
+        m = occ[i] < m ? occ[i] : m;
+    return m;
 }
 
 bool layer_decode_supported(int64_t E, int64_t d_h, int members)
@@ -806,11 +938,15 @@ DecodeArgs decode_args(const FfnPlan &p, int xcds, int members, const uint16_t *
     a.dn_arrive = ctrl;
     a.flags = ctrl + kDecodeMaxJT;
     a.rflags = a.flags + kMaxGroups * kMaxMembers;
-    static_assert(kDecodeMaxJT + 2 * kMaxGroups * kMaxMembers == kDecodeControlEnd - kDecodeControlWord,
+    a.ln_arrive = a.rflags + kMaxGroups * kMaxMembers;
+    a.ln_depart = a.ln_arrive + 1;
+    static_assert(kDecodeMaxJT + 2 * kMaxGroups * kMaxMembers + 2 == kDecodeControlEnd - kDecodeControlWord,
                   "the control-block layout in plan.h");
     a.status = reinterpret_cast<uint32_t *>(base) + kStatusWord;
     const size_t part = align_up((size_t)(p.d_h / kDnCols) * kMaxGroups * kTileM * kDnCols * 4, 256);
     a.logits = reinterpret_cast<float *>(base + p.off_partials + hidden + part);
+    const size_t logits = align_up((size_t)kMaxGroups * kMaxLayerE * kTileM * 4, 256);
+    a.ln_stats = reinterpret_cast<float *>(base + p.off_partials + hidden + part + logits);
     a.T = (int)p.T;
     a.d_h = (int)p.d_h;
     a.E = (int)p.E;
@@ -833,7 +969,7 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
     a.masks_out = masks_out;
     a.lists_out = lists_out;
     a.counts_out = counts_out;
-    hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false>), dim3((unsigned)(xcds * members)),
+    hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false, false>), dim3((unsigned)(xcds * members)),
                        dim3(kThreads), 0, stream, a);
     return hipGetLastError();
 }
@@ -842,7 +978,7 @@ hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, con
                                     const uint16_t *w_r, const float *gain, const float *bias,
                                     float eps, const uint16_t *w1, const uint16_t *w2,
                                     bool packed, uint16_t *y, float *scores_out, void *ws,
-                                    hipStream_t stream)
+                                    const LayerEpilogue *ep, hipStream_t stream)
 {
     DecodeArgs a = decode_args(p, xcds, members, x, w1, w2, y, ws);
     a.w_r = w_r;
@@ -850,12 +986,24 @@ hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, con
     a.bias = bias;
     a.eps = eps;
     a.scores_out = scores_out;
-    if (packed)
-        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, true>), dim3((unsigned)(xcds * members)),
-                           dim3(kThreads), 0, stream, a);
+    const bool ln = ep && ep->ln_out;
+    if (ep) {
+        a.ln_gamma = ep->ln_gamma;
+        a.ln_beta = ep->ln_beta;
+        a.ln_eps = ep->ln_eps;
+        a.ln_out = ep->ln_out;
+        a.sharpness = ep->sharpness;
+        a.probs_out = ep->probs;
+    }
+    const dim3 grid((unsigned)(xcds * members)), block(kThreads);
+    if (packed && ln)
+        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, true, true>), grid, block, 0, stream, a);
+    else if (packed)
+        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, true, false>), grid, block, 0, stream, a);
+    else if (ln)
+        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, false, true>), grid, block, 0, stream, a);
     else
-        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, false>), dim3((unsigned)(xcds * members)),
-                           dim3(kThreads), 0, stream, a);
+        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, false, false>), grid, block, 0, stream, a);
     return hipGetLastError();
 }
 

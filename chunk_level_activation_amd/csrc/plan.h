@@ -35,10 +35,10 @@ int chunk1_blocks_per_cu();
 // decode_shape(): sizes that may use it on some device (the workspace is sized for
 // it); decode_supported(): sizes usable with `xcds` groups of `members` workgroups.
 // Its counters and flags occupy words [kDecodeControlWord, kDecodeControlEnd) of the
-// control block: 32 output-tile counters, then two flag arrays of kMaxGroups x 64
-// members.
+// control block: 32 output-tile counters, two flag arrays of kMaxGroups x 64 members,
+// then the fused LayerNorm's arrival and departure counters.
 constexpr int64_t kDecodeControlWord = kControlWords / 2;
-constexpr int64_t kDecodeControlEnd = kDecodeControlWord + 32 + 2 * kMaxGroups * 64;
+constexpr int64_t kDecodeControlEnd = kDecodeControlWord + 32 + 2 * kMaxGroups * 64 + 2;
 static_assert(kDecodeControlEnd <= kStatusWord, "the decode flags stay below the status word");
 // Words the single-chunk schedule uses for E experts of width d_e and d_h columns.
 inline int64_t chunk1_control_words(int64_t E, int64_t d_h, int64_t d_e)
@@ -142,11 +142,21 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
 // scores_out [T][E] is written when given. packed: w1 and w2 are in the tiled layout
 // of launch_pack_weights.
 bool layer_decode_supported(int64_t E, int64_t d_h, int members);
+// The rest of the pages' layer around the FFN, fused into the one-launch layer when
+// given: ln_out = LayerNorm(y + x) (y rounded to bf16 first; NULL = no epilogue, and
+// y may then be NULL too) and probs = sigmoid(sharpness * scores) (NULL = none).
+struct LayerEpilogue {
+    const float *ln_gamma, *ln_beta;
+    float ln_eps;
+    uint16_t *ln_out;
+    float sharpness;
+    float *probs;
+};
 hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, const uint16_t *x,
                                     const uint16_t *w_r, const float *gain, const float *bias,
                                     float eps, const uint16_t *w1, const uint16_t *w2,
                                     bool packed, uint16_t *y, float *scores_out, void *ws,
-                                    hipStream_t stream);
+                                    const LayerEpilogue *ep, hipStream_t stream);
 // W1 [E][d_e][d_h] and W2 [E][d_h][d_e] (bf16) into packed = [W1 tiles][W2 tiles], each
 // matrix as 16 x 32 tiles of 1 KB in row-major tile order, row-major inside a tile.
 hipError_t launch_pack_weights(const uint16_t *w1, const uint16_t *w2, int64_t E, int64_t d_h,

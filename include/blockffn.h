@@ -194,6 +194,49 @@ int blockffn_layer_forward_fused(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
                                  int dtype, void *stream);
 
 /*
+ * Bytes of workspace blockffn_layer_forward_full needs (0 when the sizes are invalid).
+ */
+size_t blockffn_layer_forward_full_workspace_bytes(int64_t T, int64_t d_h, int64_t E, int64_t d_e,
+                                                   int64_t n, int dtype);
+
+/*
+ * The whole layer as the pages' layer module returns it (skill page, "Full BlockFFN
+ * Layer with Combined Losses": the output is LayerNorm(FFN output + layer input) and the
+ * router's probabilities come back with it; "Router Architecture Setup"):
+ *   y     = blockffn_layer_forward(x, W_r, gain, bias, eps, W1, W2, n)
+ *   out   = LayerNorm_{d_h}(y + x) * ln_gamma + ln_beta  (y as stored: bf16-rounded for
+ *           bf16; biased variance; as blockffn_add_layernorm)
+ *   probs = sigmoid(sharpness * scores)                  (when probs != NULL)
+ * Expert weights: either w1 and w2 row-major (packed = NULL) or packed as
+ * blockffn_pack_weights writes them (w1 = w2 = NULL; only for sizes where
+ * blockffn_layer_forward_fused(...) is 1, else BLOCKFFN_EUNSUPPORTED).
+ *
+ *   ln_gamma, ln_beta  [d_h] float or NULL (= 1, 0), 16-byte aligned; ln_eps finite >= 0
+ *   out     [T, d_h] dtype, written, 16-byte aligned; must not overlap x, y, scores, probs
+ *   sharpness, probs   [T, E] float or NULL, as in blockffn_router
+ *   y       [T, d_h] dtype or NULL: receives the FFN output when given
+ *   scores  [T, E] float or NULL: receives the router's scores when given
+ *   workspace, workspace_bytes: at least blockffn_layer_forward_full_workspace_bytes(...),
+ *           ZERO-FILLED before its first use, as blockffn_layer_forward's
+ * Where the router and FFN run in one launch (blockffn_layer_forward_fused), the residual
+ * LayerNorm and the probabilities run in that launch too: the workgroup that finishes an
+ * output tile adds x, computes the tile's per-token mean and squared deviations, and
+ * after every tile's have been stored (a bounded device-wide wait, under the same
+ * co-residency assumption and time-out reporting as the FFN's) combines them and writes
+ * its columns of out. Otherwise the call is blockffn_router (with probs),
+ * blockffn_chunk_ffn and blockffn_add_layernorm. d_h must be a multiple of 8 (bf16) or 4.
+ */
+blockffn_status_t blockffn_layer_forward_full(const void *x, const void *w_r, const float *gain,
+                                              const float *bias, float eps, const void *w1,
+                                              const void *w2, const void *packed, int64_t T,
+                                              int64_t d_h, int64_t E, int64_t d_e, int64_t n,
+                                              int dtype, const float *ln_gamma,
+                                              const float *ln_beta, float ln_eps, void *out,
+                                              float sharpness, float *probs, void *y,
+                                              float *scores, void *workspace,
+                                              size_t workspace_bytes, void *stream);
+
+/*
  * blockffn_layer_forward without a caller workspace, for callers that cannot allocate
  * device memory (code under graph capture, tight serving loops, harnesses that forbid
  * hipMalloc). Same arguments, kernels and results as blockffn_layer_forward; the

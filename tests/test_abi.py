@@ -335,3 +335,34 @@ def test_control_block_regions_are_disjoint(tmp_path):
     assert out.returncode == 0, out.stdout + out.stderr
     checked, chunk1 = map(int, out.stdout.split()[1:3])
     assert checked > 1000 and chunk1 > 0
+
+
+def full(lib, x=FAKE, w_r=FAKE, w1=FAKE, w2=FAKE, packed=None, T=32, d_h=2048, E=64, d_e=128,
+         n=32, dtype=1, ln_eps=1e-5, out=FAKE + 0x100000, sharpness=1.0, probs=None, y=None,
+         scores=None, ws=FAKE, ws_bytes=1 << 40):
+    return lib.blockffn_layer_forward_full(x, w_r, None, None, 1e-6, w1, w2, packed, T, d_h, E,
+                                           d_e, n, dtype, None, None, ln_eps, out, sharpness,
+                                           probs, y, scores, ws, ws_bytes, None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(out=None), 1),
+    (dict(packed=FAKE), 1),                       # both row-major and packed weights
+    (dict(w1=None, w2=None), 1),                  # neither
+    (dict(ln_eps=-1.0), 1),
+    (dict(ln_eps=float("inf")), 1),
+    (dict(probs=FAKE + 0x200000, sharpness=float("nan")), 1),
+    (dict(out=FAKE + 8), 2),                      # misaligned out
+    (dict(out=FAKE), 1),                          # out is x
+    (dict(ws_bytes=1024), 3),
+    (dict(T=0), 1),
+])
+def test_layer_forward_full_rejects(lib, kw, status):
+    assert full(lib, **kw) == status
+
+
+def test_layer_forward_full_workspace_query(lib):
+    a = lib.blockffn_layer_forward_full_workspace_bytes(32, 2048, 64, 128, 32, 1)
+    b = lib.blockffn_layer_forward_workspace_bytes(32, 2048, 64, 128, 32, 1)
+    assert a >= b + 32 * 2048 * 2
+    assert lib.blockffn_layer_forward_full_workspace_bytes(0, 2048, 64, 128, 32, 1) == 0

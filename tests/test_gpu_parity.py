@@ -11,7 +11,7 @@ import torch
 import chunk_level_activation_amd as bf
 import oracle
 from chunk_level_activation_amd import inputs
-from gpu_helpers import DEV, TOL_BF16, TOL_F32, dev, host, rel_err, sample_rows, tol, wdtype
+from gpu_helpers import DEV, TOL_BF16, TOL_F32, dev, host, rel_err, tol, wdtype
 
 pytestmark = pytest.mark.gpu
 
@@ -84,28 +84,28 @@ def test_decode_chunk_full(decode_draws, i):
     assert 16 < counts[0] < 60     # a sparse but non-trivial union
 
 
-def test_prefill_sampled():
-    """T=2048 = 64 chunks: unions in full, y on sampled rows."""
+def test_prefill_full():
+    """T=2048 = 64 chunks: unions and every row of y (the oracle's per-token form, which
+    equals its union-then-mask form bit for bit)."""
     inp = inputs.make_workload("prefill", seed=5)
     y, masks, lists, counts = run_ffn(inp)
     check_union(inp.scores, inp.n, masks, lists, counts)
-    rows = sample_rows(inp.T, inp.n, 96)
-    y_ref = oracle.token_ffn(inp.x[rows], inp.scores[rows], inp.w1, inp.w2)
-    assert rel_err(y[rows], y_ref) <= TOL_BF16
+    y_ref = oracle.token_ffn(inp.x, inp.scores, inp.w1, inp.w2)
+    assert rel_err(y, y_ref) <= TOL_BF16
 
 
 @pytest.mark.parametrize("tls,cls,dense", [(0.5, 0.3, False), (0.8, 0.7, False),
                                            (0.9, 0.85, False), (0.8, 0.7, True)])
-def test_large_layer_sweep_sampled(tls, cls, dense):
-    """d_h=4096, E=128 (two mask words), T=512: the sparsity sweep and all-active."""
+def test_large_layer_sweep_full(tls, cls, dense):
+    """d_h=4096, E=128 (two mask words), T=512: the sparsity sweep and all-active, every
+    row of y."""
     inp = inputs.make_workload("large", seed=7, tls=tls, cls=cls, dense=dense)
     y, masks, lists, counts = run_ffn(inp)
     check_union(inp.scores, inp.n, masks, lists, counts)
     if dense:
         assert np.all(counts == 128)
-    rows = sample_rows(inp.T, inp.n, 16 if dense else 64)
-    y_ref = oracle.token_ffn(inp.x[rows], inp.scores[rows], inp.w1, inp.w2)
-    assert rel_err(y[rows], y_ref) <= TOL_BF16
+    y_ref = oracle.token_ffn(inp.x, inp.scores, inp.w1, inp.w2)
+    assert rel_err(y, y_ref) <= TOL_BF16
 
 
 # ------------------------------------------------------------------ decode schedule
@@ -463,9 +463,11 @@ def test_router_all_negative_row():
 
 # ------------------------------------------------------------------ end to end
 
-def test_end_to_end_router_then_ffn_sampled():
-    """Router on the GPU feeds the GPU chunk FFN; compared on sampled rows with the
-    oracle's router feeding the oracle's FFN."""
+def test_end_to_end_router_then_ffn_full():
+    """Router on the GPU feeds the GPU chunk FFN; every row compared with the oracle's
+    router feeding the oracle's FFN. (Where a logit is within rounding of zero the two
+    routers may decide its activity differently; such a score is itself that small, so
+    its term stays far inside the tolerance.)"""
     inp = inputs.make_workload("e2e", seed=1)
     dt = torch.bfloat16
     x = dev(inp.x, dt)
@@ -473,9 +475,8 @@ def test_end_to_end_router_then_ffn_sampled():
     y = bf.blockffn_chunk_ffn(x, s, dev(inp.w1, dt), dev(inp.w2, dt), inp.n)
     torch.cuda.synchronize()
     _, s_ref = oracle.router(inp.x, inp.w_r, gain=inp.gain, bias=inp.bias)
-    rows = sample_rows(inp.T, inp.n, 64)
-    y_ref = oracle.token_ffn(inp.x[rows], s_ref[rows].astype(np.float32), inp.w1, inp.w2)
-    assert rel_err(host(y)[rows], y_ref) <= TOL_BF16
+    y_ref = oracle.token_ffn(inp.x, s_ref.astype(np.float32), inp.w1, inp.w2)
+    assert rel_err(host(y), y_ref) <= TOL_BF16
 
 
 def test_tiny_fp32_end_to_end():
