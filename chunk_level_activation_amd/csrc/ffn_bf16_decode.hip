@@ -63,7 +63,7 @@ constexpr int kMaxKSteps = 16;       // 32-wide k steps per up wave: d_h / 4 <= 
 constexpr int kGroupUnitsMax = 1024; // hidden units of the union per group
 constexpr int kMaxRows = 32;         // W1 rows (hidden units) per member
 constexpr int kDnCols = 64;          // output columns per member
-constexpr int kMaxDnSteps = kGroupUnitsMax / 32 / 2;   // 32-unit k steps per down wave
+constexpr int kDnSlots = 24;         // W2 steps a down wave holds in registers at once
 constexpr int kMaxWords = 4;
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kMaxDh = 2048;
@@ -607,26 +607,37 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         }
     }
 
-    // W2 as the A operand of the down products (16 columns x 32 units): wave (column
-    // quarter ct, half kh of the group's 32-unit steps); lane (column l16, k group
-    // kgrp) holds W2[e][64 jt + 16 ct + l16][u + 8 kgrp .. +8] for each step (slot e,
-    // first unit u; a step never crosses a slot since 32 divides d_e).
+    // The waves split into two roles after the up products. The up waves of the first
+    // row half (rh = 0: waves 0, 2, 4, 6) hold the piece's first 16 rows, which are
+    // always full; they apply Swish and the score, store the hidden rows, take part in
+    // the group barrier and copy the group's hidden block into LDS. The waves of the
+    // second row half (rh = 1), whose rows are few or none whenever |U| * d_e is not
+    // much more than 16 units per member, stream the member's whole W2 share right
+    // after their own (short) up products and compute all the down products: wave kq
+    // takes output-column quarter ct = kq over all of the group's 32-unit steps.
+    // Vector memory completes in order per wave, so W2 in flight on the rh = 1 waves
+    // never delays the hidden rows' drain or the barrier's polls on the rh = 0 waves.
+    // Lane (column l16, k group kgrp) of a down wave holds
+    // W2[e][64 jt + 16 ct + l16][u + 8 kgrp .. +8] for each step (slot e, first unit u;
+    // a step never crosses a slot since 32 divides d_e).
     const int jt = k;
     const bool has_dn = jt < a.JT;
-    const int ct = wave & 3, kh = wave >> 2;
-    const int nst = ng / 32;
-    const int st0 = kh ? (nst + 1) / 2 : 0;
-    const int nsw = kh ? nst / 2 : (nst + 1) / 2;
-    // lane i < kMaxDnSteps finds step i's expert and first unit (one LDS read for all
-    // steps); the loads themselves are issued once the up products have their W1, so
-    // the W1 half of the stream arrives first
+    const bool dn_wave = rh == 1;
+    const int ct = kq;
+    const int nst = ng / 32;                       // <= kGroupUnitsMax / 32 = 32
+    const int n0 = nst < kDnSlots ? nst : kDnSlots;
+    // lane i < nst finds step i's expert and first unit (one LDS read for all steps)
     int sbase = 0;
-    if (lane < kMaxDnSteps && lane < nsw) {
-        const int gu = G0 + (st0 + lane) * 32;
+    if (lane < nst) {
+        const int gu = G0 + lane * 32;
         const int sl = gu / a.d_e;
         const int unit = gu - sl * a.d_e;
         sbase = sh.list[sl] * a.d_h * a.d_e + (PACKED ? (unit >> 5) * 512 : unit);
     }
+    // element (column j, unit u) of the expert's W2: row-major, or tile (j / 16, u / 32)
+    // of the tiled layout (columns come in 16-aligned groups here)
+    const int lo = PACKED ? ((jt * 4 + ct) * (a.d_e >> 5)) * 512 + l16 * 32 + kgrp * 8
+                          : (jt * kDnCols + ct * 16 + l16) * a.d_e + kgrp * 8;
 
     if constexpr (!ROUTER) {
 #pragma unroll
@@ -656,21 +667,13 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         }
     if (tid < 2 * kTileM)
         sh.s_col[tid / kTileM][tid % kTileM] = scv;
-    // this wave is done with its W1: its share of the W2 half of the stream follows
-    // (requested together with W1 instead, W2 takes the CU's load path from W1 and the
-    // up products finish later). A step past the wave's range issues nothing.
-    bf16x8 wb[kMaxDnSteps];
-    {
-        // element (column j, unit u) of the expert's W2: row-major, or tile (j / 16,
-        // u / 32) of the tiled layout (columns come in 16-aligned groups here)
-        const int lo = PACKED ? ((jt * 4 + ct) * (a.d_e >> 5)) * 512 + l16 * 32 + kgrp * 8
-                              : (jt * kDnCols + ct * 16 + l16) * a.d_e + kgrp * 8;
+    // a down wave is done with its W1: its W2 share (the first kDnSlots steps) follows
+    bf16x8 wb[kDnSlots];
 #pragma unroll
-        for (int i = 0; i < kMaxDnSteps; ++i) {
-            wb[i] = zero_bf16x8();
-            if (has_dn && i < nsw)
-                wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2));
-        }
+    for (int i = 0; i < kDnSlots; ++i) {
+        wb[i] = zero_bf16x8();
+        if (dn_wave && has_dn && i < n0)
+            wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2));
     }
     // 16x16 accumulator layout: element i of a lane is row (lane/16)*4 + i of column
     // lane%16 (here: W1 row, token)
@@ -680,32 +683,38 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         sh.red[(kq * kTileM + row) * kRedPitch + l16] = acc0[i];
         sh.red[(kq * kTileM + row) * kRedPitch + l16 + 16] = acc1[i];
     }
-    __syncthreads();
-    // k quarters in order, Swish, score, bf16: thread -> (token tt, rows r0, r0 + 1),
-    // both of one slot (pieces start at even units and d_e is even)
-    {
-        const int tt = tid >> 4, r0 = (tid & 15) * 2;
-        if (r0 < nrows) {
-            const int j = M0 + r0 >= fsu ? 1 : 0;
-            float h[2];
+    lds_barrier();
+    // k quarters in order, Swish, score, bf16 (rh = 0 waves): thread u -> (token tt,
+    // rows r0 .. r0 + 3 as two pairs, each pair of one slot: pieces start at even units
+    // and d_e is even)
+    if (!dn_wave) {
+        const int u = (wave >> 1) * kWave + lane;
+        const int tt = u >> 3, r0 = (u & 7) * 4;
 #pragma unroll
-            for (int q = 0; q < 2; ++q) {
-                float sum = 0.0f;
+        for (int pr = 0; pr < 2; ++pr) {
+            const int r = r0 + 2 * pr;
+            if (r < nrows) {
+                const int j = M0 + r >= fsu ? 1 : 0;
+                float h[2];
 #pragma unroll
-                for (int p = 0; p < 4; ++p)
-                    sum += sh.red[(p * kTileM + r0 + q) * kRedPitch + tt];
-                h[q] = swish_fast(sum) * sh.s_col[j][tt];
+                for (int q = 0; q < 2; ++q) {
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int p = 0; p < 4; ++p)
+                        sum += sh.red[(p * kTileM + r + q) * kRedPitch + tt];
+                    h[q] = swish_fast(sum) * sh.s_col[j][tt];
+                }
+                const uint32_t off = hid_offset(g, M0 + r - G0, tt);
+                const uint32_t packed = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
+                __builtin_amdgcn_raw_buffer_store_b32(packed, rhid, (int)off, 0, kSC0);
             }
-            const uint32_t off = hid_offset(g, M0 + r0 - G0, tt);
-            const uint32_t packed = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-            __builtin_amdgcn_raw_buffer_store_b32(packed, rhid, (int)off, 0, kSC0);
         }
+        drain_memory();   // this wave's hidden rows are in the XCD's L2
     }
-    drain_memory();
-    __syncthreads();
+    lds_barrier();
 
     // ---- group barrier: every member's hidden rows are in the XCD's L2. Each member
-    // publishes the call's epoch in its own flag; the first wave polls all P flags.
+    // publishes the call's epoch in its own flag; the first wave (rh = 0) polls all P.
     if (tid == 0)
         xcd_flag_store(rflag, (uint32_t)((g * a.P + k) * 4), epoch);
     if (wave == 0) {
@@ -723,7 +732,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         if (lane == 0)
             sh.flag = !ready;
     }
-    __syncthreads();
+    lds_barrier();
     const bool timed_out = sh.flag != 0 || (ROUTER && sh.rflag != 0);
     if (timed_out && tid == 0)
         __hip_atomic_fetch_or(a.status, kStatusTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -731,60 +740,69 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         return;
 
     // ---- down: B = the hidden rows (32 units x 16 tokens): lane (token l16 (+16),
-    // k group kgrp) holds units 32 (st0 + i) + 8 kgrp .. +8 of the group's range. In the
-    // fragment order the group's block is ng / 16 fragments of 1 KB, each lane-contiguous:
-    // it is copied once into LDS over the x tile (which the up products are done with) by
-    // loads that write LDS, and the four column-quarter waves that use each fragment read
-    // it from there instead of each loading it from L2.
+    // k group kgrp) holds units 32 i + 8 kgrp .. +8 of the group's range for step i. In
+    // the fragment order the group's block is ng / 16 fragments of 1 KB, each
+    // lane-contiguous: the rh = 0 waves copy it once into LDS over the x tile (which the
+    // up products are done with) by loads that write LDS, and the four down waves read
+    // it from there.
     char *hs = reinterpret_cast<char *>(sh.xs);
     static_assert(kGroupUnitsMax / 16 * 1024 <= (int)sizeof(sh.xs), "the group's hidden block fits the x tile");
-    {
-        const int nfrag = (ng / 32) * 2;
+    if (!dn_wave) {
+        const int nfrag = nst * 2;
         const uint32_t gb = (uint32_t)(g * (kGroupUnitsMax / 32) * 2) * 1024u;
 #pragma unroll
-        for (int j = 0; j < kGroupUnitsMax / 16 / kWaves; ++j) {
-            const int f = j * kWaves + wave;
-            bload_lds16<kSC0>(rhid, hs + f * 1024, f < nfrag ? gb + (uint32_t)f * 1024u + lane * 16u : kOOB);
+        for (int jj = 0; jj < kGroupUnitsMax / 16 / (kWaves / 2); ++jj) {
+            const int f = jj * (kWaves / 2) + (wave >> 1);
+            if (f < nfrag)
+                bload_lds16<kSC0>(rhid, hs + f * 1024, gb + (uint32_t)f * 1024u + lane * 16u);
+        }
+        drain_memory();
+    }
+    lds_barrier();
+    if (dn_wave) {
+        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < kDnSlots; ++i)
+            if (i < n0) {
+                const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(hs + (i * 2) * 1024 + lane * 16);
+                const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(hs + (i * 2 + 1) * 1024 + lane * 16);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h1, acc1, 0, 0, 0);
+            }
+        // the steps past the first kDnSlots (unions of more than about 3/4 of E)
+        for (int i0 = kDnSlots; i0 < nst; i0 += kDnSlots) {
+#pragma unroll
+            for (int i = 0; i < kDnSlots; ++i) {
+                wb[i] = zero_bf16x8();
+                if (i0 + i < nst)
+                    wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i0 + i) + lo) * 2));
+            }
+#pragma unroll
+            for (int i = 0; i < kDnSlots; ++i)
+                if (i0 + i < nst) {
+                    const bf16x8 h0 =
+                        *reinterpret_cast<const bf16x8 *>(hs + ((i0 + i) * 2) * 1024 + lane * 16);
+                    const bf16x8 h1 =
+                        *reinterpret_cast<const bf16x8 *>(hs + ((i0 + i) * 2 + 1) * 1024 + lane * 16);
+                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h0, acc0, 0, 0, 0);
+                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h1, acc1, 0, 0, 0);
+                }
+        }
+        // group tile: element i of a lane is column ct*16 + kgrp*4 + i of token l16 (+16)
+#pragma unroll
+        for (int th = 0; th < 2; ++th) {
+            const f32x4 v = th ? acc1 : acc0;
+            const float4 o = timed_out ? make_float4(__builtin_nanf(""), __builtin_nanf(""),
+                                                     __builtin_nanf(""), __builtin_nanf(""))
+                                       : make_float4(v[0], v[1], v[2], v[3]);
+            bstore_f4<kSC1>(rdnp,
+                            (uint32_t)((((jt * a.X + g) * kTileM + l16 + 16 * th) * kDnCols + ct * 16 +
+                                        kgrp * 4) * 4),
+                            o);
         }
     }
-    __syncthreads();
-    bf16x8 hv[kMaxDnSteps][2];
-#pragma unroll
-    for (int i = 0; i < kMaxDnSteps; ++i)
-#pragma unroll
-        for (int th = 0; th < 2; ++th)
-            hv[i][th] = i < nsw ? *reinterpret_cast<const bf16x8 *>(hs + ((st0 + i) * 2 + th) * 1024 + lane * 16)
-                                : zero_bf16x8();
-    acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < kMaxDnSteps; ++i)
-        if (i < nsw) {
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], hv[i][0], acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], hv[i][1], acc1, 0, 0, 0);
-        }
-    // element i: column ct*16 + kgrp*4 + i, token l16 (+16)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int c = ct * 16 + kgrp * 4 + i;
-        sh.red[(kh * kDnCols + c) * kRedPitch + l16] = acc0[i];
-        sh.red[(kh * kDnCols + c) * kRedPitch + l16 + 16] = acc1[i];
-    }
-    __syncthreads();
-
-    // group tile: the 2 halves of the steps in order; thread -> (token tt, columns c0 .. +3)
     const int tt = tid >> 4, c0 = (tid & 15) * 4;
-    {
-        float o[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const float sum = sh.red[(c0 + q) * kRedPitch + tt] +
-                              sh.red[(kDnCols + c0 + q) * kRedPitch + tt];
-            o[q] = timed_out ? __builtin_nanf("") : sum;
-        }
-        bstore_f4<kSC1>(rdnp, (uint32_t)((((jt * a.X + g) * kTileM + tt) * kDnCols + c0) * 4),
-                        make_float4(o[0], o[1], o[2], o[3]));
-    }
     drain_memory();
     __syncthreads();
     if (tid == 0) {
