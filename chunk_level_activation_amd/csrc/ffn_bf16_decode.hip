@@ -83,7 +83,7 @@ struct DecodeArgs {
     float *dn_part;         // [JT][X][32][64] fp32 group tiles
     uint32_t *flags;        // [X][P] per member: calls whose hidden rows it has stored
     uint32_t *rflags;       // [X][P] per member: calls whose router logits it has stored
-    float *logits;          // [X][E][32] router logits, one copy per group
+    float *logits;          // [X][32 tokens][16][4] router logits (expert 16 i + j at [j][i]), one copy per group
     uint32_t *dn_arrive;    // [JT] group tiles stored per output tile
     uint32_t *status;       // the workspace's status word: set when a wait times out
     // fused epilogue (LN = true): ln_out = LayerNorm(bf16(y) + x) over d_h with ln_gamma,
@@ -430,18 +430,20 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         float *part = sh.red;                     // [8 k eighths][2 experts][32 tokens]
         {
             f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+            // branch-free, so that all the LDS reads go out before the first MFMA: steps
+            // past KS8 (d_h < 2048) re-read the last step with a zero A operand
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                if (j < KS8) {
-                    const int c = (wave * (a.d_h / 8) + j * 32) / 8 + kgrp;
-                    const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
-                    const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
-                    // A: rows 0 and 1 of the 16-row block are the member's W_r rows
-                    const bf16x8 wa_r = l16 < 2 ? *reinterpret_cast<const bf16x8 *>(&sh.wr[l16 * a.d_h + c * 8])
-                                                : zero_bf16x8();
-                    acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa_r, b0, acc0, 0, 0, 0);
-                    acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa_r, b1, acc1, 0, 0, 0);
-                }
+            for (int j = 0; j < 8; ++j) {
+                const int jc = j < KS8 ? j : KS8 - 1;
+                const int c = (wave * (a.d_h / 8) + jc * 32) / 8 + kgrp;
+                const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
+                const bf16x8 b1 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
+                // A: rows 0 and 1 of the 16-row block are the member's W_r rows
+                const bf16x8 wr = *reinterpret_cast<const bf16x8 *>(&sh.wr[(l16 & 1) * a.d_h + c * 8]);
+                const bf16x8 wa_r = (l16 < 2 && j < KS8) ? wr : zero_bf16x8();
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa_r, b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa_r, b1, acc1, 0, 0, 0);
+            }
             // element i: row (expert) kgrp*4 + i, token l16 (+16); rows 0 and 1 are kept
             if (kgrp == 0) {
 #pragma unroll
@@ -452,7 +454,9 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             }
         }
         __syncthreads();
-        const __amdgpu_buffer_rsrc_t rlg = make_rsrc(a.logits, (uint64_t)a.X * a.E * kTileM * 4);
+        // the group's logits in L2 as [token][e % 16][e / 16] (E <= 64): the 4 logits a
+        // thread needs below are one 16-byte piece
+        const __amdgpu_buffer_rsrc_t rlg = make_rsrc(a.logits, (uint64_t)a.X * kTileM * kMaxLayerE * 4);
         if (tid < 64) {
             const int el = tid >> 5, tok = tid & 31, e = e0 + el;
             float l = 0.0f;
@@ -460,7 +464,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             for (int q = 0; q < 8; ++q)
                 l += part[(q * 2 + el) * kTileM + tok];
             if (el < EPM && e < a.E)
-                bstore_f1<kSC0>(rlg, (uint32_t)(((g * a.E + e) * kTileM + tok) * 4), l);
+                bstore_f1<kSC0>(rlg, (uint32_t)(((g * kTileM + tok) * kMaxLayerE + (e & 15) * 4 + (e >> 4)) * 4), l);
         }
         drain_memory();
         __syncthreads();
@@ -491,13 +495,8 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
             // this thread's 4 logits from L2, then bias, ReLU, RMSNorm over the E experts,
             // gain; the scores go to LDS [e][token] (pitch kRedPitch) and to sv for the
             // union; tokens past T get 0
-            float lv[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int e = sub + 16 * i;
-                lv[i] = bload_f1<kSC0>(rlg, e < a.E ? (uint32_t)(((g * a.E + e) * kTileM + tt) * 4)
-                                                    : kOOB);
-            }
+            const float4 l4 = bload_f4<kSC0>(rlg, (uint32_t)(((g * kTileM + tt) * kMaxLayerE + sub * 4) * 4));
+            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
             float rv[4], sumsq = 0.0f;
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
