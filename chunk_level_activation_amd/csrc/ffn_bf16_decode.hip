@@ -91,9 +91,8 @@ struct DecodeArgs {
     const float *ln_gamma, *ln_beta;
     float ln_eps;
     uint16_t *ln_out;
-    float *ln_stats;        // [JT][32 tokens][2]: each output tile's mean and squared deviations
-    uint32_t *ln_arrive;    // output tiles whose statistics are stored
-    uint32_t *ln_depart;    // output tiles done reading them (the last resets both to zero)
+    uint32_t *ln_arrive;    // group tiles stored (all output tiles, all groups)
+    uint32_t *ln_depart;    // row owners done reading them (the last resets both to zero)
     // router probabilities (ROUTER = true): probs_out [T][E] = sigmoid(sharpness * s)
     float sharpness;
     float *probs_out;
@@ -213,103 +212,86 @@ __device__ __forceinline__ uint32_t hid_offset(int g, int lu, int t)
     return (uint32_t)((((g * (kGroupUnitsMax / 32) * 2 + frag) * kWave + ln) * 8 + (lu & 7)) * 2);
 }
 
-// Residual + LayerNorm of the layer output fused into the last step (skill page, "Full
+// Residual + LayerNorm of the layer output fused into the final sum (skill page, "Full
 // BlockFFN Layer with Combined Losses": the layer returns LayerNorm(output + x) over
-// d_h). The owner of output tile jt (64 columns; the last group to arrive there) holds,
-// per thread, token tt and columns c0 .. c0 + 3 of y (rounded to bf16, as the unfused
-// layer stores it) and of x (xw, loaded with the group tiles). v = y + x; the 16 threads of a token reduce the tile's mean and sum
-// of squared deviations exactly (two passes over its 64 values) and store them; once the
-// statistics of all JT tiles are stored (a device-scope arrival count), each owner
-// combines the JT pairs of its tokens (equal-size parts: mean of the means, and the
-// squared deviations plus 64 times the squared offsets of the tile means), normalises
-// its columns and writes ln_out; the last owner to have read the statistics returns both
-// counters to zero. All JT owners are resident at once (the schedule's one workgroup
-// per CU), and the wait is bounded like the others (on time-out the columns become NaN
-// and the status word is set).
-__device__ void layernorm_tail(const DecodeArgs &a, int jt, int tt, int c0, const uint16_t (&yb)[4],
-                               const unsigned int (&xw)[2], bool timed_out)
+// d_h). Once every member has stored its group tile (a device-scope arrival count over
+// all JT x X of them), the owner of token row t adds up the row's X group partials over
+// all d_h columns itself (thread -> 4 columns, the groups in order, as the per-tile sum
+// does), rounds y to bf16 (as the unfused layer stores it), adds x, and normalises the
+// row with its own exact two-pass mean and variance (wave sums, then the 8 waves in
+// order through LDS): the statistics never leave the workgroup. y is written only when
+// it is asked for.
+__device__ void layernorm_row(const DecodeArgs &a, __amdgpu_buffer_rsrc_t rdnp, float *red, int t,
+                              bool bad)
 {
-    const __amdgpu_buffer_rsrc_t rst = make_rsrc(a.ln_stats, (uint64_t)a.JT * kTileM * 2 * 4);
-    const int col = jt * kDnCols + c0;
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int c = tid * 4;
+    const bool act = c < a.d_h;
+    const int jt = c / kDnCols, cc = c % kDnCols;
+    float4 pv[kMaxGroups];
+#pragma unroll
+    for (int q = 0; q < kMaxGroups; ++q)
+        if (q < a.X)
+            pv[q] = bload_f4<kSC1>(rdnp, act ? (uint32_t)((((jt * a.X + q) * kTileM + t) * kDnCols + cc) * 4)
+                                             : kOOB);
+    uint2 xw = make_uint2(0u, 0u);
+    if (act && t < a.T)
+        xw = *reinterpret_cast<const uint2 *>(a.x + (int64_t)t * a.d_h + c);
+    float4 sum = pv[0];
+#pragma unroll
+    for (int q = 1; q < kMaxGroups; ++q)
+        if (q < a.X) {
+            sum.x += pv[q].x;
+            sum.y += pv[q].y;
+            sum.z += pv[q].z;
+            sum.w += pv[q].w;
+        }
+    const uint16_t yb[4] = {f32_to_bf16(sum.x), f32_to_bf16(sum.y), f32_to_bf16(sum.z),
+                            f32_to_bf16(sum.w)};
     float v[4];
-    v[0] = bf16_to_f32(yb[0]) + bf16_to_f32((uint16_t)(xw[0] & 0xffffu));
-    v[1] = bf16_to_f32(yb[1]) + bf16_to_f32((uint16_t)(xw[0] >> 16));
-    v[2] = bf16_to_f32(yb[2]) + bf16_to_f32((uint16_t)(xw[1] & 0xffffu));
-    v[3] = bf16_to_f32(yb[3]) + bf16_to_f32((uint16_t)(xw[1] >> 16));
-    // the tile's statistics of token tt (16 threads x 4 columns)
-    const float tmean = row16_sum_f32((v[0] + v[1]) + (v[2] + v[3])) * (1.0f / kDnCols);
-    float m2 = 0.0f;
+    v[0] = bf16_to_f32(yb[0]) + bf16_to_f32((uint16_t)(xw.x & 0xffffu));
+    v[1] = bf16_to_f32(yb[1]) + bf16_to_f32((uint16_t)(xw.x >> 16));
+    v[2] = bf16_to_f32(yb[2]) + bf16_to_f32((uint16_t)(xw.y & 0xffffu));
+    v[3] = bf16_to_f32(yb[3]) + bf16_to_f32((uint16_t)(xw.y >> 16));
+    // mean, then the squared deviations from it, over the row
+    float ps = act ? (v[0] + v[1]) + (v[2] + v[3]) : 0.0f;
+    ps = wave_sum_f32(ps);
+    if (lane == 0)
+        red[wave] = ps;
+    lds_barrier();
+    float tot = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+        tot += red[w];
+    const float mean = tot / (float)a.d_h;
+    float pd = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-        m2 = fmaf(v[i] - tmean, v[i] - tmean, m2);
-    m2 = row16_sum_f32(m2);
-    if ((threadIdx.x & 15) == 0)
-        __builtin_amdgcn_raw_buffer_store_b64(
-            __builtin_bit_cast(unsigned int __attribute__((ext_vector_type(2))), make_float2(tmean, m2)),
-            rst, (int)((jt * kTileM + tt) * 2 * 4), 0, kSC1);
-    drain_memory();
-    __syncthreads();
-    __shared__ int ln_flag;
-    if (threadIdx.x == 0) {
-        add_counter(a.ln_arrive, 1u);
-        uint32_t spins = 0;
-        bool ready = false;
-        while (!ready && spins < kSpinLimit) {
-            ready = ld_counter(a.ln_arrive) >= (uint32_t)a.JT;
-            if (!ready) {
-                ++spins;
-                __builtin_amdgcn_s_sleep(1);
-            }
-        }
-        ln_flag = !ready;
-        if (!ready)
-            __hip_atomic_fetch_or(a.status, kStatusTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __syncthreads();
-    // combine the JT tiles' statistics of token tt: thread (tt, i) loads tile i (and
-    // i + 16), the 16 threads of the token meet by row sums
-    const int i0 = threadIdx.x & 15;
-    float2 st[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        const int q = i0 + 16 * h;
-        st[h] = __builtin_bit_cast(float2, __builtin_amdgcn_raw_buffer_load_b64(
-                                               rst, q < a.JT ? (int)((q * kTileM + tt) * 2 * 4) : (int)kOOB,
-                                               0, kSC1));
-    }
-    const float rjt = 1.0f / (float)a.JT;
-    const float mean = row16_sum_f32(st[0].x + st[1].x) * rjt;
+        pd = fmaf(v[i] - mean, v[i] - mean, pd);
+    pd = wave_sum_f32(act ? pd : 0.0f);
+    if (lane == 0)
+        red[kWaves + wave] = pd;
+    lds_barrier();
     float dev = 0.0f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-        if (i0 + 16 * h < a.JT) {
-            const float dm = st[h].x - mean;
-            dev += st[h].y + (float)kDnCols * dm * dm;
-        }
-    const float var = row16_sum_f32(dev) / (float)a.d_h;
-    const float inv = 1.0f / sqrtf(var + a.ln_eps);
-    const bool bad = timed_out || ln_flag != 0;
-    // every thread has its statistics (used above): depart
-    __syncthreads();
-    if (threadIdx.x == 0 && !bad) {
-        const uint32_t prev = add_counter(a.ln_depart, 1u);
-        if (prev == (uint32_t)(a.JT - 1)) {
-            st_counter(a.ln_arrive, 0u);
-            st_counter(a.ln_depart, 0u);
-        }
-    }
-    uint16_t o[4];
+    for (int w = 0; w < kWaves; ++w)
+        dev += red[kWaves + w];
+    const float inv = 1.0f / sqrtf(dev / (float)a.d_h + a.ln_eps);
+    if (act && t < a.T) {
+        uint16_t o[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float g = a.ln_gamma ? a.ln_gamma[col + i] : 1.0f;
-        const float b = a.ln_beta ? a.ln_beta[col + i] : 0.0f;
-        o[i] = f32_to_bf16(bad ? __builtin_nanf("") : (v[i] - mean) * inv * g + b);
+        for (int i = 0; i < 4; ++i) {
+            const float gm = a.ln_gamma ? a.ln_gamma[c + i] : 1.0f;
+            const float bt = a.ln_beta ? a.ln_beta[c + i] : 0.0f;
+            o[i] = f32_to_bf16(bad ? __builtin_nanf("") : (v[i] - mean) * inv * gm + bt);
+        }
+        *reinterpret_cast<uint64_t *>(a.ln_out + (int64_t)t * a.d_h + c) =
+            (uint64_t)o[0] | ((uint64_t)o[1] << 16) | ((uint64_t)o[2] << 32) | ((uint64_t)o[3] << 48);
+        if (a.y)
+            *reinterpret_cast<uint64_t *>(a.y + (int64_t)t * a.d_h + c) =
+                (uint64_t)yb[0] | ((uint64_t)yb[1] << 16) | ((uint64_t)yb[2] << 32) | ((uint64_t)yb[3] << 48);
     }
-    if (tt < a.T) {
-        const uint64_t packed = (uint64_t)o[0] | ((uint64_t)o[1] << 16) | ((uint64_t)o[2] << 32) |
-                                ((uint64_t)o[3] << 48);
-        *reinterpret_cast<uint64_t *>(a.ln_out + (int64_t)tt * a.d_h + col) = packed;
-    }
+    lds_barrier();    // red is reused by the next row
 }
 
 // ROUTER = false: the scores are an input. ROUTER = true: the launch first computes
@@ -801,9 +783,45 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                             o);
         }
     }
-    const int tt = tid >> 4, c0 = (tid & 15) * 4;
     drain_memory();
     __syncthreads();
+    if constexpr (LN) {
+        // every member's group tile, then the token rows: member mid = k * X + g owns rows
+        // mid, mid + JT * X, ... (the first 32 members own one each at the decode shape)
+        const int NM = a.JT * a.X, mid = k * a.X + g;
+        const int owners = NM < kTileM ? NM : kTileM;
+        if (tid == 0)
+            add_counter(a.ln_arrive, 1u);
+        if (mid >= kTileM)
+            return;
+        if (tid == 0) {
+            uint32_t spins = 0;
+            bool ready = false;
+            while (!ready && spins < kSpinLimit) {
+                ready = ld_counter(a.ln_arrive) >= (uint32_t)NM;
+                if (!ready) {
+                    ++spins;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+            }
+            sh.last = !ready;
+            if (!ready)
+                __hip_atomic_fetch_or(a.status, kStatusTimedOut, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        const bool bad = timed_out || sh.last != 0;
+        for (int t = mid; t < kTileM; t += NM)
+            layernorm_row(a, rdnp, sh.red, t, bad);
+        // this owner has read the tiles: the last of the owners returns both counters to zero
+        if (tid == 0 && !bad) {
+            const uint32_t prev = add_counter(a.ln_depart, 1u);
+            if (prev == (uint32_t)(owners - 1)) {
+                st_counter(a.ln_arrive, 0u);
+                st_counter(a.ln_depart, 0u);
+            }
+        }
+        return;
+    }
     if (tid == 0) {
         const uint32_t prev = add_counter(&a.dn_arrive[jt], 1u);
         sh.last = prev == (uint32_t)(a.X - 1);
@@ -813,17 +831,8 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     __syncthreads();
     if (!sh.last)
         return;
-    // last group tile of this output tile: add the X tiles in group order (with the
-    // fused LayerNorm, the residual's x values are requested first, alongside)
-    unsigned int xw[2] = {0u, 0u};
-    if constexpr (LN) {
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)a.T * a.d_h * 2);
-        const int col = jt * kDnCols + c0;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-            xw[h] = __builtin_amdgcn_raw_buffer_load_b32(
-                rx, tt < a.T ? (int)((tt * a.d_h + col + 2 * h) * 2) : (int)kOOB, 0, 0);
-    }
+    // last group tile of this output tile: add the X tiles in group order
+    const int tt = tid >> 4, c0 = (tid & 15) * 4;
     float4 pv[kMaxGroups];
 #pragma unroll
     for (int q = 0; q < kMaxGroups; ++q)
@@ -841,13 +850,11 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         }
     const uint16_t yb[4] = {f32_to_bf16(sum.x), f32_to_bf16(sum.y), f32_to_bf16(sum.z),
                             f32_to_bf16(sum.w)};
-    if (tt < a.T && (!LN || a.y)) {
+    if (tt < a.T) {
         const uint64_t packed = (uint64_t)yb[0] | ((uint64_t)yb[1] << 16) | ((uint64_t)yb[2] << 32) |
                                 ((uint64_t)yb[3] << 48);
         *reinterpret_cast<uint64_t *>(a.y + (int64_t)tt * a.d_h + jt * kDnCols + c0) = packed;
     }
-    if constexpr (LN)
-        layernorm_tail(a, jt, tt, c0, yb, xw, timed_out);
 }
 
 // The tiled weight layout: a row-major R x C bf16 matrix as (R/16) x (C/32) tiles of
@@ -907,8 +914,7 @@ size_t decode_scratch_bytes(int64_t d_h, int64_t d_e)
     const size_t hidden = (size_t)kMaxGroups * kGroupUnitsMax * kTileM * 2;
     const size_t part = (size_t)(d_h / kDnCols) * kMaxGroups * kTileM * kDnCols * 4;
     const size_t logits = (size_t)kMaxGroups * kMaxLayerE * kTileM * 4;
-    const size_t ln_stats = (size_t)kDecodeMaxJT * kTileM * 2 * 4;
-    return align_up(hidden, 256) + align_up(part, 256) + align_up(logits, 256) + ln_stats;
+    return align_up(hidden, 256) + align_up(part, 256) + logits;
 }
 
 int decode_blocks_per_cu()
@@ -962,8 +968,6 @@ DecodeArgs decode_args(const FfnPlan &p, int xcds, int members, const uint16_t *
     a.status = reinterpret_cast<uint32_t *>(base) + kStatusWord;
     const size_t part = align_up((size_t)(p.d_h / kDnCols) * kMaxGroups * kTileM * kDnCols * 4, 256);
     a.logits = reinterpret_cast<float *>(base + p.off_partials + hidden + part);
-    const size_t logits = align_up((size_t)kMaxGroups * kMaxLayerE * kTileM * 4, 256);
-    a.ln_stats = reinterpret_cast<float *>(base + p.off_partials + hidden + part + logits);
     a.T = (int)p.T;
     a.d_h = (int)p.d_h;
     a.E = (int)p.E;
