@@ -60,8 +60,8 @@ static_assert(kWaves == 8, "the fused router splits d_h into eighths, one per wa
 constexpr int kMaxXLoads = 16;       // 16-byte x chunks per thread: d_h <= 2048
 constexpr int kMaxScoreLoads = 8;    // scores per thread (token tid/16, experts tid%16 + 16 i): E <= 128
 constexpr int kMaxKSteps = 16;       // 32-wide k steps per up wave: d_h / 4 <= 512
-constexpr int kGroupUnitsMax = 1024; // hidden units of the union per group
-constexpr int kMaxRows = 32;         // W1 rows (hidden units) per member
+constexpr int kGroupUnitsMax = 2048; // hidden units of the union per group (the block fills the x tile)
+constexpr int kMaxRows = 64;         // W1 rows (hidden units) per member: up to two passes of 32
 constexpr int kDnCols = 64;          // output columns per member
 constexpr int kDnSlots = 24;         // W2 steps a down wave holds in registers at once
 constexpr int kMaxWords = 4;
@@ -526,7 +526,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     }
     // The N = |U| * d_e hidden units of the union (slot-major) are split evenly: group
     // g takes the 32-unit-aligned range [G0, G1), member k of it the even-sized piece
-    // [M0, M0 + nrows). A member's piece spans at most 2 slots (nrows <= 32 <= d_e).
+    // [M0, M0 + nrows). A member's piece spans at most 2 slots (nrows <= 64 <= d_e).
     const int nblk = cnt * (a.d_e / 32);     // <= 1024 blocks: 32-bit products suffice
     const int G0 = 32 * (g * nblk / a.X);
     const int ng = 32 * ((g + 1) * nblk / a.X) - G0;
@@ -560,8 +560,10 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     const int KSU = a.d_h / 128;          // 32-wide k steps per quarter
     const int kq0 = kq * (a.d_h / 4);
     bf16x8 wa[kMaxKSteps];
-    {
-        const int row = rh * 16 + l16;
+    // rows [32 pass, 32 pass + 32) of the piece: a piece of more than 32 rows (large
+    // unions of wide experts) takes a second pass
+    auto issue_w1 = [&](int pass) {
+        const int row = pass * 32 + rh * 16 + l16;
         const bool vr = row < nrows;
         const int gu = M0 + row;
         const int sl = fs + (gu >= fsu ? 1 : 0);
@@ -581,12 +583,13 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
 #pragma unroll
         for (int ks = 0; ks < kMaxKSteps; ++ks)
             wa[ks] = zero_bf16x8();
-        if (rh * 16 < nrows && vr) {
+        if (pass * 32 + rh * 16 < nrows && vr) {
 #pragma unroll
             for (int ks = 0; ks < kMaxKSteps; ++ks)
                 wa[ks] = bload<kNT>(rw1, ks < KSU ? base + ks * kstride : kOOB);
         }
-    }
+    };
+    issue_w1(0);
 
     // The waves split into two roles after the up products. The up waves of the first
     // row half (rh = 0: waves 0, 2, 4, 6) hold the piece's first 16 rows, which are
@@ -605,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     const bool has_dn = jt < a.JT;
     const bool dn_wave = rh == 1;
     const int ct = kq;
-    const int nst = ng / 32;                       // <= kGroupUnitsMax / 32 = 32
+    const int nst = ng / 32;                       // <= kGroupUnitsMax / 32 = 64
     const int n0 = nst < kDnSlots ? nst : kDnSlots;
     // lane i < nst finds step i's expert and first unit (one LDS read for all steps)
     int sbase = 0;
@@ -635,64 +638,81 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     // router staged it long ago); the score columns are read only after the next barrier
     if constexpr (!ROUTER)
         lds_barrier();
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < kMaxKSteps; ++ks)
-        if (ks < KSU) {
-            const int c = (kq0 + ks * 32) / 8 + kgrp;
-            const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
-            const bf16x8 b1 =
-                *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b0, acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b1, acc1, 0, 0, 0);
-        }
-    if (tid < 2 * kTileM)
-        sh.s_col[tid / kTileM][tid % kTileM] = scv;
     // a down wave is done with its W1: its W2 share (the first kDnSlots steps) follows
     bf16x8 wb[kDnSlots];
+    auto issue_w2 = [&]() {
 #pragma unroll
-    for (int i = 0; i < kDnSlots; ++i) {
-        wb[i] = zero_bf16x8();
-        if (dn_wave && has_dn && i < n0)
-            wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2));
-    }
-    // 16x16 accumulator layout: element i of a lane is row (lane/16)*4 + i of column
-    // lane%16 (here: W1 row, token)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int row = rh * 16 + kgrp * 4 + i;
-        sh.red[(kq * kTileM + row) * kRedPitch + l16] = acc0[i];
-        sh.red[(kq * kTileM + row) * kRedPitch + l16 + 16] = acc1[i];
-    }
-    lds_barrier();
-    // k quarters in order, Swish, score, bf16 (rh = 0 waves): thread u -> (token tt,
-    // rows r0 .. r0 + 3 as two pairs, each pair of one slot: pieces start at even units
-    // and d_e is even)
-    if (!dn_wave) {
-        const int u = (wave >> 1) * kWave + lane;
-        const int tt = u >> 3, r0 = (u & 7) * 4;
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-            const int r = r0 + 2 * pr;
-            if (r < nrows) {
-                const int j = M0 + r >= fsu ? 1 : 0;
-                float h[2];
-#pragma unroll
-                for (int q = 0; q < 2; ++q) {
-                    float sum = 0.0f;
-#pragma unroll
-                    for (int p = 0; p < 4; ++p)
-                        sum += sh.red[(p * kTileM + r + q) * kRedPitch + tt];
-                    h[q] = swish_fast(sum) * sh.s_col[j][tt];
-                }
-                const uint32_t off = hid_offset(g, M0 + r - G0, tt);
-                const uint32_t packed = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
-                __builtin_amdgcn_raw_buffer_store_b32(packed, rhid, (int)off, 0, kSC0);
-            }
+        for (int i = 0; i < kDnSlots; ++i) {
+            wb[i] = zero_bf16x8();
+            if (dn_wave && has_dn && i < n0)
+                wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2));
         }
-        drain_memory();   // this wave's hidden rows are in the XCD's L2
+    };
+    // The products of one 32-row block of the piece (rows [pb, pb + 32)) from the W1 in
+    // wa, its k quarters added in order, Swish, score, bf16 hidden rows (rh = 0 waves).
+    // Thread u -> (token tt, rows r0 .. r0 + 3 of the block as two pairs, each pair of
+    // one slot: pieces start at even units and d_e is even).
+    auto up_block = [&](int pb, bool last) {
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < kMaxKSteps; ++ks)
+            if (ks < KSU) {
+                const int c = (kq0 + ks * 32) / 8 + kgrp;
+                const bf16x8 b0 = *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16, c, cpr) * 8]);
+                const bf16x8 b1 =
+                    *reinterpret_cast<const bf16x8 *>(&sh.xs[xs_chunk(l16 + 16, c, cpr) * 8]);
+                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b0, acc0, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa[ks], b1, acc1, 0, 0, 0);
+            }
+        if (pb == 0 && tid < 2 * kTileM)
+            sh.s_col[tid / kTileM][tid % kTileM] = scv;
+        if (last)
+            issue_w2();
+        // 16x16 accumulator layout: element i of a lane is row (lane/16)*4 + i of column
+        // lane%16 (here: W1 row, token)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int row = rh * 16 + kgrp * 4 + i;
+            sh.red[(kq * kTileM + row) * kRedPitch + l16] = acc0[i];
+            sh.red[(kq * kTileM + row) * kRedPitch + l16 + 16] = acc1[i];
+        }
+        lds_barrier();
+        if (!dn_wave) {
+            const int u = (wave >> 1) * kWave + lane;
+            const int tt = u >> 3, r0 = (u & 7) * 4;
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+                const int r = r0 + 2 * pr;
+                if (pb + r < nrows) {
+                    const int j = M0 + pb + r >= fsu ? 1 : 0;
+                    float h[2];
+#pragma unroll
+                    for (int q = 0; q < 2; ++q) {
+                        float sum = 0.0f;
+#pragma unroll
+                        for (int p = 0; p < 4; ++p)
+                            sum += sh.red[(p * kTileM + r + q) * kRedPitch + tt];
+                        h[q] = swish_fast(sum) * sh.s_col[j][tt];
+                    }
+                    const uint32_t off = hid_offset(g, M0 + pb + r - G0, tt);
+                    const uint32_t packed = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
+                    __builtin_amdgcn_raw_buffer_store_b32(packed, rhid, (int)off, 0, kSC0);
+                }
+            }
+            if (last)
+                drain_memory();   // this wave's hidden rows are in the XCD's L2
+        }
+        lds_barrier();
+    };
+    // a piece of more than 32 rows (large unions of wide experts) takes a first pass over
+    // its rows 0-31, then the W1 of rows 32-63; the last pass issues W2 as above
+    int pb = 0;
+    if (nrows > 32) {
+        up_block(0, false);
+        issue_w1(1);
+        pb = 32;
     }
-    lds_barrier();
+    up_block(pb, true);
 
     // ---- group barrier: every member's hidden rows are in the XCD's L2. Each member
     // publishes the call's epoch in its own flag; the first wave (rh = 0) polls all P.
@@ -741,8 +761,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     }
     lds_barrier();
     if (dn_wave) {
-        acc0 = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc1 = f32x4{0.f, 0.f, 0.f, 0.f};
+        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int i = 0; i < kDnSlots; ++i)
             if (i < n0) {

@@ -48,7 +48,7 @@ inline int64_t chunk1_control_words(int64_t E, int64_t d_h, int64_t d_e)
 inline bool decode_shape(int dtype, int64_t CT, int64_t d_h, int64_t d_e)
 {
     return dtype == 1 && CT == 1 && d_h % 128 == 0 && d_h <= 2048 && d_e % 64 == 0 &&
-           d_e <= 128;
+           d_e <= 256;
 }
 bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds, int members);
 size_t decode_scratch_bytes(int64_t d_h, int64_t d_e);

@@ -50,7 +50,7 @@ def _check(inp, g, b, n, y, s):
 
 
 CASES = [
-    # (label, seed, T, d_h, E, d_e, n, gain, bias): the first seven run fused
+    # (label, seed, T, d_h, E, d_e, n, gain, bias): the first NFUSED run fused
     ("decode chunk", 1, 32, 2048, 64, 128, 32, True, True),
     ("5 tokens", 2, 5, 2048, 64, 128, 32, True, True),
     ("one token", 3, 1, 2048, 64, 128, 32, True, True),
@@ -58,17 +58,19 @@ CASES = [
     ("E=16 d_h=1024 d_e=64", 5, 32, 1024, 16, 64, 32, True, True),
     ("no gain, no bias", 6, 32, 2048, 64, 128, 32, False, False),
     ("d_h=768", 10, 32, 768, 64, 128, 32, True, True),
+    ("d_e=256 (recommended E=40)", 9, 32, 2048, 40, 256, 32, True, True),
     # router + chunk FFN launches
     ("E=128", 7, 32, 2048, 128, 128, 32, True, True),
     ("multi-chunk T=256", 8, 256, 1024, 64, 128, 32, True, True),
-    ("d_e=256", 9, 32, 2048, 40, 256, 32, True, True),
+    ("d_e=512 (recommended E=40)", 12, 32, 2048, 40, 512, 32, True, True),
 ]
+NFUSED = 8
 
 
 @pytest.mark.parametrize("idx", range(len(CASES)), ids=[c[0] for c in CASES])
 def test_layer_forward(idx):
     label, seed, T, d_h, E, d_e, n, gain, bias = CASES[idx]
-    assert bf.blockffn_layer_forward_fused(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16) == (idx < 7)
+    assert bf.blockffn_layer_forward_fused(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16) == (idx < NFUSED)
     inp, g, b = _draw(seed, T, d_h, E, d_e, n, gain, bias)
     y, s = _run(inp, g, b, n)
     _check(inp, g, b, n, y, s)

@@ -123,11 +123,17 @@ DECODE = [
     ("E=8", 32, 8, 2048, 128, 0.5, 0.3, False),
     ("E=1", 32, 1, 2048, 128, 0.5, 0.3, False),
     ("E=40", 32, 40, 2048, 128, 0.8, 0.7, False),
+    # wide experts: pieces of more than 32 rows take a second pass (all active: 40 rows
+    # per member at E=40, 64 at E=64, whose group ranges fill the hidden block)
+    ("d_e=256", 32, 32, 2048, 256, 0.8, 0.7, False),
+    ("recommended E=40 d_e=256", 32, 40, 2048, 256, 0.8, 0.7, False),
+    ("recommended E=40 d_e=256 T=5", 5, 40, 2048, 256, 0.8, 0.7, False),
+    ("recommended E=40 d_e=256 all active", 32, 40, 2048, 256, 0.8, 0.7, True),
+    ("E=64 d_e=256 all active", 32, 64, 2048, 256, 0.8, 0.7, True),
+    ("d_e=256 d_h=1024 all active", 32, 64, 1024, 256, 0.8, 0.7, True),
     # sizes outside the one-workgroup-per-CU schedule (other single-chunk paths)
     ("d_h=4096", 32, 64, 4096, 128, 0.8, 0.7, False),
     ("E=128", 32, 128, 2048, 128, 0.8, 0.7, False),
-    ("d_e=256", 32, 32, 2048, 256, 0.8, 0.7, False),
-    ("recommended E=40 d_e=256", 32, 40, 2048, 256, 0.8, 0.7, False),
     ("recommended E=40 d_e=512", 32, 40, 2048, 512, 0.8, 0.7, False),
     ("recommended d_e=512 T=7", 7, 40, 2048, 512, 0.8, 0.7, False),
 ]
