@@ -24,19 +24,21 @@
 //     reads are conflict-free). A CU's load pipe handles contiguous accesses several
 //     times faster than the row-strided ones of MFMA operand layouts, and x is the
 //     one operand every CU reads whole.
-//   * Up: member k owns an even-sized piece (at most 32 units, at most 2 slots) of
-//     its group's range over the whole of d_h, so no split-k partial ever leaves the
-//     workgroup. Wave w = (16-row half rh, quarter kq of d_h): A = the W1
-//     rows (16 x 32 k, straight from memory into registers: 16 rows x 64 bytes per
-//     access), B = x from LDS, 16x16x32 MFMAs for both 16-token halves; the 4 k
-//     quarters meet in LDS and are added in order, then Swish and the score.
+//   * Up: member k owns an even-sized piece of its group's range (up to 32 units per
+//     pass, up to 3 passes for wide experts, at most 2 slots per pass) over the whole
+//     of d_h, so no split-k partial ever leaves the workgroup. Wave w = (16-row half
+//     rh, quarter kq of d_h): A = the W1 rows (16 x 32 k, straight from memory into
+//     registers: 16 rows x 64 bytes per access), B = x from LDS, 16x16x32 MFMAs for
+//     both 16-token halves; the 4 k quarters meet in LDS and are added in order, then
+//     Swish and the score.
 //   * Down: member k owns the 64 output columns [64k, 64k + 64) over its group's
-//     range. Its W2 block is loaded together with W1, right after the union, so both
-//     halves of the weight stream are in flight at once. Wave w = (16-column quarter
-//     ct, half kh of the range's 32-unit steps): A = W2 rows, B = the hidden rows from
-//     L2. After the group's barrier (per-member flags all P members set once their
-//     hidden rows are in L2) each wave loads its hidden operand and runs the MFMAs;
-//     the 2 halves meet in LDS.
+//     range. The waves of the second row half issue their W2 share right after their
+//     last W1 pass, so both halves of the weight stream are in flight at once, and
+//     compute every down product: wave kq takes the 16-column quarter kq over all of
+//     the range's 32-unit steps. After the group's barrier (per-member flags all P
+//     members set once their hidden rows are in L2) the first-half waves copy the
+//     group's hidden block into LDS (in chunks of 2048 units for the widest ranges)
+//     and the down waves run their MFMAs from it.
 //   * The X group tiles of an output tile come from different XCDs: they go to
 //     memory with device-scope stores, and the last of the X to arrive (an atomic
 //     counter) adds them in group order and writes y.
@@ -60,8 +62,9 @@ static_assert(kWaves == 8, "the fused router splits d_h into eighths, one per wa
 constexpr int kMaxXLoads = 16;       // 16-byte x chunks per thread: d_h <= 2048
 constexpr int kMaxScoreLoads = 8;    // scores per thread (token tid/16, experts tid%16 + 16 i): E <= 128
 constexpr int kMaxKSteps = 16;       // 32-wide k steps per up wave: d_h / 4 <= 512
-constexpr int kGroupUnitsMax = 2048; // hidden units of the union per group (the block fills the x tile)
-constexpr int kMaxRows = 64;         // W1 rows (hidden units) per member: up to two passes of 32
+constexpr int kGroupUnitsMax = 4096; // hidden units of the union per group (<= 128 32-unit steps)
+constexpr int kHidChunk = 64;        // 32-unit steps of the hidden block in LDS at once (fills the x tile)
+constexpr int kMaxRows = 96;         // W1 rows (hidden units) per member: up to three passes of 32
 constexpr int kDnCols = 64;          // output columns per member
 constexpr int kDnSlots = 24;         // W2 steps a down wave holds in registers at once
 constexpr int kMaxWords = 4;
@@ -79,7 +82,7 @@ struct DecodeArgs {
     const uint16_t *w1;
     const uint16_t *w2;
     uint16_t *y;
-    uint16_t *hidden;       // [X][kGroupUnitsMax / 32][2] fragments of 1 KB (bf16)
+    uint16_t *hidden;       // [X][gfrag] fragments of 1 KB (bf16)
     float *dn_part;         // [JT][X][32][64] fp32 group tiles
     uint32_t *flags;        // [X][P] per member: calls whose hidden rows it has stored
     uint32_t *rflags;       // [X][P] per member: calls whose router logits it has stored
@@ -107,6 +110,7 @@ struct DecodeArgs {
     float *scores_out;
     int T, d_h, E, d_e;
     int X, P;               // groups (XCDs), members per group
+    int gfrag;              // hidden fragments per group: 2 per 32 units of the largest group range
     int JT;                 // d_h / 64 output tiles
 };
 
@@ -205,11 +209,11 @@ __device__ __forceinline__ int xs_chunk(int t, int c, int chunks_per_row)
 // (lu / 32, t / 16) of 1 KB holds, at lane kgrp*16 + t%16, the 8 units 8*kgrp .. +8 of
 // its 32 (kgrp = (lu % 32) / 8), so each operand load of a down wave is one contiguous
 // access.
-__device__ __forceinline__ uint32_t hid_offset(int g, int lu, int t)
+__device__ __forceinline__ uint32_t hid_offset(int g, int gfrag, int lu, int t)
 {
     const int frag = (lu >> 5) * 2 + (t >> 4);
     const int ln = ((lu & 31) >> 3) * 16 + (t & 15);
-    return (uint32_t)((((g * (kGroupUnitsMax / 32) * 2 + frag) * kWave + ln) * 8 + (lu & 7)) * 2);
+    return (uint32_t)((((g * gfrag + frag) * kWave + ln) * 8 + (lu & 7)) * 2);
 }
 
 // Residual + LayerNorm of the layer output fused into the final sum (skill page, "Full
@@ -310,7 +314,12 @@ __device__ void layernorm_row(const DecodeArgs &a, __amdgpu_buffer_rsrc_t rdnp, 
 // matrix as 16 x 32 tiles of 1 KB, rows and columns in order), so a wave's operand
 // load of 16 rows x 32 k is one contiguous 1 KB access (two runs when a piece's rows
 // do not start on a tile) instead of 16 separate 64-byte pieces.
-template <bool ROUTER, bool PACKED, bool LN>
+//
+// WC (width class, for wide experts): 0 = pieces of at most 32 rows, group ranges of at
+// most 2048 units (one pass, the hidden block in LDS at once); 1 = pieces of up to 64
+// rows (a second pass); 2 = pieces of up to 96 rows and ranges of up to 4096 units (the
+// hidden block in LDS chunks of 2048 units). The lower classes keep the shorter code.
+template <bool ROUTER, bool PACKED, bool LN, int WC>
 __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs a)
 {
     __shared__ Shared sh;
@@ -326,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(a.w1, (uint64_t)a.E * a.d_e * a.d_h * 2);
     const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(a.w2, (uint64_t)a.E * a.d_h * a.d_e * 2);
     const __amdgpu_buffer_rsrc_t rhid =
-        make_rsrc(a.hidden, (uint64_t)a.X * kGroupUnitsMax * kTileM * 2);
+        make_rsrc(a.hidden, (uint64_t)a.X * a.gfrag * 1024);
     const __amdgpu_buffer_rsrc_t rdnp =
         make_rsrc(a.dn_part, (uint64_t)a.JT * a.X * kTileM * kDnCols * 4);
     const __amdgpu_buffer_rsrc_t rflag = make_rsrc(a.flags, (uint64_t)a.X * a.P * 4);
@@ -608,16 +617,30 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     const bool has_dn = jt < a.JT;
     const bool dn_wave = rh == 1;
     const int ct = kq;
-    const int nst = ng / 32;                       // <= kGroupUnitsMax / 32 = 64
+    const int nst = ng / 32;                       // <= kGroupUnitsMax / 32 = 128
     const int n0 = nst < kDnSlots ? nst : kDnSlots;
-    // lane i < nst finds step i's expert and first unit (one LDS read for all steps)
-    int sbase = 0;
-    if (lane < nst) {
-        const int gu = G0 + lane * 32;
-        const int sl = gu / a.d_e;
-        const int unit = gu - sl * a.d_e;
-        sbase = sh.list[sl] * a.d_h * a.d_e + (PACKED ? (unit >> 5) * 512 : unit);
+    // lane i finds step i's (sbase) and step 64 + i's (sbase2) expert and first unit
+    int sbase = 0, sbase2 = 0;
+    {
+        auto step_base = [&](int st) {
+            const int gu = G0 + st * 32;
+            const int sl = gu / a.d_e;
+            const int unit = gu - sl * a.d_e;
+            return sh.list[sl] * a.d_h * a.d_e + (PACKED ? (unit >> 5) * 512 : unit);
+        };
+        if (lane < nst)
+            sbase = step_base(lane);
+        if (WC == 2 && lane + 64 < nst)
+            sbase2 = step_base(lane + 64);
     }
+    // (wave-uniform st)
+    auto step_off = [&](int st) {
+        if constexpr (WC < 2)
+            return __builtin_amdgcn_readlane(sbase, st);
+        const int b1 = __builtin_amdgcn_readlane(sbase, st & 63);
+        const int b2 = __builtin_amdgcn_readlane(sbase2, st & 63);
+        return st < 64 ? b1 : b2;
+    };
     // element (column j, unit u) of the expert's W2: row-major, or tile (j / 16, u / 32)
     // of the tiled layout (columns come in 16-aligned groups here)
     const int lo = PACKED ? ((jt * 4 + ct) * (a.d_e >> 5)) * 512 + l16 * 32 + kgrp * 8
@@ -645,7 +668,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         for (int i = 0; i < kDnSlots; ++i) {
             wb[i] = zero_bf16x8();
             if (dn_wave && has_dn && i < n0)
-                wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i) + lo) * 2));
+                wb[i] = bload<kNT>(rw2, (uint32_t)((step_off(i) + lo) * 2));
         }
     };
     // The products of one 32-row block of the piece (rows [pb, pb + 32)) from the W1 in
@@ -694,7 +717,7 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
                             sum += sh.red[(p * kTileM + r + q) * kRedPitch + tt];
                         h[q] = swish_fast(sum) * sh.s_col[j][tt];
                     }
-                    const uint32_t off = hid_offset(g, M0 + pb + r - G0, tt);
+                    const uint32_t off = hid_offset(g, a.gfrag, M0 + pb + r - G0, tt);
                     const uint32_t packed = (uint32_t)f32_to_bf16(h[0]) | ((uint32_t)f32_to_bf16(h[1]) << 16);
                     __builtin_amdgcn_raw_buffer_store_b32(packed, rhid, (int)off, 0, kSC0);
                 }
@@ -704,13 +727,22 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
         }
         lds_barrier();
     };
-    // a piece of more than 32 rows (large unions of wide experts) takes a first pass over
-    // its rows 0-31, then the W1 of rows 32-63; the last pass issues W2 as above
+    // a piece of more than 32 rows (large unions of wide experts) takes passes over its
+    // rows 0-31 (and 32-63), each followed by the W1 of the next 32 rows; the last pass
+    // issues W2 as above
     int pb = 0;
-    if (nrows > 32) {
-        up_block(0, false);
-        issue_w1(1);
-        pb = 32;
+    if constexpr (WC == 1) {
+        if (nrows > 32) {
+            up_block(0, false);
+            issue_w1(1);
+            pb = 32;
+        }
+    } else if constexpr (WC == 2) {
+        while (nrows - pb > 32) {
+            up_block(pb, false);
+            issue_w1((pb >> 5) + 1);
+            pb += 32;
+        }
     }
     up_block(pb, true);
 
@@ -743,52 +775,99 @@ __global__ void __launch_bounds__(kThreads, 1) ffn_bf16_decode_kernel(DecodeArgs
     // ---- down: B = the hidden rows (32 units x 16 tokens): lane (token l16 (+16),
     // k group kgrp) holds units 32 i + 8 kgrp .. +8 of the group's range for step i. In
     // the fragment order the group's block is ng / 16 fragments of 1 KB, each
-    // lane-contiguous: the rh = 0 waves copy it once into LDS over the x tile (which the
-    // up products are done with) by loads that write LDS, and the four down waves read
-    // it from there.
+    // lane-contiguous: the rh = 0 waves copy it into LDS over the x tile (which the up
+    // products are done with) by loads that write LDS, up to 64 steps (128 KB) at a
+    // time, and the four down waves read it from there.
     char *hs = reinterpret_cast<char *>(sh.xs);
-    static_assert(kGroupUnitsMax / 16 * 1024 <= (int)sizeof(sh.xs), "the group's hidden block fits the x tile");
-    if (!dn_wave) {
-        const int nfrag = nst * 2;
-        const uint32_t gb = (uint32_t)(g * (kGroupUnitsMax / 32) * 2) * 1024u;
-#pragma unroll
-        for (int jj = 0; jj < kGroupUnitsMax / 16 / (kWaves / 2); ++jj) {
-            const int f = jj * (kWaves / 2) + (wave >> 1);
-            if (f < nfrag)
-                bload_lds16<kSC0>(rhid, hs + f * 1024, gb + (uint32_t)f * 1024u + lane * 16u);
+    static_assert(kHidChunk * 2 * 1024 <= (int)sizeof(sh.xs), "a chunk of the hidden block fits the x tile");
+    const uint32_t gb = (uint32_t)(g * a.gfrag) * 1024u;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    if constexpr (WC == 2) {
+        // the group's steps in LDS chunks of kHidChunk (one chunk unless the group range
+        // exceeds 2048 units)
+        for (int c0 = 0; c0 < nst; c0 += kHidChunk) {
+            const int cend = nst < c0 + kHidChunk ? nst : c0 + kHidChunk;
+            if (c0 > 0)
+                lds_barrier();   // the down waves are done with the previous chunk
+            if (!dn_wave) {
+                const int nfrag = (cend - c0) * 2;
+    #pragma unroll
+                for (int jj = 0; jj < kHidChunk * 2 / (kWaves / 2); ++jj) {
+                    const int f = jj * (kWaves / 2) + (wave >> 1);
+                    if (f < nfrag)
+                        bload_lds16<kSC0>(rhid, hs + f * 1024, gb + (uint32_t)(2 * c0 + f) * 1024u + lane * 16u);
+                }
+                drain_memory();
+            }
+            lds_barrier();
+            if (dn_wave) {
+                for (int s0 = c0; s0 < cend; s0 += kDnSlots) {
+                    // the first kDnSlots steps were requested with the up products; the
+                    // steps past them (unions of more than about 3/4 of E) come here
+                    if (s0 > 0) {
+    #pragma unroll
+                        for (int i = 0; i < kDnSlots; ++i) {
+                            wb[i] = zero_bf16x8();
+                            if (s0 + i < cend)
+                                wb[i] = bload<kNT>(rw2, (uint32_t)((step_off(s0 + i) + lo) * 2));
+                        }
+                    }
+    #pragma unroll
+                    for (int i = 0; i < kDnSlots; ++i)
+                        if (s0 + i < cend) {
+                            const int f = (s0 + i - c0) * 2;
+                            const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(hs + f * 1024 + lane * 16);
+                            const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(hs + (f + 1) * 1024 + lane * 16);
+                            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h0, acc0, 0, 0, 0);
+                            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h1, acc1, 0, 0, 0);
+                        }
+                }
+            }
         }
-        drain_memory();
-    }
-    lds_barrier();
-    if (dn_wave) {
-        f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    } else {
+        // the whole block at once (at most 2048 units)
+        if (!dn_wave) {
+            const int nfrag = nst * 2;
 #pragma unroll
-        for (int i = 0; i < kDnSlots; ++i)
-            if (i < n0) {
-                const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(hs + (i * 2) * 1024 + lane * 16);
-                const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(hs + (i * 2 + 1) * 1024 + lane * 16);
-                acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h0, acc0, 0, 0, 0);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h1, acc1, 0, 0, 0);
+            for (int jj = 0; jj < kHidChunk * 2 / (kWaves / 2); ++jj) {
+                const int f = jj * (kWaves / 2) + (wave >> 1);
+                if (f < nfrag)
+                    bload_lds16<kSC0>(rhid, hs + f * 1024, gb + (uint32_t)f * 1024u + lane * 16u);
             }
-        // the steps past the first kDnSlots (unions of more than about 3/4 of E)
-        for (int i0 = kDnSlots; i0 < nst; i0 += kDnSlots) {
-#pragma unroll
-            for (int i = 0; i < kDnSlots; ++i) {
-                wb[i] = zero_bf16x8();
-                if (i0 + i < nst)
-                    wb[i] = bload<kNT>(rw2, (uint32_t)((__builtin_amdgcn_readlane(sbase, i0 + i) + lo) * 2));
-            }
+            drain_memory();
+        }
+        lds_barrier();
+        if (dn_wave) {
 #pragma unroll
             for (int i = 0; i < kDnSlots; ++i)
-                if (i0 + i < nst) {
-                    const bf16x8 h0 =
-                        *reinterpret_cast<const bf16x8 *>(hs + ((i0 + i) * 2) * 1024 + lane * 16);
-                    const bf16x8 h1 =
-                        *reinterpret_cast<const bf16x8 *>(hs + ((i0 + i) * 2 + 1) * 1024 + lane * 16);
+                if (i < n0) {
+                    const bf16x8 h0 = *reinterpret_cast<const bf16x8 *>(hs + (i * 2) * 1024 + lane * 16);
+                    const bf16x8 h1 = *reinterpret_cast<const bf16x8 *>(hs + (i * 2 + 1) * 1024 + lane * 16);
                     acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h0, acc0, 0, 0, 0);
                     acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h1, acc1, 0, 0, 0);
                 }
+            // the steps past the first kDnSlots (unions of more than about 3/4 of E)
+            for (int i0 = kDnSlots; i0 < nst; i0 += kDnSlots) {
+#pragma unroll
+                for (int i = 0; i < kDnSlots; ++i) {
+                    wb[i] = zero_bf16x8();
+                    if (i0 + i < nst)
+                        wb[i] = bload<kNT>(rw2, (uint32_t)((step_off(i0 + i) + lo) * 2));
+                }
+#pragma unroll
+                for (int i = 0; i < kDnSlots; ++i)
+                    if (i0 + i < nst) {
+                        const bf16x8 h0 =
+                            *reinterpret_cast<const bf16x8 *>(hs + ((i0 + i) * 2) * 1024 + lane * 16);
+                        const bf16x8 h1 =
+                            *reinterpret_cast<const bf16x8 *>(hs + ((i0 + i) * 2 + 1) * 1024 + lane * 16);
+                        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h0, acc0, 0, 0, 0);
+                        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wb[i], h1, acc1, 0, 0, 0);
+                    }
+            }
         }
+    }
+    if (dn_wave) {
         // group tile: element i of a lane is column ct*16 + kgrp*4 + i of token l16 (+16)
 #pragma unroll
         for (int th = 0; th < 2; ++th) {
@@ -912,45 +991,62 @@ hipError_t launch_pack_weights(const uint16_t *w1, const uint16_t *w2, int64_t E
     return hipGetLastError();
 }
 
+// Hidden units of the largest group range: every expert in the union, split over the
+// xcds groups in 32-unit blocks.
+static int64_t decode_group_units(int64_t E, int64_t d_e, int xcds)
+{
+    return 32 * ((E * (d_e / 32) + xcds - 1) / xcds);
+}
+
 bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds, int members)
 {
     if (CT != 1 || xcds < 1 || xcds > kMaxGroups || members < 1 || members > kMaxMembers)
         return false;
     if (d_h % 128 != 0 || d_h > kMaxDh || d_h / kDnCols > members)
         return false;
-    if (d_e % 32 != 0 || d_e < kMaxRows)
+    if (d_e % 32 != 0)
         return false;
     if (E * kTileM > kMaxScoreLoads * kThreads)
         return false;
-    // the largest group range (all E experts in the union) and its largest member piece
-    const int64_t ng = 32 * ((E * (d_e / 32) + xcds - 1) / xcds);
-    return ng <= kGroupUnitsMax && 2 * ((ng / 2 + members - 1) / members) <= kMaxRows;
+    // the largest group range (all E experts in the union) and its largest member piece,
+    // which must span at most two slots (rows <= d_e)
+    const int64_t ng = decode_group_units(E, d_e, xcds);
+    const int64_t rows = 2 * ((ng / 2 + members - 1) / members);
+    return ng <= kGroupUnitsMax && rows <= kMaxRows && rows <= d_e;
 }
 
-size_t decode_scratch_bytes(int64_t d_h, int64_t d_e)
+size_t decode_scratch_bytes(int64_t d_h, int64_t E, int64_t d_e)
 {
-    (void)d_e;
-    const size_t hidden = (size_t)kMaxGroups * kGroupUnitsMax * kTileM * 2;
+    // X groups of at most ceil(E d_e / 32 / X) 32-unit blocks: X * ng <= E d_e + 32 X
+    const size_t hidden = (size_t)(E * d_e + 32 * kMaxGroups) * kTileM * 2;
     const size_t part = (size_t)(d_h / kDnCols) * kMaxGroups * kTileM * kDnCols * 4;
     const size_t logits = (size_t)kMaxGroups * kMaxLayerE * kTileM * 4;
     return align_up(hidden, 256) + align_up(part, 256) + logits;
 }
 
+template <bool ROUTER, bool PACKED, bool LN, int WC>
+static int occupancy_of()
+{
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, ffn_bf16_decode_kernel<ROUTER, PACKED, LN, WC>,
+                                                     kThreads, 0) != hipSuccess)
+        return 0;
+    return occ;
+}
+template <bool ROUTER, bool PACKED, bool LN>
+static int occupancy_min3()
+{
+    const int a = occupancy_of<ROUTER, PACKED, LN, 0>(), b = occupancy_of<ROUTER, PACKED, LN, 1>(),
+              c = occupancy_of<ROUTER, PACKED, LN, 2>();
+    return a < b ? (a < c ? a : c) : (b < c ? b : c);
+}
+
 int decode_blocks_per_cu()
 {
     // every variant must fit one workgroup per CU
-    int occ[5] = {0, 0, 0, 0, 0};
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[0], ffn_bf16_decode_kernel<false, false, false>,
-                                                     kThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[1], ffn_bf16_decode_kernel<true, false, false>,
-                                                     kThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[2], ffn_bf16_decode_kernel<true, true, false>,
-                                                     kThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[3], ffn_bf16_decode_kernel<true, false, true>,
-                                                     kThreads, 0) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ[4], ffn_bf16_decode_kernel<true, true, true>,
-                                                     kThreads, 0) != hipSuccess)
-        return 0;
+    const int occ[5] = {occupancy_min3<false, false, false>(), occupancy_min3<true, false, false>(),
+                        occupancy_min3<true, true, false>(), occupancy_min3<true, false, true>(),
+                        occupancy_min3<true, true, true>()};
     int m = occ[0];
     for (int i = 1; i < 5; ++i)
         m = occ[i] < m ? occ[i] : m;
@@ -964,6 +1060,16 @@ bool layer_decode_supported(int64_t E, int64_t d_h, int members)
 
 namespace {
 
+// The width class a launch needs: its worst-case piece rows and group range.
+int decode_width(const FfnPlan &p, int xcds, int members)
+{
+    const int64_t ng = decode_group_units(p.E, p.d_e, xcds);
+    const int64_t rows = 2 * ((ng / 2 + members - 1) / members);
+    if (ng > (int64_t)kHidChunk * 32 || rows > 64)
+        return 2;
+    return rows > 32 ? 1 : 0;
+}
+
 DecodeArgs decode_args(const FfnPlan &p, int xcds, int members, const uint16_t *x,
                        const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *ws)
 {
@@ -975,7 +1081,8 @@ DecodeArgs decode_args(const FfnPlan &p, int xcds, int members, const uint16_t *
     a.w2 = w2;
     a.y = y;
     a.hidden = reinterpret_cast<uint16_t *>(base + p.off_partials);
-    const size_t hidden = align_up((size_t)kMaxGroups * kGroupUnitsMax * kTileM * 2, 256);
+    const size_t hidden = align_up((size_t)(p.E * p.d_e + 32 * kMaxGroups) * kTileM * 2, 256);
+    a.gfrag = (int)(2 * decode_group_units(p.E, p.d_e, xcds) / 32);
     a.dn_part = reinterpret_cast<float *>(base + p.off_partials + hidden);
     a.dn_arrive = ctrl;
     a.flags = ctrl + kDecodeMaxJT;
@@ -1009,8 +1116,12 @@ hipError_t launch_ffn_bf16_decode(const FfnPlan &p, int xcds, int members, const
     a.masks_out = masks_out;
     a.lists_out = lists_out;
     a.counts_out = counts_out;
-    hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false, false>), dim3((unsigned)(xcds * members)),
-                       dim3(kThreads), 0, stream, a);
+    const dim3 grid((unsigned)(xcds * members)), block(kThreads);
+    switch (decode_width(p, xcds, members)) {
+    case 0: hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false, false, 0>), grid, block, 0, stream, a); break;
+    case 1: hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false, false, 1>), grid, block, 0, stream, a); break;
+    default: hipLaunchKernelGGL((ffn_bf16_decode_kernel<false, false, false, 2>), grid, block, 0, stream, a); break;
+    }
     return hipGetLastError();
 }
 
@@ -1036,14 +1147,25 @@ hipError_t launch_layer_bf16_decode(const FfnPlan &p, int xcds, int members, con
         a.probs_out = ep->probs;
     }
     const dim3 grid((unsigned)(xcds * members)), block(kThreads);
+    const int width = decode_width(p, xcds, members);
+#define BLOCKFFN_LAYER_LAUNCH(PK, L)                                                                 \
+    do {                                                                                           \
+        if (width == 0)                                                                            \
+            hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, PK, L, 0>), grid, block, 0, stream, a);  \
+        else if (width == 1)                                                                       \
+            hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, PK, L, 1>), grid, block, 0, stream, a);  \
+        else                                                                                       \
+            hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, PK, L, 2>), grid, block, 0, stream, a);  \
+    } while (0)
     if (packed && ln)
-        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, true, true>), grid, block, 0, stream, a);
+        BLOCKFFN_LAYER_LAUNCH(true, true);
     else if (packed)
-        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, true, false>), grid, block, 0, stream, a);
+        BLOCKFFN_LAYER_LAUNCH(true, false);
     else if (ln)
-        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, false, true>), grid, block, 0, stream, a);
+        BLOCKFFN_LAYER_LAUNCH(false, true);
     else
-        hipLaunchKernelGGL((ffn_bf16_decode_kernel<true, false, false>), grid, block, 0, stream, a);
+        BLOCKFFN_LAYER_LAUNCH(false, false);
+#undef BLOCKFFN_LAYER_LAUNCH
     return hipGetLastError();
 }
 

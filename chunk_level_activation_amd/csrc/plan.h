@@ -48,10 +48,10 @@ inline int64_t chunk1_control_words(int64_t E, int64_t d_h, int64_t d_e)
 inline bool decode_shape(int dtype, int64_t CT, int64_t d_h, int64_t d_e)
 {
     return dtype == 1 && CT == 1 && d_h % 128 == 0 && d_h <= 2048 && d_e % 64 == 0 &&
-           d_e <= 256;
+           d_e <= 512;
 }
 bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds, int members);
-size_t decode_scratch_bytes(int64_t d_h, int64_t d_e);
+size_t decode_scratch_bytes(int64_t d_h, int64_t E, int64_t d_e);
 int decode_blocks_per_cu();
 
 // Expert-grouped multi-chunk bf16 schedule (ffn_bf16_grouped.hip): sizes it takes and
@@ -105,8 +105,8 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     size_t partials = 0;
     if (p.chunk1)
         partials = chunk1_partial_bytes(d_h, E, d_e);
-    if (p.decode && decode_scratch_bytes(d_h, d_e) > partials)
-        partials = decode_scratch_bytes(d_h, d_e);
+    if (p.decode && decode_scratch_bytes(d_h, E, d_e) > partials)
+        partials = decode_scratch_bytes(d_h, E, d_e);
     off = align_up(off + partials, 256);
     p.off_tiles = off;
     if (p.grouped)

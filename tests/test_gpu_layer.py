@@ -59,12 +59,13 @@ CASES = [
     ("no gain, no bias", 6, 32, 2048, 64, 128, 32, False, False),
     ("d_h=768", 10, 32, 768, 64, 128, 32, True, True),
     ("d_e=256 (recommended E=40)", 9, 32, 2048, 40, 256, 32, True, True),
+    ("d_e=512 (recommended E=40)", 12, 32, 2048, 40, 512, 32, True, True),
     # router + chunk FFN launches
     ("E=128", 7, 32, 2048, 128, 128, 32, True, True),
     ("multi-chunk T=256", 8, 256, 1024, 64, 128, 32, True, True),
-    ("d_e=512 (recommended E=40)", 12, 32, 2048, 40, 512, 32, True, True),
+    ("E=64 d_e=512", 13, 32, 2048, 64, 512, 32, True, True),
 ]
-NFUSED = 8
+NFUSED = 9
 
 
 @pytest.mark.parametrize("idx", range(len(CASES)), ids=[c[0] for c in CASES])

@@ -79,6 +79,7 @@ CASES = [
     ("d_h=1024 E=16 d_e=64", 3, 32, 1024, 16, 64, "bf16", True),
     ("d_h=768", 4, 32, 768, 64, 128, "bf16", True),
     ("recommended E=40 d_e=256", 8, 32, 2048, 40, 256, "bf16", True),
+    ("recommended E=40 d_e=512", 9, 32, 2048, 40, 512, "bf16", True),
     ("E=128 (router, FFN, LayerNorm launches)", 5, 32, 2048, 128, 128, "bf16", False),
     ("multi-chunk T=256", 6, 256, 1024, 64, 128, "bf16", False),
     ("tiny fp32", 7, 64, 256, 16, 64, "f32", False),

@@ -131,11 +131,16 @@ DECODE = [
     ("recommended E=40 d_e=256 all active", 32, 40, 2048, 256, 0.8, 0.7, True),
     ("E=64 d_e=256 all active", 32, 64, 2048, 256, 0.8, 0.7, True),
     ("d_e=256 d_h=1024 all active", 32, 64, 1024, 256, 0.8, 0.7, True),
+    # d_e=512: pieces of up to 96 rows (three passes) and group ranges of up to 2560
+    # units (the hidden block in two LDS chunks when all 40 experts are active)
+    ("recommended E=40 d_e=512", 32, 40, 2048, 512, 0.8, 0.7, False),
+    ("recommended d_e=512 T=7", 7, 40, 2048, 512, 0.8, 0.7, False),
+    ("recommended E=40 d_e=512 all active", 32, 40, 2048, 512, 0.8, 0.7, True),
+    ("E=24 d_e=512 d_h=1024 all active", 32, 24, 1024, 512, 0.5, 0.3, True),
     # sizes outside the one-workgroup-per-CU schedule (other single-chunk paths)
     ("d_h=4096", 32, 64, 4096, 128, 0.8, 0.7, False),
     ("E=128", 32, 128, 2048, 128, 0.8, 0.7, False),
-    ("recommended E=40 d_e=512", 32, 40, 2048, 512, 0.8, 0.7, False),
-    ("recommended d_e=512 T=7", 7, 40, 2048, 512, 0.8, 0.7, False),
+    ("E=64 d_e=512", 32, 64, 2048, 512, 0.8, 0.7, False),
 ]
 
 
