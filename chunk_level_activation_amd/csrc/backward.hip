@@ -23,10 +23,10 @@
 //   1. transpose_tiles_kernel: x and dy copied per 32-token chunk tile as
 //      [tile][d_h][32 tokens], so the weight-gradient products, whose k is the token,
 //      read k-contiguous operands;
-//   2. expert_pass_kernel, workgroup = (expert e, 4 of its tiles), 8 waves: a = X W1_e^T
-//      on waves 0-3 and G = DY W2_e on waves 4-7 over d_h (B = W2^T rows), both on the
-//      128 x 128 tile loop of tile_gemm.h; then ds, and dA and SH in bf16 in both
-//      [token][unit] and [unit][token] order;
+//   2. expert_pass_kernel, workgroup = (expert e, 4 of its tiles), 16 waves: a = X W1_e^T
+//      on waves 0-7 and G = DY W2_e on waves 8-15 over d_h (B = W2^T rows), each a
+//      128 x 128 tile on 8 waves; then ds, and dA and SH in bf16 in both [token][unit]
+//      and [unit][token] order;
 //   3. wgrad_kernel, workgroup = (expert, dW1 or dW2, 128 x 128 output tile): k over the
 //      expert's tiles' tokens; every output element is owned by one workgroup (an
 //      expert no chunk uses gets zeros);
@@ -160,30 +160,36 @@ struct PassArgs {
 };
 
 constexpr int kPP = kPKP;                 // the expert pass's LDS pitch (same k step)
-constexpr int kPassThreads = 2 * kBT;     // two 4-wave groups: X W1^T and DY W2
+constexpr int kPassGroup = 2 * kBT;       // 8 waves per product
+constexpr int kPassThreads = 2 * kPassGroup;
+constexpr int kPassDepth = 2;             // k steps of loads in flight
+static_assert(kPassDepth % 2 == 0, "the LDS double buffer alternates with the ring slot");
 
-// Waves 0-3 multiply X by W1_e^T and waves 4-7 DY by W2_e (the same 128 x 128 tile
-// loop on their own LDS tiles, three k steps of loads in flight); the second group then
-// hands G to the first through LDS (each thread's accumulators to the thread with the
-// same position in the first group), which applies the epilogue.
-__global__ void __launch_bounds__(kPassThreads, 2) expert_pass_kernel(PassArgs a)
+// Two 8-wave groups, one workgroup per CU: group 0 forms a = X W1_e^T and group 1
+// G = DY W2_e at the same time, each on its own LDS double buffer, each wave a 32 x 64
+// block of the 128 x 128 tile (wm = 32-row tile, wn = 64-unit half) with two k steps of
+// loads in flight (at most 128 registers: 16 waves per CU). Group 1 then hands G to
+// group 0 through LDS (each thread's accumulators to the thread at the same position),
+// which applies the epilogue.
+__global__ void __launch_bounds__(kPassThreads, 4) expert_pass_kernel(PassArgs a)
 {
     const Dims &d = a.d;
     const int e = blockIdx.x % d.E, grp = blockIdx.x / d.E;
     const int cnt = a.tile_count[e];
     if (grp * kPassTiles >= cnt)
         return;
-    // operand tiles As1 Bs1 As2 Bs2, reused after the k loop for the hand-over of G
-    __shared__ alignas(16) uint16_t ops[4 * kTM * kPP];
-    static_assert(sizeof(ops) >= (size_t)kBT * 64 * sizeof(float), "G hand-over fits the operand tiles");
-    __shared__ float red[kTM][65];
+    // [group][A, B][buffer]; afterwards group 1's hold G and group 0's the ds partials
+    __shared__ alignas(16) uint16_t ops[2][2][2][kTM * kPP];
+    static_assert(sizeof(ops[1]) >= (size_t)kPassGroup * 32 * sizeof(float), "G fits group 1's buffers");
+    static_assert(sizeof(ops[0]) >= (size_t)kTM * 65 * sizeof(float), "the ds partials fit group 0's buffers");
     __shared__ float dsacc[kTM], scol[kTM];
     __shared__ int64_t tok[kTM];
     __shared__ int tiles[kPassTiles];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int g = __builtin_amdgcn_readfirstlane(wave >> 2);   // 0: X W1^T, 1: DY W2
-    const int gt = tid & (kBT - 1);                            // thread within the group
-    const int wm = wave & 1, wn = (wave >> 1) & 1;
+    const int g = __builtin_amdgcn_readfirstlane(wave >> 3);   // 0: X W1^T, 1: DY W2
+    const int gt = tid & (kPassGroup - 1);                     // thread within the group
+    const int wm = wave & 3, wn = (wave >> 2) & 1;
+    const int col = lane & 31, kg = lane >> 5;
     if (tid < kPassTiles)
         tiles[tid] = grp * kPassTiles + tid < cnt ? a.tile_list[(int64_t)e * d.CT + grp * kPassTiles + tid] : -1;
     __syncthreads();
@@ -197,108 +203,159 @@ __global__ void __launch_bounds__(kPassThreads, 2) expert_pass_kernel(PassArgs a
 
     // the group's operands: token rows of x or dy, hidden-unit rows of W1 or W2^T (both
     // [E][d_e][d_h], so the same offsets serve either)
-    const __amdgpu_buffer_rsrc_t rA =
-        make_rsrc(g ? a.dy : a.x, (uint64_t)d.T * d.d_h * 2);
-    const __amdgpu_buffer_rsrc_t rB =
-        make_rsrc(g ? a.w2t : a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
-    uint16_t *As = ops + (2 * g) * kTM * kPP, *Bs = ops + (2 * g + 1) * kTM * kPP;
-    // piece i of this thread: row (gt + 256 i) / 8, k offset (gt % 8) * 8
-    constexpr int kV = kTM * kPK / 8 / kBT;    // 4
-    uint32_t xoff[kV], xmask[kV];
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g ? a.dy : a.x, (uint64_t)d.T * d.d_h * 2);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g ? a.w2t : a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
+    uint16_t *const As0 = ops[g][0][0], *const As1 = ops[g][0][1];
+    uint16_t *const Bs0 = ops[g][1][0], *const Bs1 = ops[g][1][1];
+    // piece i of this thread per k step: row (gt + 512 i) / 8, k offset (gt % 8) * 8
+    uint32_t aoff[2], amask[2];
+    int lrow[2], lcol[2];
 #pragma unroll
-    for (int i = 0; i < kV; ++i) {
-        const int q = gt + i * kBT;
-        const int64_t t = tok[q >> 3];
-        xmask[i] = 0u - (uint32_t)(t >= 0);
-        xoff[i] = t >= 0 ? (uint32_t)((t * d.d_h + (q & 7) * 8) * 2) : 0u;
+    for (int i = 0; i < 2; ++i) {
+        const int q = gt + i * kPassGroup;
+        lrow[i] = q >> 3;
+        lcol[i] = (q & 7) * 8;
+        const int64_t t = tok[lrow[i]];
+        amask[i] = 0u - (uint32_t)(t >= 0);
+        aoff[i] = t >= 0 ? (uint32_t)((t * d.d_h + lcol[i]) * 2) : 0u;
     }
     const int KS = d.d_h / kPK;
-    float *gbuf = reinterpret_cast<float *>(ops);   // [64 values][256 threads]
+    float *gbuf = reinterpret_cast<float *>(ops[1]);   // [32 values][512 threads]
+    float *red = reinterpret_cast<float *>(ops[0]);    // [128 rows][65]
+    const int tile = __builtin_amdgcn_readfirstlane(tiles[wm]);
+    // the epilogue's stores: wave-uniform descriptors of this (tile, expert) block of
+    // the [token][unit] and [unit][token] arrays, one lane offset each; the (row group,
+    // row, unit block) parts are uniform
+    const int64_t blk = ((int64_t)(tile < 0 ? 0 : tile) * d.E + e) * kTileM * d.d_e;
+    const uint32_t blk_bytes = (uint32_t)(kTileM * d.d_e * 2);
+    const __amdgpu_buffer_rsrc_t rtu = make_rsrc(a.da_tu + blk, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rdut = make_rsrc(a.da_ut + blk, blk_bytes);
+    const __amdgpu_buffer_rsrc_t rsut = make_rsrc(a.sh_ut + blk, blk_bytes);
+    const uint32_t tu_lane = (uint32_t)(((lane >> 5) * 4 * d.d_e + wn * 64 + col) * 2);
+    const uint32_t ut_lane = (uint32_t)(((wn * 64 + col) * kTileM + (lane >> 5) * 4) * 2);
     for (int u0 = 0; u0 < d.d_e; u0 += kTM) {
-        uint32_t woff[kV];
+        uint32_t boff[2];
 #pragma unroll
-        for (int i = 0; i < kV; ++i) {
-            const int q = gt + i * kBT;
-            woff[i] = (uint32_t)((((int64_t)e * d.d_e + u0 + (q >> 3)) * d.d_h + (q & 7) * 8) * 2);
-        }
-        auto load = [&](int s, u32x4(&ra)[4], u32x4(&rb)[4]) {
-            const uint32_t okm = 0u - (uint32_t)(s < KS);
-            const uint32_t ko = (uint32_t)(s * kPK * 2);
+        for (int i = 0; i < 2; ++i)
+            boff[i] = (uint32_t)((((int64_t)e * d.d_e + u0 + lrow[i]) * d.d_h + lcol[i]) * 2);
+        f32x16 acc[2];
 #pragma unroll
-            for (int i = 0; i < kV; ++i) {
-                const uint32_t am = okm & xmask[i];
-                ra[i] = load16(rA, ((xoff[i] + ko) & am) | (kOOB & ~am));
-                rb[i] = load16(rB, ((woff[i] + ko) & okm) | (kOOB & ~okm));
+        for (int j = 0; j < 2; ++j)
+            zero_acc(acc[j]);
+        {
+            u32x4 ra[kPassDepth][2], rb[kPassDepth][2];
+            // every load is issued: rows without a token, and steps past KS, read zeros
+            auto issue = [&](int st, int dd) {
+                const uint32_t okm = 0u - (uint32_t)(st < KS);
+                const uint32_t kb = (uint32_t)(st * kPK * 2);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    const uint32_t am = okm & amask[i];
+                    ra[dd][i] = load16(rA, ((aoff[i] + kb) & am) | (kOOB & ~am));
+                    rb[dd][i] = load16(rB, ((boff[i] + kb) & okm) | (kOOB & ~okm));
+                }
+            };
+            // in ring order (the scheduling barriers keep it), so that the wait before a
+            // slot's LDS store counts only the younger slots' loads
+#pragma unroll
+            for (int dd = 0; dd < kPassDepth; ++dd) {
+                issue(dd, dd);
+                __builtin_amdgcn_sched_barrier(0);
             }
-        };
-        f32x16 acc[2][2];
-        tile::zero_acc(acc);
-        kloop_128x128(load, KS, As, Bs, acc, gt, wm, wn, lane);
-        // the k loop ended with a barrier: the operand tiles are free for G
-        if (g == 1) {
+            // whole turns of the ring (steps past KS add zeros); both groups take the
+            // same steps, so the workgroup barriers pair up
+            for (int s0 = 0; s0 < KS; s0 += kPassDepth) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+                for (int dd = 0; dd < kPassDepth; ++dd) {
+                    uint16_t *As = (dd & 1) ? As1 : As0;
+                    uint16_t *Bs = (dd & 1) ? Bs1 : Bs0;
 #pragma unroll
-                for (int j = 0; j < 2; ++j)
+                    for (int i = 0; i < 2; ++i) {
+                        *reinterpret_cast<u32x4 *>(&As[lrow[i] * kPP + lcol[i]]) = ra[dd][i];
+                        *reinterpret_cast<u32x4 *>(&Bs[lrow[i] * kPP + lcol[i]]) = rb[dd][i];
+                    }
+                    __syncthreads();
+                    issue(s0 + dd + kPassDepth, dd);
 #pragma unroll
-                    for (int v = 0; v < 16; ++v)
-                        gbuf[((i * 2 + j) * 16 + v) * kBT + gt] = acc[i][j][v];
-        }
-        __syncthreads();
-        if (g == 0) {
-            // epilogue: Swish, its slope, the score
-            float part[2][16];
+                    for (int ks = 0; ks < kPK / 16; ++ks) {
+                        const bf16x8 fa =
+                            *reinterpret_cast<const bf16x8 *>(&As[(wm * 32 + col) * kPP + ks * 16 + kg * 8]);
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int v = 0; v < 16; ++v)
-                    part[i][v] = 0.0f;
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-#pragma unroll
-                for (int j = 0; j < 2; ++j) {
-                    const int unit = u0 + wn * 64 + j * 32 + (lane & 31);
-#pragma unroll
-                    for (int vg = 0; vg < 4; ++vg) {
-                        uint32_t da_pk[2] = {0u, 0u}, sh_pk[2] = {0u, 0u};
-                        const int row0 = wm * 64 + i * 32 + acc_row(vg * 4, lane);   // 4 consecutive rows
-                        const int tile = tiles[row0 / kTileM];
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const int v = vg * 4 + q, row = row0 + q;
-                            const float av = acc[i][j][v], s = scol[row];
-                            const float gv = gbuf[((i * 2 + j) * 16 + v) * kBT + gt];
-                            const float sig = 1.0f / (1.0f + expf(-av));
-                            const float h = av * sig;
-                            part[i][v] += gv * h;
-                            const float dA = s * gv * (sig * (1.0f + av * (1.0f - sig)));
-                            const float sh = s * h;
-                            const uint32_t b_da = f32_to_bf16(dA), b_sh = f32_to_bf16(sh);
-                            da_pk[q >> 1] |= b_da << ((q & 1) * 16);
-                            sh_pk[q >> 1] |= b_sh << ((q & 1) * 16);
-                            if (tile >= 0)
-                                a.da_tu[(((int64_t)tile * d.E + e) * kTileM + row % kTileM) * d.d_e + unit] =
-                                    (uint16_t)b_da;
-                        }
-                        if (tile >= 0) {
-                            const int64_t o = (((int64_t)tile * d.E + e) * d.d_e + unit) * kTileM + row0 % kTileM;
-                            *reinterpret_cast<uint64_t *>(&a.da_ut[o]) = (uint64_t)da_pk[0] | ((uint64_t)da_pk[1] << 32);
-                            *reinterpret_cast<uint64_t *>(&a.sh_ut[o]) = (uint64_t)sh_pk[0] | ((uint64_t)sh_pk[1] << 32);
+                        for (int j = 0; j < 2; ++j) {
+                            const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
+                                &Bs[(wn * 64 + j * 32 + col) * kPP + ks * 16 + kg * 8]);
+                            acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
                         }
                     }
                 }
-            // ds: per-lane row partials -> LDS [row][64 columns] -> summed in column order
+            }
+        }
+        // every wave is done with the operand buffers: group 1's take G
+        __syncthreads();
+        if (g == 1) {
 #pragma unroll
-            for (int i = 0; i < 2; ++i)
+            for (int j = 0; j < 2; ++j)
 #pragma unroll
                 for (int v = 0; v < 16; ++v)
-                    red[wm * 64 + i * 32 + acc_row(v, lane)][wn * 32 + (lane & 31)] = part[i][v];
+                    gbuf[(j * 16 + v) * kPassGroup + gt] = acc[j][v];
+        }
+        __syncthreads();
+        if (g == 0) {
+            // epilogue: Swish, its slope, the score; element v of accumulator j is row
+            // wm * 32 + acc_row(v) (row acc_row(v) of tile wm) and unit u0 + wn * 64 +
+            // j * 32 + col
+            float part[16];
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                part[v] = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) {
+                    uint32_t da_pk[2] = {0u, 0u}, sh_pk[2] = {0u, 0u};
+                    const int r0 = acc_row(vg * 4, lane);   // 4 consecutive rows of the tile
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int v = vg * 4 + q, r = r0 + q;
+                        const float av = acc[j][v], s = scol[wm * 32 + r];
+                        const float gv = gbuf[(j * 16 + v) * kPassGroup + gt];
+                        const float sig = 1.0f / (1.0f + expf(-av));
+                        const float h = av * sig;
+                        part[v] += gv * h;
+                        const float dA = s * gv * (sig * (1.0f + av * (1.0f - sig)));
+                        const uint32_t b_da = f32_to_bf16(dA), b_sh = f32_to_bf16(s * h);
+                        da_pk[q >> 1] |= b_da << ((q & 1) * 16);
+                        sh_pk[q >> 1] |= b_sh << ((q & 1) * 16);
+                        // row r = (lane / 32) * 4 + 8 vg + q, unit u0 + j * 32 + wn * 64 + col
+                        if (tile >= 0)
+                            __builtin_amdgcn_raw_buffer_store_b16(
+                                (unsigned short)b_da, rtu, (int)tu_lane,
+                                (int)(((vg * 8 + q) * d.d_e + u0 + j * 32) * 2), 0);
+                    }
+                    if (tile >= 0) {
+                        const uint32_t so = (uint32_t)(((u0 + j * 32) * kTileM + vg * 8) * 2);
+                        const uint64_t dpk = (uint64_t)da_pk[0] | ((uint64_t)da_pk[1] << 32);
+                        const uint64_t spk = (uint64_t)sh_pk[0] | ((uint64_t)sh_pk[1] << 32);
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(unsigned int __attribute__((ext_vector_type(2))), dpk), rdut,
+                            (int)ut_lane, (int)so, 0);
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(unsigned int __attribute__((ext_vector_type(2))), spk), rsut,
+                            (int)ut_lane, (int)so, 0);
+                    }
+                }
+            }
+            // ds: row partials (units j * 32 + col of this wave's half, j summed) -> LDS
+            // [row][64] -> summed in column order
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[(wm * 32 + acc_row(v, lane)) * 65 + wn * 32 + col] = part[v];
         }
         __syncthreads();
         if (tid < kTM) {
             float sum = 0.0f;
             for (int c = 0; c < 64; ++c)
-                sum += red[tid][c];
+                sum += red[tid * 65 + c];
             dsacc[tid] += sum;
         }
         __syncthreads();
