@@ -24,7 +24,11 @@
 //      with the hidden rows of a tile whose chunk does not use the expert read as
 //      zero (those terms are exactly zero: the scores are zero there). Every output
 //      element is owned by one workgroup, so there is no cross-workgroup sum, and the
-//      column tiles map to XCDs so each W2 column slice stays in one L2.
+//      column tiles map to XCDs so each W2 column slice stays in one L2. When those
+//      workgroups would not fill the chip (few chunks, e.g. 16 chunks of a d_h = 4096
+//      layer: 128 workgroups), k is split in 2 or 4 contiguous ranges, each
+//      workgroup writes its fp32 partial tile, and 5. down_reduce_kernel adds the
+//      partials in split order into y.
 #include "common.h"
 #include "plan.h"
 #include "sync.h"
@@ -59,8 +63,10 @@ struct GroupedArgs {
     const uint64_t *masks;       // [C][W]
     int32_t *tile_list;          // [E][CT]
     int32_t *tile_count;         // [E]
+    float *dn_part;              // [splits][CT * 32][d_h] when splits > 1
     int64_t T;
     int n, d_h, E, d_e, C, MPC, CT, W;
+    int splits;
 };
 
 // Token of row r of chunk tile `tile`, or -1 when the row holds no token.
@@ -236,8 +242,10 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs a)
 {
     const int NCT = a.d_h / kDnCols;
+    const int NBT = (a.CT + kDnTiles - 1) / kDnTiles;
     const int ct = blockIdx.x % NCT;
-    const int bt = blockIdx.x / NCT;
+    const int bt = (blockIdx.x / NCT) % NBT;
+    const int split = blockIdx.x / NCT / NBT;
     __shared__ alignas(16) uint16_t As[2][kDnRows * kPitch];   // hidden rows x 64 units
     __shared__ alignas(16) uint16_t Bs[2][kDnCols * kPitch];   // W2 rows (output columns) x 64 units
     __shared__ uint64_t m_tile[kDnTiles][kMaxWords];
@@ -284,7 +292,10 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     const int a_tile_i = arow / kTileM, a_r = arow % kTileM;
     const int a_tile = tile_of[a_tile_i];
     const int DK = a.d_e / kKStep;
-    const int steps = nlist * DK;
+    // this split's contiguous range [st0, st1) of the k steps
+    const int steps_all = nlist * DK;
+    const int st0 = (int)((int64_t)split * steps_all / a.splits);
+    const int st1 = (int)((int64_t)(split + 1) * steps_all / a.splits);
     f32x16 acc[2];
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -298,7 +309,7 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     auto issue = [&](int st, int d) {
         // branch-free: the list entry is read even past the end (masked to a valid
         // expert index) and the offsets are replaced afterwards
-        const bool ok = st < steps;
+        const bool ok = st < st1;
         const int li = st / DK;
         const int e = list[li < 255 ? li : 255] & 255;
         const int k0 = (st - li * DK) * kKStep;
@@ -317,10 +328,10 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     };
 #pragma unroll
     for (int d = 0; d < kDepth; ++d) {
-        issue(d, d);
+        issue(st0 + d, d);
         __builtin_amdgcn_sched_barrier(0);
     }
-    for (int s0 = 0; s0 < steps; s0 += kDepth) {
+    for (int s0 = st0; s0 < st1; s0 += kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
             const int st = s0 + d;
@@ -350,6 +361,18 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     const int tile = tile_of[wm];
     if (tile < 0)
         return;
+    if (a.splits > 1) {
+        // the split's fp32 partial of the tile's rows
+        float *dst = a.dn_part + ((int64_t)split * a.CT + tile) * kTileM * a.d_h;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int cidx = ct * kDnCols + wn * 64 + j * 32 + col;
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                dst[(int64_t)acc_row(v, lane) * a.d_h + cidx] = acc[j][v];
+        }
+        return;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
         const int cidx = ct * kDnCols + wn * 64 + j * 32 + col;
@@ -362,7 +385,50 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     }
 }
 
+// ------------------------------------------------------------------ split sum
+// y[t][c] = bf16(sum over the splits, in order, of the partials of t's tile row);
+// thread -> 4 consecutive columns of one tile row.
+__global__ void __launch_bounds__(256) down_reduce_kernel(GroupedArgs a)
+{
+    const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    const int c4 = a.d_h / 4;
+    const int64_t rows = (int64_t)a.CT * kTileM;
+    if (q >= rows * c4)
+        return;
+    const int64_t row = q / c4;
+    const int c = (int)(q - row * c4) * 4;
+    const int64_t t = tile_token(a, (int)(row / kTileM), (int)(row % kTileM));
+    if (t < 0)
+        return;
+    float4 sum = *reinterpret_cast<const float4 *>(a.dn_part + row * a.d_h + c);
+    for (int s = 1; s < a.splits; ++s) {
+        const float4 v = *reinterpret_cast<const float4 *>(a.dn_part + ((int64_t)s * rows + row) * a.d_h + c);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
+    const uint64_t packed = (uint64_t)f32_to_bf16(sum.x) | ((uint64_t)f32_to_bf16(sum.y) << 16) |
+                            ((uint64_t)f32_to_bf16(sum.z) << 32) | ((uint64_t)f32_to_bf16(sum.w) << 48);
+    *reinterpret_cast<uint64_t *>(a.y + t * a.d_h + c) = packed;
+}
+
 }  // namespace
+
+int grouped_down_splits(int64_t CT, int64_t d_h)
+{
+    const int64_t blocks = ((CT + kDnTiles - 1) / kDnTiles) * (d_h / kDnCols);
+    int s = 1;
+    while (s < 4 && blocks * s < 256)
+        s *= 2;
+    return s;
+}
+
+size_t grouped_partial_bytes(int64_t CT, int64_t d_h)
+{
+    const int s = grouped_down_splits(CT, d_h);
+    return s > 1 ? (size_t)s * CT * kTileM * d_h * 4 : 0;
+}
 
 bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_e)
 {
@@ -423,12 +489,18 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
     a.MPC = (int)p.MPC;
     a.CT = (int)p.CT;
     a.W = (int)p.W;
+    a.splits = grouped_down_splits(p.CT, p.d_h);
+    a.dn_part = reinterpret_cast<float *>(base + p.off_dnpart);
     hipLaunchKernelGGL(expert_tiles_kernel, dim3((unsigned)p.E), dim3(256), 0, stream, a);
     const int64_t up_blocks = p.E * ((p.CT + kUpTiles - 1) / kUpTiles);
     hipLaunchKernelGGL(up_grouped_kernel, dim3((unsigned)up_blocks), dim3(kGThreads), 0, stream, a);
-    const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols);
+    const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols) * a.splits;
     hipLaunchKernelGGL(down_grouped_kernel, dim3((unsigned)dn_blocks), dim3(kGThreads), 0, stream,
                        a);
+    if (a.splits > 1) {
+        const int64_t q = p.CT * kTileM * (p.d_h / 4);
+        hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((q + 255) / 256)), dim3(256), 0, stream, a);
+    }
     return hipGetLastError();
 }
 

@@ -58,6 +58,11 @@ int decode_blocks_per_cu();
 // the bytes of its per-expert tile lists.
 bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_e);
 size_t grouped_tile_bytes(int64_t CT, int64_t E);
+// k splits of its down-projection: 1, or 2 / 4 when the (tile pair, column tile)
+// workgroups would not fill the chip's 256 CUs; the splits' fp32 partials need
+// grouped_partial_bytes() of scratch.
+int grouped_down_splits(int64_t CT, int64_t d_h);
+size_t grouped_partial_bytes(int64_t CT, int64_t d_h);
 
 // Problem sizes plus everything derived from them that the kernels and the
 // workspace layout need. Built once per call by make_plan().
@@ -75,6 +80,7 @@ struct FfnPlan {
     // scratch after the control block (byte offsets)
     size_t off_masks, off_lists, off_counts;   // fp32 path union
     size_t off_hidden, off_partials, off_tiles;
+    size_t off_dnpart;    // grouped schedule: the down-projection's split partials
     size_t total_bytes;
 };
 
@@ -111,6 +117,9 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     p.off_tiles = off;
     if (p.grouped)
         off = align_up(off + grouped_tile_bytes(p.CT, E), 256);
+    p.off_dnpart = off;
+    if (p.grouped)
+        off = align_up(off + grouped_partial_bytes(p.CT, d_h), 256);
     p.total_bytes = off;
     return p;
 }
