@@ -10,8 +10,9 @@
 // Over many chunks an expert's weights serve every chunk whose union holds it, so
 // each launch should read them once, not once per chunk:
 //   1. union_kernel: per-chunk union masks, lists and counts.
-//   2. expert_tiles_kernel: for every expert, the ascending list of 32-token chunk
-//      tiles whose chunk uses it.
+//   2. (expert_tiles_kernel, for the layer backward: for every expert, the ascending
+//      list of 32-token chunk tiles whose chunk uses it. The forward does without it:
+//      each up workgroup finds its own tiles in the masks.)
 //   3. up_grouped_kernel: workgroup = (expert e, 4 of e's tiles): a 128 x d_e x d_h
 //      GEMM (x rows gathered, W1_e read once per workgroup and shared through the
 //      XCD's L2 by the workgroups of the same expert, which the grid places on one
@@ -124,22 +125,42 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 {
     const int e = blockIdx.x % a.E;
     const int b = blockIdx.x / a.E;
-    const int cnt = a.tile_count[e];
-    if (b * kUpTiles >= cnt)
-        return;
     __shared__ alignas(16) uint16_t As[2][kUpRows * kPitch];   // x rows x 64 k
     __shared__ alignas(16) uint16_t Bs[2][kUpCols * kPitch];   // W1 rows (hidden units) x 64 k
     __shared__ int64_t tok[kUpRows];
     __shared__ float scol[kUpRows];   // score of (row's token, e), zero for rows without one
     __shared__ int tiles[kUpTiles];
 
+    __shared__ int ntiles;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
     const int wm = wave & 3, wn = wave >> 2;       // 32-row tile, 64-unit half
     const int col = lane & 31, kg = lane >> 5;
-    if (tid < kUpTiles)
-        tiles[tid] = b * kUpTiles + tid < cnt ? a.tile_list[(int64_t)e * a.CT + b * kUpTiles + tid]
-                                              : -1;
+    // Tiles 4b .. 4b + 3 of e's ascending tile list, from the chunks' union masks: lane
+    // c of the first wave tests chunk c0 + c, and a chunk's rank among e's chunks is
+    // the count of set ballot bits below it (plus the earlier blocks' counts).
+    if (wave == 0) {
+        if (lane < kUpTiles)
+            tiles[lane] = -1;
+        int base = 0;
+        for (int c0 = 0; c0 < a.C; c0 += kWave) {
+            const int c = c0 + lane;
+            const bool f = c < a.C && ((a.masks[(int64_t)c * a.W + (e >> 6)] >> (e & 63)) & 1ull);
+            const uint64_t bal = __ballot(f);
+            const int rank = base + __popcll(bal & ((1ull << lane) - 1ull));
+            if (f)
+                for (int m = 0; m < a.MPC; ++m) {
+                    const int i = rank * a.MPC + m - b * kUpTiles;
+                    if (i >= 0 && i < kUpTiles)
+                        tiles[i] = c * a.MPC + m;
+                }
+            base += __popcll(bal);
+        }
+        if (lane == 0)
+            ntiles = base * a.MPC;
+    }
     __syncthreads();
+    if (b * kUpTiles >= ntiles)
+        return;
     if (tid < kUpRows) {
         const int64_t t = tile_token(a, tiles[tid / kTileM], tid % kTileM);
         tok[tid] = t;
@@ -491,7 +512,6 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
     a.W = (int)p.W;
     a.splits = grouped_down_splits(p.CT, p.d_h);
     a.dn_part = reinterpret_cast<float *>(base + p.off_dnpart);
-    hipLaunchKernelGGL(expert_tiles_kernel, dim3((unsigned)p.E), dim3(256), 0, stream, a);
     const int64_t up_blocks = p.E * ((p.CT + kUpTiles - 1) / kUpTiles);
     hipLaunchKernelGGL(up_grouped_kernel, dim3((unsigned)up_blocks), dim3(kGThreads), 0, stream, a);
     const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols) * a.splits;
