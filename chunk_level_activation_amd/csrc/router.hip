@@ -21,15 +21,17 @@
 namespace blockffn {
 
 // bf16: 32 tokens x all experts per workgroup, ET tiles of 32 experts, 8 waves. The
-// 32x32x16 bf16 MFMA takes A = x rows (32 tokens x 16 k) and B = W_r rows
-// transposed (16 k x 32 experts). Wave w owns expert tile w % ET and every
-// (8/ET)-th k step of the workgroup's range, issuing the loads of KB steps together;
-// the 8/ET k parts of a tile meet in LDS after one barrier and are added in part
-// order.
+// workgroup's k range goes through LDS in chunks of KC: the x rows and the W_r rows of
+// a chunk are loaded contiguously (16 bytes per lane, a row's pieces on consecutive
+// lanes) into padded [row][k] tiles. The 32x32x16 bf16 MFMA then takes A = x rows
+// (32 tokens x 16 k) and B = W_r rows transposed (16 k x 32 experts) from there. Wave
+// w owns expert tile w % ET and every (8/ET)-th k step of the chunk; the 8/ET k parts
+// of a tile meet in LDS after one barrier and are added in part order.
 constexpr int kRouterThreads = 512;
 constexpr int kRouterWaves = kRouterThreads / kWave;
 constexpr int64_t kRouterTargetBlocks = 256;   // split the d_h sum until about this many (one per CU)
 constexpr int kRouterMaxSplits = 8;
+constexpr uint32_t kOOBRouter = 0x80000000u;   // buffer offset past every range: reads zero
 
 // LOCAL: the S splits of a tile run on one XCD (the caller verified round-robin
 // placement and laid the grid out so), and their partials meet in that XCD's L2;
@@ -52,9 +54,16 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
                    float *__restrict__ part, uint32_t *__restrict__ arrive)
 {
     constexpr int KPARTS = kRouterWaves / ET;
-    constexpr int KB = 8;
     constexpr int kPitch = ET * 32 + 1;
+    // k per LDS chunk: (32 + 32 ET) rows of KC bf16 stay within 100 KB, so that a
+    // workgroup's range (d_h / S) usually is one chunk: one memory round trip
+    constexpr int KC = ET <= 2 ? 512 : (ET <= 4 ? 256 : 128);
+    constexpr int KP = KC + 8;                        // row pitch (bf16): conflict-free reads
+    constexpr int PPR = KC / 8;                       // 16-byte pieces per row
+    constexpr int NROWS = kTileM + ET * 32;
+    constexpr int NPT = (NROWS * PPR + kRouterThreads - 1) / kRouterThreads;
     __shared__ float red[KPARTS][kTileM][kPitch];
+    __shared__ alignas(16) uint16_t ops[NROWS * KP];   // x rows, then the W_r rows
     __shared__ float sgain[ET * 32], sbias[ET * 32];
     __shared__ int last;
 
@@ -85,11 +94,6 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
         sgain[tid] = gain ? gain[tid] : 1.0f;
         sbias[tid] = bias ? bias[tid] : 0.0f;
     }
-    const bool vt = t0 + row < T;
-    const int e_row = et * 32 + row;
-    const bool ve = e_row < E;
-    const uint16_t *xr = x + (vt ? t0 + row : 0) * d_h + kg * 8;
-    const uint16_t *wr = w_r + (int64_t)(ve ? e_row : 0) * d_h + kg * 8;
     f32x16 acc;
 #pragma unroll
     for (int i = 0; i < 16; ++i)
@@ -97,18 +101,46 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     // this split's range of 16-wide k steps
     const int KS = d_h / 16;
     const int ks0 = (int)((int64_t)KS * split / S), ks1 = (int)((int64_t)KS * (split + 1) / S);
-    for (int kb = ks0 + kp; kb < ks1; kb += KPARTS * KB) {
-        bf16x8 av[KB], bv[KB];
+    const int k_end = ks1 * 16;
+    // the tile's rows of x (offsets stay small whatever T is) and all of W_r
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + t0 * d_h, (uint64_t)kTileM * d_h * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_r, (uint64_t)E * d_h * 2);
+    for (int kc = ks0 * 16; kc < k_end; kc += KC) {
+        // piece q = tid + 512 i: row q / PPR (x rows first), k kc + (q % PPR) * 8; rows
+        // past T or E, pieces past the range and q past the tile read zero
+        bf16x8 v[NPT];
 #pragma unroll
-        for (int i = 0; i < KB; ++i) {
-            const int ks = kb + i * KPARTS;
-            const bool ok = ks < ks1;
-            av[i] = ok && vt ? load_bf16x8(xr + ks * 16) : zero_bf16x8();
-            bv[i] = ok && ve ? load_bf16x8(wr + ks * 16) : zero_bf16x8();
+        for (int i = 0; i < NPT; ++i) {
+            const int q = tid + i * kRouterThreads;
+            const int r = q / PPR, c8 = (q % PPR) * 8;
+            const int k = kc + c8;
+            uint32_t off = kOOBRouter;
+            bool xrow = r < kTileM;
+            if (q < NROWS * PPR && k < k_end) {
+                if (xrow) {
+                    if (t0 + r < T)
+                        off = (uint32_t)((r * d_h + k) * 2);
+                } else if (r - kTileM < E) {
+                    off = (uint32_t)(((r - kTileM) * d_h + k) * 2);
+                }
+            }
+            v[i] = bload<0>(xrow ? rx : rw, off);
         }
 #pragma unroll
-        for (int i = 0; i < KB; ++i)
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[i], bv[i], acc, 0, 0, 0);
+        for (int i = 0; i < NPT; ++i) {
+            const int q = tid + i * kRouterThreads;
+            if (q < NROWS * PPR)
+                *reinterpret_cast<bf16x8 *>(&ops[(q / PPR) * KP + (q % PPR) * 8]) = v[i];
+        }
+        __syncthreads();
+        const int nsteps = (k_end - kc < KC ? k_end - kc : KC) / 16;
+        for (int st = kp; st < nsteps; st += KPARTS) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8 *>(&ops[row * KP + st * 16 + kg * 8]);
+            const bf16x8 b =
+                *reinterpret_cast<const bf16x8 *>(&ops[(kTileM + et * 32 + row) * KP + st * 16 + kg * 8]);
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
+        }
+        __syncthreads();
     }
 
     // 32x32 accumulator layout: element i is row (i/4)*8 + (lane/32)*4 + i%4 (token)
