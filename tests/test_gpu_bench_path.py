@@ -105,3 +105,39 @@ def test_bench_path_union_outputs_of_chunk_ffn(bench_inputs):
         assert np.array_equal(lists.cpu().numpy(), l_ref)
         assert np.array_equal(counts.cpu().numpy(), c_ref)
         assert rel_err(host(y), host(y2)) <= 1e-2
+
+
+@pytest.mark.parametrize("T", [2048, 100])
+def test_multichunk_layer_on_bench_inputs(T):
+    """The layer over several 32-token chunks (the bench's prefill step, router activity
+    following the same Markov masks, so the chunk unions are sparse): every row of y
+    against the oracle's router feeding the oracle's per-token FFN (equal to its
+    union-then-mask form), the scores against the oracle's, and the chunk union masks
+    the layer leaves in its workspace (the chunk FFN's first scratch region, after the
+    64 KB control block) bit-exact against the oracle's union of its scores. T=100 ends
+    in a partial chunk."""
+    args = bench.parse_args(["--rotate-mib", "1", "--draws", "2", "--seed", "7"])
+    cfg, copies, draws, xs, S = bench.make_inputs(args, torch, np, inputs, "prefill")
+    w = copies[0]
+    x = xs[0][:T].contiguous()
+    d_h, E, d_e, n = cfg["d_h"], cfg["E"], cfg["d_e"], cfg["n"]
+    gain = torch.ones(E, dtype=torch.float32, device=DEV)
+    ws = bf.blockffn_layer_forward_workspace(T, d_h, E, d_e, n, bf.BLOCKFFN_BF16, DEV)
+    ws.zero_()
+    sc = torch.empty((T, E), dtype=torch.float32, device=DEV)
+    y = bf.blockffn_layer_forward(x, w["w_r"], w["w1"], w["w2"], n, gain=gain, bias=w["bias"],
+                                  scores=sc, workspace=ws)
+    torch.cuda.synchronize()
+    x_h = host(x)
+    bias = None if w["bias"] is None else host(w["bias"])
+    logits, s_ref = oracle.router(x_h, host(w["w_r"]), bias=bias)
+    assert np.abs(logits).min() > 1e-3          # no ill-conditioned activity decision
+    s = host(sc)
+    assert rel_err(s, s_ref) <= 1e-4
+    masks_ref, _, counts_ref = oracle.chunk_union(s_ref.astype(np.float32), n)
+    C, W = masks_ref.shape
+    masks = ws[65536:65536 + C * W * 8].cpu().numpy().view(np.uint64).reshape(C, W)
+    assert np.array_equal(masks, masks_ref)
+    assert 8 < counts_ref.mean() < 56             # sparse, non-trivial unions
+    y_ref = oracle.token_ffn(x_h, s_ref.astype(np.float32), host(w["w1"]), host(w["w2"]))
+    assert rel_err(host(y), y_ref) <= TOL_BF16
