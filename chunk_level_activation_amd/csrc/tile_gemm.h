@@ -1,11 +1,12 @@
-// The 128 x 128 bf16 output tile of the backward's expert-pass and dx products: 256
-// threads = 4 waves, each wave a 64 x 64 block of 2 x 2 32x32x16 MFMA accumulators,
-// operands staged through LDS as [row][k] tiles of 64 k.
+// The 128 x 128 bf16 output tile of the backward's weight-gradient and dx products:
+// 256 threads = 4 waves, each wave a 64 x 64 block of 2 x 2 32x32x16 MFMA
+// accumulators, operands staged through LDS as [row][k] tiles of 64 k.
 //
 // A 64 x 64 wave block reads 16 KB of LDS per 64-wide k step for 512 KFLOP (32 flops
-// per byte), twice the ratio of a 32 x 64 block: with LDS delivering about 150 bytes
-// per clock per CU and the CU's four matrix cores doing about 4 KFLOP per clock, a
-// smaller block leaves the products waiting on LDS.
+// per byte), twice the ratio of a 32 x 64 block, so with LDS delivering about 150
+// bytes per clock per CU four waves can keep the matrix cores fed. (The expert pass
+// instead runs 16 waves of 32 x 64 blocks per CU: more waves in flight, at half the
+// LDS ratio.)
 #pragma once
 
 #include "common.h"
