@@ -61,7 +61,9 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     constexpr int KP = KC + 8;                        // row pitch (bf16): conflict-free reads
     constexpr int PPR = KC / 8;                       // 16-byte pieces per row
     constexpr int NROWS = kTileM + ET * 32;
-    constexpr int NPT = (NROWS * PPR + kRouterThreads - 1) / kRouterThreads;
+    constexpr int NX = kTileM * PPR / kRouterThreads;                        // x pieces per thread
+    constexpr int NW = (ET * 32 * PPR + kRouterThreads - 1) / kRouterThreads;   // W_r pieces
+    static_assert(kTileM * PPR % kRouterThreads == 0, "x pieces fill the threads");
     __shared__ float red[KPARTS][kTileM][kPitch];
     __shared__ alignas(16) uint16_t ops[NROWS * KP];   // x rows, then the W_r rows
     __shared__ float sgain[ET * 32], sbias[ET * 32];
@@ -106,31 +108,33 @@ router_bf16_kernel(const uint16_t *__restrict__ x, const uint16_t *__restrict__ 
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(x + t0 * d_h, (uint64_t)kTileM * d_h * 2);
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(w_r, (uint64_t)E * d_h * 2);
     for (int kc = ks0 * 16; kc < k_end; kc += KC) {
-        // piece q = tid + 512 i: row q / PPR (x rows first), k kc + (q % PPR) * 8; rows
-        // past T or E, pieces past the range and q past the tile read zero
-        bf16x8 v[NPT];
+        // piece q = tid + 512 i: row q / PPR, k kc + (q % PPR) * 8, of the x rows and of the
+        // W_r rows (each with its own buffer, so the descriptor stays uniform); rows past
+        // T or E, pieces past the range and q past the rows read zero
+        bf16x8 vx[NX], vw[NW];
 #pragma unroll
-        for (int i = 0; i < NPT; ++i) {
+        for (int i = 0; i < NX; ++i) {
             const int q = tid + i * kRouterThreads;
-            const int r = q / PPR, c8 = (q % PPR) * 8;
-            const int k = kc + c8;
-            uint32_t off = kOOBRouter;
-            bool xrow = r < kTileM;
-            if (q < NROWS * PPR && k < k_end) {
-                if (xrow) {
-                    if (t0 + r < T)
-                        off = (uint32_t)((r * d_h + k) * 2);
-                } else if (r - kTileM < E) {
-                    off = (uint32_t)(((r - kTileM) * d_h + k) * 2);
-                }
-            }
-            v[i] = bload<0>(xrow ? rx : rw, off);
+            const int r = q / PPR, k = kc + (q % PPR) * 8;
+            vx[i] = bload<0>(rx, k < k_end && t0 + r < T ? (uint32_t)((r * d_h + k) * 2) : kOOBRouter);
         }
 #pragma unroll
-        for (int i = 0; i < NPT; ++i) {
+        for (int i = 0; i < NW; ++i) {
             const int q = tid + i * kRouterThreads;
-            if (q < NROWS * PPR)
-                *reinterpret_cast<bf16x8 *>(&ops[(q / PPR) * KP + (q % PPR) * 8]) = v[i];
+            const int r = q / PPR, k = kc + (q % PPR) * 8;
+            vw[i] = bload<0>(rw, q < ET * 32 * PPR && k < k_end && r < E ? (uint32_t)((r * d_h + k) * 2)
+                                                                        : kOOBRouter);
+        }
+#pragma unroll
+        for (int i = 0; i < NX; ++i) {
+            const int q = tid + i * kRouterThreads;
+            *reinterpret_cast<bf16x8 *>(&ops[(q / PPR) * KP + (q % PPR) * 8]) = vx[i];
+        }
+#pragma unroll
+        for (int i = 0; i < NW; ++i) {
+            const int q = tid + i * kRouterThreads;
+            if (q < ET * 32 * PPR)
+                *reinterpret_cast<bf16x8 *>(&ops[(kTileM + q / PPR) * KP + (q % PPR) * 8]) = vw[i];
         }
         __syncthreads();
         const int nsteps = (k_end - kc < KC ? k_end - kc : KC) / 16;
