@@ -237,9 +237,13 @@ def measure(args, torch, np, bf, inputs, workload, *, steps, warmup, exact=False
     replays = max(1, math.ceil(steps / S))
 
     def rotation_ms(g):
-        """Average step time over replays of an S-step graph (one warm replay first)."""
+        """Average step time over replays of an S-step graph (one warm replay first): the
+        median of three timed samples, so that one stall of the box does not become the
+        line."""
         timer(g.replay)
-        return timer(lambda: [g.replay() for _ in range(replays)]) / (replays * S)
+        samples = [timer(lambda: [g.replay() for _ in range(replays)]) / (replays * S)
+                   for _ in range(3)]
+        return float(np.median(samples))
 
     # eager warm-up (loads the code objects); the router's scores of every step, for
     # the FFN-alone timing and the realised unions
