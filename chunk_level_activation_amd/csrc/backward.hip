@@ -364,6 +364,156 @@ __global__ void __launch_bounds__(kPassThreads, 4) expert_pass_kernel(PassArgs a
         a.ds[tok[tid] * d.E + e] = dsacc[tid];
 }
 
+// For few tiles (a backward of a decode-sized batch) the expert pass above would run
+// one workgroup per expert and leave most CUs idle. Here each workgroup takes 32 of
+// the expert's hidden units, so there are d_e / 32 times as many: waves 0-3 form
+// a = X W1_e^T and waves 4-7 G = DY W2_e for the 128 token rows x 32 units (one 32 x 32
+// block per wave, two k steps in flight), G goes to the first group through LDS, and
+// the epilogue is the one above. The workgroup's share of ds (its 32 units) goes to
+// slice ub of ds, [d_e / 32][T][E]; the router backward adds the slices in order.
+constexpr int kNarrowUnits = 32;
+constexpr int kNarrowGroup = kBT;             // 4 waves per product
+constexpr int kNarrowThreads = 2 * kNarrowGroup;
+
+__global__ void __launch_bounds__(kNarrowThreads, 2) expert_pass_narrow_kernel(PassArgs a)
+{
+    const Dims &d = a.d;
+    const int nub = d.d_e / kNarrowUnits;
+    const int e = blockIdx.x % d.E;
+    const int rest = blockIdx.x / d.E;
+    const int ub = rest % nub, grp = rest / nub;
+    const int cnt = a.tile_count[e];
+    if (grp * kPassTiles >= cnt)
+        return;
+    __shared__ alignas(16) uint16_t As[2][2][kTM * kPP];            // [group][buffer] token rows
+    __shared__ alignas(16) uint16_t Bs[2][2][kNarrowUnits * kPP];   // [group][buffer] unit rows
+    __shared__ float gbuf[16][kNarrowGroup];                         // G of group 1
+    __shared__ float red[kTM][kNarrowUnits + 1];
+    __shared__ float scol[kTM];
+    __shared__ int64_t tok[kTM];
+    __shared__ int tiles[kPassTiles];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    const int g = __builtin_amdgcn_readfirstlane(wave >> 2);   // 0: X W1^T, 1: DY W2
+    const int gt = tid & (kNarrowGroup - 1);
+    const int wm = wave & 3;                                   // 32-row tile
+    const int col = lane & 31, kg = lane >> 5;
+    if (tid < kPassTiles)
+        tiles[tid] = grp * kPassTiles + tid < cnt ? a.tile_list[(int64_t)e * d.CT + grp * kPassTiles + tid] : -1;
+    __syncthreads();
+    if (tid < kTM) {
+        const int64_t t = tile_token(d, tiles[tid / kTileM], tid % kTileM);
+        tok[tid] = t;
+        scol[tid] = t >= 0 ? a.scores[t * d.E + e] : 0.0f;
+    }
+    __syncthreads();
+
+    const __amdgpu_buffer_rsrc_t rA = make_rsrc(g ? a.dy : a.x, (uint64_t)d.T * d.d_h * 2);
+    const __amdgpu_buffer_rsrc_t rB = make_rsrc(g ? a.w2t : a.w1, (uint64_t)d.E * d.d_e * d.d_h * 2);
+    // per k step: A pieces gt + 256 i (row q / 8, k (q % 8) * 8) of the 128 x 64 token
+    // tile, and B piece gt (row gt / 8) of the 32 x 64 unit tile
+    uint32_t aoff[4], amask[4];
+    int arow[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = gt + i * kNarrowGroup;
+        arow[i] = q >> 3;
+        const int64_t t = tok[arow[i]];
+        amask[i] = 0u - (uint32_t)(t >= 0);
+        aoff[i] = t >= 0 ? (uint32_t)((t * d.d_h + (q & 7) * 8) * 2) : 0u;
+    }
+    const int acol = (gt & 7) * 8, brow = gt >> 3;
+    const uint32_t boff = (uint32_t)((((int64_t)e * d.d_e + ub * kNarrowUnits + brow) * d.d_h + acol) * 2);
+    const int KS = d.d_h / kPK;
+    f32x16 acc;
+    zero_acc(acc);
+    {
+        u32x4 ra[kPassDepth][4], rb[kPassDepth];
+        auto issue = [&](int st, int dd) {
+            const uint32_t okm = 0u - (uint32_t)(st < KS);
+            const uint32_t kb = (uint32_t)(st * kPK * 2);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const uint32_t am = okm & amask[i];
+                ra[dd][i] = load16(rA, ((aoff[i] + kb) & am) | (kOOB & ~am));
+            }
+            rb[dd] = load16(rB, ((boff + kb) & okm) | (kOOB & ~okm));
+        };
+#pragma unroll
+        for (int dd = 0; dd < kPassDepth; ++dd) {
+            issue(dd, dd);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        for (int s0 = 0; s0 < KS; s0 += kPassDepth) {
+#pragma unroll
+            for (int dd = 0; dd < kPassDepth; ++dd) {
+                const int buf = dd & 1;
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    *reinterpret_cast<u32x4 *>(&As[g][buf][arow[i] * kPP + ((gt + i * kNarrowGroup) & 7) * 8]) =
+                        ra[dd][i];
+                *reinterpret_cast<u32x4 *>(&Bs[g][buf][brow * kPP + acol]) = rb[dd];
+                __syncthreads();
+                issue(s0 + dd + kPassDepth, dd);
+#pragma unroll
+                for (int ks = 0; ks < kPK / 16; ++ks) {
+                    const bf16x8 fa =
+                        *reinterpret_cast<const bf16x8 *>(&As[g][buf][(wm * 32 + col) * kPP + ks * 16 + kg * 8]);
+                    const bf16x8 fb =
+                        *reinterpret_cast<const bf16x8 *>(&Bs[g][buf][col * kPP + ks * 16 + kg * 8]);
+                    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+                }
+            }
+        }
+    }
+    if (g == 1) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+            gbuf[v][gt] = acc[v];
+    }
+    __syncthreads();
+    if (g == 0) {
+        // element v: row acc_row(v) of tile wm, unit ub * 32 + col
+        const int tile = __builtin_amdgcn_readfirstlane(tiles[wm]);
+        const int unit = ub * kNarrowUnits + col;
+        if (tile >= 0) {
+            const int64_t blk = ((int64_t)tile * d.E + e) * kTileM * d.d_e;
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+                uint32_t da_pk[2] = {0u, 0u}, sh_pk[2] = {0u, 0u};
+                const int r0 = acc_row(vg * 4, lane);   // 4 consecutive rows of the tile
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int v = vg * 4 + q, r = r0 + q;
+                    const float av = acc[v], s = scol[wm * 32 + r], gv = gbuf[v][gt];
+                    const float sig = 1.0f / (1.0f + expf(-av));
+                    const float h = av * sig;
+                    red[wm * 32 + r][col] = gv * h;
+                    const float dA = s * gv * (sig * (1.0f + av * (1.0f - sig)));
+                    const uint32_t b_da = f32_to_bf16(dA), b_sh = f32_to_bf16(s * h);
+                    da_pk[q >> 1] |= b_da << ((q & 1) * 16);
+                    sh_pk[q >> 1] |= b_sh << ((q & 1) * 16);
+                    a.da_tu[blk + (int64_t)r * d.d_e + unit] = (uint16_t)b_da;
+                }
+                const int64_t o = blk + (int64_t)unit * kTileM + r0;
+                *reinterpret_cast<uint64_t *>(&a.da_ut[o]) = (uint64_t)da_pk[0] | ((uint64_t)da_pk[1] << 32);
+                *reinterpret_cast<uint64_t *>(&a.sh_ut[o]) = (uint64_t)sh_pk[0] | ((uint64_t)sh_pk[1] << 32);
+            }
+        } else {
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                red[wm * 32 + acc_row(v, lane)][col] = 0.0f;
+        }
+    }
+    __syncthreads();
+    // this unit block's share of ds, summed over its 32 units in order
+    if (tid < kTM && tok[tid] >= 0) {
+        float sum = 0.0f;
+        for (int c = 0; c < kNarrowUnits; ++c)
+            sum += red[tid][c];
+        a.ds[((int64_t)ub * d.T + tok[tid]) * d.E + e] = sum;
+    }
+}
+
 // ------------------------------------------------------------------ 3. weight gradients
 struct WgradArgs {
     const uint16_t *xt, *dyt;             // [CT][d_h][32]
@@ -568,11 +718,13 @@ __global__ void __launch_bounds__(kBT) dx_reduce_kernel(DxArgs a)
 struct RouterArgs {
     const uint16_t *x, *w_r;
     const float *gain, *dprobs;
-    const float *logits, *scores, *ds;    // [T][E]
+    const float *logits, *scores;        // [T][E]
+    const float *ds;                      // [ds_splits][T][E]: slices added in order
     const uint64_t *masks;                // [C][W]
     float *dl, *gt;                       // [T][E]
     float *dx, *dw_r, *dgain, *dbias;
     float eps, sharpness;
+    int ds_splits;
     Dims d;
 };
 
@@ -614,7 +766,8 @@ __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
             ds[i] = 0.0f;
             if (ve) {
                 if ((a.masks[(int64_t)c * d.W + (e >> 6)] >> (e & 63)) & 1ull)
-                    ds[i] = a.ds[t * d.E + e];
+                    for (int q = 0; q < a.ds_splits; ++q)
+                        ds[i] += a.ds[((int64_t)q * d.T + t) * d.E + e];
                 if (a.dprobs) {
                     const float p = 1.0f / (1.0f + expf(-a.sharpness * a.scores[t * d.E + e]));
                     ds[i] += a.dprobs[t * d.E + e] * a.sharpness * p * (1.0f - p);
@@ -814,10 +967,17 @@ struct BwdLayout {
     size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, w1t, w2t, dx_part;
     size_t router;        // the forward router's split workspace (0 bytes when it takes none)
     int dx_splits;
+    int ds_splits;        // 1, or d_e / 32 with the narrow expert pass
     size_t total;
 };
 
 constexpr int kDxTargetBlocks = 256;
+
+// The narrow expert pass when the (expert, 4 tiles) workgroups would not fill the CUs.
+bool pass_narrow(int64_t E, int64_t CT, int64_t d_e)
+{
+    return E * ((CT + kPassTiles - 1) / kPassTiles) < 256 && d_e % kNarrowUnits == 0;
+}
 
 // Expert splits of the dx products: enough workgroups for one per CU.
 int dx_splits(int64_t CT, int64_t d_h, int64_t E)
@@ -849,7 +1009,8 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
     L.tile_count = take(4 * E);
     L.logits = take(4 * T * E);
     L.scores = take(4 * T * E);
-    L.ds = take(4 * T * E);
+    L.ds_splits = pass_narrow(E, p.CT, d_e) ? (int)(d_e / kNarrowUnits) : 1;
+    L.ds = take(4 * (size_t)L.ds_splits * T * E);
     L.dl = take(4 * T * E);
     L.gt = take(4 * T * E);
     L.xt = take(2 * p.CT * d_h * kTileM);
@@ -953,7 +1114,11 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     pa.sh_ut = reinterpret_cast<uint16_t *>(at(L.sh_ut));
     pa.d = d;
     const int64_t pass_blocks = b.E * ((p.CT + kPassTiles - 1) / kPassTiles);
-    hipLaunchKernelGGL(expert_pass_kernel, dim3((unsigned)pass_blocks), dim3(kPassThreads), 0, stream, pa);
+    if (L.ds_splits > 1)
+        hipLaunchKernelGGL(expert_pass_narrow_kernel, dim3((unsigned)(pass_blocks * L.ds_splits)),
+                           dim3(kNarrowThreads), 0, stream, pa);
+    else
+        hipLaunchKernelGGL(expert_pass_kernel, dim3((unsigned)pass_blocks), dim3(kPassThreads), 0, stream, pa);
 
     WgradArgs wa;
     wa.xt = xt;
@@ -1003,6 +1168,7 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     ra.dbias = b.dbias;
     ra.eps = b.eps;
     ra.sharpness = b.sharpness;
+    ra.ds_splits = L.ds_splits;
     ra.d = d;
     hipLaunchKernelGGL(router_token_kernel, dim3((unsigned)((b.T + kRtTokens - 1) / kRtTokens)), dim3(kBT), 0,
                        stream, ra);
