@@ -725,16 +725,18 @@ struct RouterArgs {
     float *dx, *dw_r, *dgain, *dbias;
     float eps, sharpness;
     int ds_splits;
+    int rt_slices;                        // 256-column slices of dx per router-token workgroup
     Dims d;
 };
 
 constexpr int kRtTokens = 4;              // tokens per router-token workgroup (one per wave)
 constexpr int kRtPer = 256 / kWave;       // experts per lane (E <= 256)
+constexpr int kRtCols = 256;              // d_h columns of dx per router-token workgroup
+constexpr int kRtPieces = kRtCols / 8;    // 8-column pieces: 32
+constexpr int kRtGroups = kBT / kRtPieces;   // expert groups: 8
+static_assert(kRtGroups * kRtPieces == kBT, "thread = (piece, expert group)");
+constexpr int64_t kRtMinBlocks = 512;
 
-// Per token (one wavefront each, kRtTokens per workgroup): ds (masked to the chunk's
-// union, plus the probability term), the RMSNorm and ReLU backward -> dl, and the gain
-// term; then dx[t] += W_r^T dl for the workgroup's tokens, each W_r row loaded once for
-// all of them (experts in order, eight rows in flight).
 // p[0 .. n) = 0 (the recomputed router's arrival counters: this workspace is not
 // zero-filled by the caller)
 __global__ void __launch_bounds__(kBT) zero_words_kernel(uint32_t *p, int64_t n)
@@ -744,11 +746,21 @@ __global__ void __launch_bounds__(kBT) zero_words_kernel(uint32_t *p, int64_t n)
         p[i] = 0u;
 }
 
+// Per token (one wavefront each, kRtTokens per workgroup): ds (masked to the chunk's
+// union, plus the probability term), the RMSNorm and ReLU backward -> dl, and the gain
+// term; then dx[t] += W_r^T dl for the workgroup's tokens, each W_r row piece loaded
+// once for all of them. !SPLIT: one workgroup per token group, over all of d_h. SPLIT
+// (few token groups): one workgroup per token group and run of rt_slices 256-column
+// slices of d_h, so that more workgroups share the W_r stream; the first run writes dl
+// and the gain term.
+template <bool SPLIT>
 __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
 {
     const Dims &d = a.d;
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int64_t t0 = (int64_t)blockIdx.x * kRtTokens;
+    const int nsb = SPLIT ? d.d_h / kRtCols / a.rt_slices : 1;   // slice blocks per token group
+    const int64_t t0 = (int64_t)(blockIdx.x / nsb) * kRtTokens;
+    const int slice0 = (blockIdx.x % nsb) * a.rt_slices;
     __shared__ float dl_s[kRtTokens][256];
     {
         const int64_t t = t0 + wave;
@@ -787,7 +799,7 @@ __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
             const float dr = g[i] * inv * ds[i] - inv * inv * inv * r[i] / (float)d.E * coup;
             const float dl = l[i] > 0.0f ? dr : 0.0f;
             dl_s[wave][e] = dl;
-            if (vt && e < d.E) {
+            if (vt && e < d.E && slice0 == 0) {
                 a.dl[t * d.E + e] = dl;
                 a.gt[t * d.E + e] = ds[i] * r[i] * inv;
             }
@@ -795,41 +807,106 @@ __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
     }
     __syncthreads();
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w_r, (uint64_t)d.E * d.d_h * 2);
-    for (int jv = tid; jv < d.d_h / 8; jv += kBT) {
-        float acc[kRtTokens][8];
+    if constexpr (!SPLIT) {
+        // dx[t] += W_r^T dl, all of d_h: thread -> 8 columns, the experts in order
+        for (int jv = tid; jv < d.d_h / 8; jv += kBT) {
+            float acc[kRtTokens][8];
 #pragma unroll
-        for (int k = 0; k < kRtTokens; ++k)
+            for (int k = 0; k < kRtTokens; ++k)
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                acc[k][q] = 0.0f;
-        for (int k0 = 0; k0 < d.E; k0 += 8) {
-            u32x4 w[8];
+                for (int q = 0; q < 8; ++q)
+                    acc[k][q] = 0.0f;
+            for (int k0 = 0; k0 < d.E; k0 += 8) {
+                u32x4 w[8];
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
-                w[u] = load16(rw, k0 + u < d.E ? (uint32_t)((((int64_t)(k0 + u)) * d.d_h + jv * 8) * 2) : kOOB);
+                for (int u = 0; u < 8; ++u)
+                    w[u] = load16(rw, k0 + u < d.E ? (uint32_t)((((int64_t)(k0 + u)) * d.d_h + jv * 8) * 2) : kOOB);
 #pragma unroll
-            for (int u = 0; u < 8; ++u)
+                for (int u = 0; u < 8; ++u)
 #pragma unroll
-                for (int k = 0; k < kRtTokens; ++k) {
-                    const float dk = k0 + u < d.E ? dl_s[k][k0 + u] : 0.0f;
+                    for (int k = 0; k < kRtTokens; ++k) {
+                        const float dk = k0 + u < d.E ? dl_s[k][k0 + u] : 0.0f;
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        acc[k][2 * q] = fmaf(dk, __uint_as_float(w[u][q] << 16), acc[k][2 * q]);
-                        acc[k][2 * q + 1] = fmaf(dk, __uint_as_float(w[u][q] & 0xffff0000u), acc[k][2 * q + 1]);
+                        for (int q = 0; q < 4; ++q) {
+                            acc[k][2 * q] = fmaf(dk, __uint_as_float(w[u][q] << 16), acc[k][2 * q]);
+                            acc[k][2 * q + 1] = fmaf(dk, __uint_as_float(w[u][q] & 0xffff0000u), acc[k][2 * q + 1]);
+                        }
+                    }
+            }
+#pragma unroll
+            for (int k = 0; k < kRtTokens; ++k) {
+                const int64_t t = t0 + k;
+                if (t >= d.T)
+                    continue;
+                float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + jv * 8]);
+                float4 o0 = o[0], o1 = o[1];
+                o0.x += acc[k][0], o0.y += acc[k][1], o0.z += acc[k][2], o0.w += acc[k][3];
+                o1.x += acc[k][4], o1.y += acc[k][5], o1.z += acc[k][6], o1.w += acc[k][7];
+                o[0] = o0;
+                o[1] = o1;
+            }
+        }
+    } else {
+        // dx[t, slice columns] += W_r^T dl: thread (8-column piece pc, expert group eg) sums
+        // experts eg, eg + 8, ... (all of its W_r loads in flight at once); the 8 groups'
+        // partials are added in group order through LDS
+        __shared__ float part[kRtGroups][kRtTokens][kRtCols + 4];
+        const int pc = tid % kRtPieces, eg = tid / kRtPieces;
+        for (int slice = slice0; slice < slice0 + a.rt_slices; ++slice) {
+            const int j0 = slice * kRtCols + pc * 8;
+            float acc[kRtTokens][8];
+#pragma unroll
+            for (int k = 0; k < kRtTokens; ++k)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    acc[k][q] = 0.0f;
+            for (int e0 = eg; e0 < d.E; e0 += kRtGroups * 8) {
+                u32x4 w[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + u * kRtGroups;
+                    w[u] = load16(rw, e < d.E ? (uint32_t)(((int64_t)e * d.d_h + j0) * 2) : kOOB);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const int e = e0 + u * kRtGroups;
+#pragma unroll
+                    for (int k = 0; k < kRtTokens; ++k) {
+                        const float dk = e < d.E ? dl_s[k][e] : 0.0f;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            acc[k][2 * q] = fmaf(dk, __uint_as_float(w[u][q] << 16), acc[k][2 * q]);
+                            acc[k][2 * q + 1] = fmaf(dk, __uint_as_float(w[u][q] & 0xffff0000u), acc[k][2 * q + 1]);
+                        }
                     }
                 }
-        }
+            }
 #pragma unroll
-        for (int k = 0; k < kRtTokens; ++k) {
-            const int64_t t = t0 + k;
-            if (t >= d.T)
-                continue;
-            float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + jv * 8]);
-            float4 o0 = o[0], o1 = o[1];
-            o0.x += acc[k][0], o0.y += acc[k][1], o0.z += acc[k][2], o0.w += acc[k][3];
-            o1.x += acc[k][4], o1.y += acc[k][5], o1.z += acc[k][6], o1.w += acc[k][7];
-            o[0] = o0;
-            o[1] = o1;
+            for (int k = 0; k < kRtTokens; ++k)
+#pragma unroll
+                for (int q = 0; q < 8; ++q)
+                    part[eg][k][pc * 8 + q] = acc[k][q];
+            __syncthreads();
+            // thread -> (token k, 4 columns c4): the groups in order, then dx += the sum
+            for (int v = tid; v < kRtTokens * kRtCols / 4; v += kBT) {
+                const int k = v / (kRtCols / 4), c4 = (v % (kRtCols / 4)) * 4;
+                const int64_t t = t0 + k;
+                if (t >= d.T)
+                    continue;
+                float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+                for (int g = 0; g < kRtGroups; ++g) {
+                    sum.x += part[g][k][c4];
+                    sum.y += part[g][k][c4 + 1];
+                    sum.z += part[g][k][c4 + 2];
+                    sum.w += part[g][k][c4 + 3];
+                }
+                float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + slice * kRtCols + c4]);
+                float4 o0 = *o;
+                o0.x += sum.x, o0.y += sum.y, o0.z += sum.z, o0.w += sum.w;
+                *o = o0;
+            }
+            __syncthreads();   // part is refilled by the next slice
         }
     }
 }
@@ -1170,8 +1247,21 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     ra.sharpness = b.sharpness;
     ra.ds_splits = L.ds_splits;
     ra.d = d;
-    hipLaunchKernelGGL(router_token_kernel, dim3((unsigned)((b.T + kRtTokens - 1) / kRtTokens)), dim3(kBT), 0,
-                       stream, ra);
+    // a long batch: one workgroup per token group over all of d_h; a short one: the
+    // columns split into 256-column slices, rt_slices of them per workgroup, as many as
+    // keep at least kRtMinBlocks workgroups
+    const int64_t tgroups = (b.T + kRtTokens - 1) / kRtTokens, nslice = b.d_h / kRtCols;
+    ra.rt_slices = 1;
+    if (tgroups >= kRtMinBlocks) {
+        ra.rt_slices = (int)nslice;
+        hipLaunchKernelGGL(router_token_kernel<false>, dim3((unsigned)tgroups), dim3(kBT), 0, stream, ra);
+    } else {
+        while (ra.rt_slices < nslice && nslice % (2 * ra.rt_slices) == 0 &&
+               tgroups * (nslice / (2 * ra.rt_slices)) >= kRtMinBlocks)
+            ra.rt_slices *= 2;
+        hipLaunchKernelGGL(router_token_kernel<true>, dim3((unsigned)(tgroups * (nslice / ra.rt_slices))),
+                           dim3(kBT), 0, stream, ra);
+    }
     const int splits = router_param_splits(b.T, b.d_h, b.E);
     float *rp = reinterpret_cast<float *>(at(L.rp_part));
     const unsigned eb = (unsigned)((b.E + kRpE - 1) / kRpE), jb = (unsigned)(b.d_h / kBT);

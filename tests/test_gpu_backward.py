@@ -67,6 +67,9 @@ CASES = [
     ("multi-chunk E=40", 7, 128, 512, 40, 128, 32, True, True, False, False, 1.0),
     # enough tiles that dx runs one workgroup per (4 tiles, 128 columns), no expert split
     ("many tiles, unsplit dx", 10, 16384, 256, 4, 128, 32, False, False, False, False, 1.0),
+    # 300 token groups (the last one of 2 tokens) over 4 column slices: the router's dx
+    # runs two 256-column slices per workgroup
+    ("router dx in slice runs", 11, 1198, 1024, 16, 128, 32, True, False, False, False, 1.0),
 ]
 
 
