@@ -573,6 +573,7 @@ blockffn_status_t blockffn_layer_backward(const void *x, const void *w_r, const 
     b.dbias = dbias;
     b.dw1 = dw1;
     b.dw2 = dw2;
+    b.xcds = placement_xcds(static_cast<hipStream_t>(stream));
     const hipError_t err =
         blockffn::launch_layer_backward(b, workspace, static_cast<hipStream_t>(stream));
     if (err != hipSuccess)

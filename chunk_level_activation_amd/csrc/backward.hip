@@ -912,128 +912,179 @@ __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
 }
 
 constexpr int kRpE = 8;       // experts per router-parameter workgroup
-constexpr int kRpTargetBlocks = 1024;
+constexpr int kRpTargetBlocks = 512;
+constexpr int kRpMaxSplits = 16;
 
-// Token splits of the router-parameter sums: enough workgroups to fill the chip,
-// at least 32 tokens per split.
+// Token splits of the router-parameter sums: about kRpTargetBlocks workgroups (two per
+// CU), at most kRpMaxSplits splits, at least 32 tokens per split.
 int router_param_splits(int64_t T, int64_t d_h, int64_t E)
 {
     const int64_t base = ((E + kRpE - 1) / kRpE) * (d_h / kBT);
     int64_t s = (kRpTargetBlocks + base - 1) / base;
-    const int64_t smax = (T + 31) / 32;
+    int64_t smax = (T + 31) / 32;
+    if (smax > kRpMaxSplits)
+        smax = kRpMaxSplits;
     if (s > smax)
         s = smax;
     return s < 1 ? 1 : (int)s;
 }
 
-// Partial dW_r over token split z: part[z][e][j] = sum_{t in split z} dl[t][e] x[t][j],
-// tokens in order.
-__global__ void __launch_bounds__(kBT) router_param_kernel(RouterArgs a, int splits, float *part)
+constexpr int kRpTok = 128;   // tokens of dl (and gt) staged in LDS at a time
+constexpr int kRpLanes = 8;   // token lanes: thread = (8-column piece, token lane)
+constexpr int kRpCols = 256;  // columns per router-parameter workgroup
+static_assert((kRpCols / 8) * kRpLanes == kBT, "thread = (piece, token lane)");
+
+// Partial sums over token split z, tokens ascending within each token lane:
+//   part[z][e][j] = sum_{t in z} dl[t][e] x[t][j]      (dW_r)
+//   gpart[z][e]   = (sum_{t in z} gt[t][e], sum_{t in z} dl[t][e])   (dgain, dbias)
+// Thread (piece pc, token lane tl) takes 8 columns of x (one 16-byte load per token)
+// over the tokens tl, tl + 8, ... of the split, 8 of them in flight; the 8 lanes are
+// added in lane order through LDS. The workgroups of column block 0 also sum gt and
+// dl per expert (thread (expert tid % 8, slice tid / 8 of 32), slices in order).
+__global__ void __launch_bounds__(kBT) router_param_kernel(RouterArgs a, int splits, float *part,
+                                                           float *gpart)
 {
     const Dims &d = a.d;
-    const int e0 = blockIdx.x * kRpE, j = blockIdx.y * kBT + threadIdx.x, z = blockIdx.z;
+    const int e0 = blockIdx.x * kRpE, jb = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
     const int64_t per = (d.T + splits - 1) / splits;
     const int64_t t0 = z * per, t1 = t0 + per < d.T ? t0 + per : d.T;
-    // dl[t][e0 .. e0+8) of 128 tokens at a time staged in LDS (read back as broadcasts);
-    // x of 16 tokens in flight at a time
-    __shared__ float dls[128][kRpE];
-    const int tid = threadIdx.x;
-    float acc[kRpE];
+    __shared__ alignas(16) float dls[kRpTok][kRpE];
+    __shared__ float gts[kRpTok][kRpE];
+    __shared__ float red[kRpLanes][kRpE][kRpCols + 4];
+    const int pc = tid % (kRpCols / 8), tl = tid / (kRpCols / 8);
+    const int j0 = jb * kRpCols + pc * 8;
+    const int gq = tid % kRpE, gsl = tid / kRpE;
+    float acc[kRpE][8];
 #pragma unroll
     for (int q = 0; q < kRpE; ++q)
-        acc[q] = 0.0f;
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)d.T * d.d_h * 2);
-    for (int64_t tb = t0; tb < t1; tb += 128) {
-        {
-            const int64_t t = tb + tid / 2;
-            const int q0 = (tid % 2) * 4;
 #pragma unroll
-            for (int q = 0; q < 4; ++q)
-                dls[tid / 2][q0 + q] = (t < t1 && e0 + q0 + q < d.E) ? a.dl[t * d.E + e0 + q0 + q] : 0.0f;
-        }
-        __syncthreads();
-        const int nt = (int)(t1 - tb < 128 ? t1 - tb : 128);
-        for (int u0 = 0; u0 < nt; u0 += 16) {
-            float xv[16];
-#pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const uint32_t off = u0 + u < nt ? (uint32_t)(((tb + u0 + u) * d.d_h + j) * 2) : kOOB;
-                xv[u] = __uint_as_float((uint32_t)__builtin_amdgcn_raw_buffer_load_b16(rx, (int)off, 0, 0)
-                                        << 16);
-            }
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-#pragma unroll
-                for (int q = 0; q < kRpE; ++q)
-                    acc[q] = fmaf(dls[u0 + u][q], xv[u], acc[q]);
-        }
-        __syncthreads();
-    }
-#pragma unroll
-    for (int q = 0; q < kRpE; ++q)
-        if (e0 + q < d.E)
-            part[((int64_t)z * d.E + e0 + q) * d.d_h + j] = acc[q];
-}
-
-// dW_r = the splits' partials added in split order; the workgroups of column block 0
-// also sum dgain and dbias (thread = (expert q = tid % 8, token slice tid / 8 of 32),
-// then the 32 slices in order).
-__global__ void __launch_bounds__(kBT) router_param_reduce_kernel(RouterArgs a, int splits,
-                                                                  const float *part)
-{
-    const Dims &d = a.d;
-    const int e0 = blockIdx.x * kRpE, j = blockIdx.y * kBT + threadIdx.x, tid = threadIdx.x;
-    // the kRpE experts' partials of up to 16 splits requested together, then added in
-    // split order (experts past E and splits past `splits` read zero and are not added)
-    const __amdgpu_buffer_rsrc_t rpp = make_rsrc(part, (uint64_t)splits * d.E * d.d_h * 4);
-    for (int z0 = 0; z0 < splits; z0 += 16) {
-        float pv[16][kRpE];
-#pragma unroll
-        for (int z = 0; z < 16; ++z)
-#pragma unroll
-            for (int q = 0; q < kRpE; ++q) {
-                const bool ok = z0 + z < splits && e0 + q < d.E;
-                pv[z][q] = __builtin_bit_cast(
-                    float, __builtin_amdgcn_raw_buffer_load_b32(
-                               rpp, ok ? (int)((((int64_t)(z0 + z) * d.E + e0 + q) * d.d_h + j) * 4) : (int)kOOB, 0, 0));
-            }
-#pragma unroll
-        for (int q = 0; q < kRpE; ++q)
-            if (e0 + q < d.E) {
-                float sum = z0 == 0 ? 0.0f : a.dw_r[(int64_t)(e0 + q) * d.d_h + j];
-#pragma unroll
-                for (int z = 0; z < 16; ++z)
-                    if (z0 + z < splits)
-                        sum += pv[z][q];
-                a.dw_r[(int64_t)(e0 + q) * d.d_h + j] = sum;
-            }
-    }
-    if (blockIdx.y != 0)
-        return;
-    __shared__ float pg[kBT], pb[kBT];
-    const int q = tid % kRpE, sl = tid / kRpE;
+        for (int c = 0; c < 8; ++c)
+            acc[q][c] = 0.0f;
     float sg = 0.0f, sb = 0.0f;
-    if (e0 + q < d.E) {
-#pragma unroll 16
-        for (int64_t t = sl; t < d.T; t += kBT / kRpE) {
-            sg += a.gt[t * d.E + e0 + q];
-            sb += a.dl[t * d.E + e0 + q];
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, (uint64_t)d.T * d.d_h * 2);
+    for (int64_t tb = t0; tb < t1; tb += kRpTok) {
+        const int nt = (int)(t1 - tb < kRpTok ? t1 - tb : kRpTok);
+        {
+            const int u = tid / 2, q0 = (tid % 2) * 4;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const bool ok = u < nt && e0 + q0 + q < d.E;
+                const int64_t o = (tb + u) * d.E + e0 + q0 + q;
+                dls[u][q0 + q] = ok ? a.dl[o] : 0.0f;
+                if (jb == 0)
+                    gts[u][q0 + q] = ok ? a.gt[o] : 0.0f;
+            }
+        }
+        __syncthreads();
+        if (jb == 0)
+            for (int u = gsl; u < nt; u += kBT / kRpE) {
+                sg += gts[u][gq];
+                sb += dls[u][gq];
+            }
+        for (int u0 = tl; u0 < nt; u0 += kRpLanes * 8) {
+            u32x4 xv[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int u = u0 + i * kRpLanes;
+                xv[i] = load16(rx, u < nt ? (uint32_t)(((tb + u) * d.d_h + j0) * 2) : kOOB);
+            }
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int u = u0 + i * kRpLanes;
+                if (u < nt) {
+                    const float4 dA = *reinterpret_cast<const float4 *>(&dls[u][0]);
+                    const float4 dB = *reinterpret_cast<const float4 *>(&dls[u][4]);
+                    const float dv[kRpE] = {dA.x, dA.y, dA.z, dA.w, dB.x, dB.y, dB.z, dB.w};
+#pragma unroll
+                    for (int q = 0; q < kRpE; ++q)
+#pragma unroll
+                        for (int c = 0; c < 4; ++c) {
+                            acc[q][2 * c] = fmaf(dv[q], __uint_as_float(xv[i][c] << 16), acc[q][2 * c]);
+                            acc[q][2 * c + 1] =
+                                fmaf(dv[q], __uint_as_float(xv[i][c] & 0xffff0000u), acc[q][2 * c + 1]);
+                        }
+                }
+            }
+        }
+        __syncthreads();
+    }
+#pragma unroll
+    for (int q = 0; q < kRpE; ++q)
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            red[tl][q][pc * 8 + c] = acc[q][c];
+    float *const pg = &red[0][0][0], *const pb = pg + kBT;   // reused after the lane sums
+    __syncthreads();
+    // thread -> (expert q, 8 columns): the token lanes in order
+    {
+        const int q = tid / (kRpCols / 8), c0 = (tid % (kRpCols / 8)) * 8;
+        float sum[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            sum[c] = 0.0f;
+#pragma unroll
+        for (int l = 0; l < kRpLanes; ++l)
+#pragma unroll
+            for (int c = 0; c < 8; ++c)
+                sum[c] += red[l][q][c0 + c];
+        if (e0 + q < d.E) {
+            float4 *o = reinterpret_cast<float4 *>(&part[((int64_t)z * d.E + e0 + q) * d.d_h + jb * kRpCols + c0]);
+            o[0] = make_float4(sum[0], sum[1], sum[2], sum[3]);
+            o[1] = make_float4(sum[4], sum[5], sum[6], sum[7]);
         }
     }
+    if (jb != 0)
+        return;
+    __syncthreads();
     pg[tid] = sg;
     pb[tid] = sb;
     __syncthreads();
     if (tid < kRpE && e0 + tid < d.E) {
-        float g = 0.0f, b = 0.0f;
+        float g = 0.0f, bsum = 0.0f;
         for (int s2 = 0; s2 < kBT / kRpE; ++s2) {
             g += pg[s2 * kRpE + tid];
-            b += pb[s2 * kRpE + tid];
+            bsum += pb[s2 * kRpE + tid];
         }
-        if (a.dgain)
-            a.dgain[e0 + tid] = g;
-        if (a.dbias)
-            a.dbias[e0 + tid] = b;
+        gpart[((int64_t)z * d.E + e0 + tid) * 2] = g;
+        gpart[((int64_t)z * d.E + e0 + tid) * 2 + 1] = bsum;
     }
+}
+
+// dW_r, dgain and dbias = the splits' partials added in split order: workgroup =
+// (expert e, 256 columns), thread = column, all of its ZC >= splits loads requested
+// together (past the last split they read zero and are not added). The workgroups of
+// column block 0 also add the expert's dgain and dbias partials.
+template <int ZC>
+__global__ void __launch_bounds__(kBT) router_param_reduce_kernel(RouterArgs a, int splits,
+                                                                  const float *part,
+                                                                  const float *gpart)
+{
+    const Dims &d = a.d;
+    const int e = blockIdx.x, j = blockIdx.y * kBT + threadIdx.x, tid = threadIdx.x;
+    const __amdgpu_buffer_rsrc_t rpp = make_rsrc(part, (uint64_t)splits * d.E * d.d_h * 4);
+    float pv[ZC];
+#pragma unroll
+    for (int z = 0; z < ZC; ++z)
+        pv[z] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       rpp, z < splits ? (int)((((int64_t)z * d.E + e) * d.d_h + j) * 4) : (int)kOOB, 0, 0));
+    float sum = 0.0f;
+#pragma unroll
+    for (int z = 0; z < ZC; ++z)
+        if (z < splits)
+            sum += pv[z];
+    a.dw_r[(int64_t)e * d.d_h + j] = sum;
+    if (blockIdx.y != 0 || tid != 0)
+        return;
+    float g = 0.0f, bsum = 0.0f;
+    for (int z = 0; z < splits; ++z) {
+        g += gpart[((int64_t)z * d.E + e) * 2];
+        bsum += gpart[((int64_t)z * d.E + e) * 2 + 1];
+    }
+    if (a.dgain)
+        a.dgain[e] = g;
+    if (a.dbias)
+        a.dbias[e] = bsum;
 }
 
 // ------------------------------------------------------------------ workspace layout
@@ -1041,7 +1092,7 @@ struct BwdLayout {
     FfnPlan p;
     size_t masks, lists, counts, tile_list, tile_count;
     size_t logits, scores, ds, dl, gt;
-    size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, w1t, w2t, dx_part;
+    size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, rp_gpart, w1t, w2t, dx_part;
     size_t router;        // the forward router's split workspace (0 bytes when it takes none)
     int dx_splits;
     int ds_splits;        // 1, or d_e / 32 with the narrow expert pass
@@ -1096,6 +1147,7 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
     L.da_ut = take(2 * p.CT * E * kTileM * d_e);
     L.sh_ut = take(2 * p.CT * E * kTileM * d_e);
     L.rp_part = take(4 * (size_t)router_param_splits(T, d_h, E) * E * d_h);
+    L.rp_gpart = take(8 * (size_t)router_param_splits(T, d_h, E) * E);
     L.router = take(router_workspace_bytes(T, d_h, E));
     L.w1t = take(2 * (size_t)E * d_e * d_h);
     L.w2t = take(2 * (size_t)E * d_e * d_h);
@@ -1144,7 +1196,7 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
                            static_cast<uint32_t *>(rws), tiles);
     }
     hipError_t err = launch_router_bf16(b.x, b.w_r, b.gain, b.bias, b.eps, b.T, b.d_h, b.E, scores,
-                                        logits, 1.0f, nullptr, rws, 0, stream);
+                                        logits, 1.0f, nullptr, rws, rws ? b.xcds : 0, stream);
     if (err != hipSuccess)
         return err;
     if ((err = launch_union(p, scores, ws, nullptr, nullptr, nullptr, stream)) != hipSuccess)
@@ -1264,11 +1316,23 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     }
     const int splits = router_param_splits(b.T, b.d_h, b.E);
     float *rp = reinterpret_cast<float *>(at(L.rp_part));
-    const unsigned eb = (unsigned)((b.E + kRpE - 1) / kRpE), jb = (unsigned)(b.d_h / kBT);
-    hipLaunchKernelGGL(router_param_kernel, dim3(eb, jb, (unsigned)splits), dim3(kBT), 0, stream,
-                       ra, splits, rp);
-    hipLaunchKernelGGL(router_param_reduce_kernel, dim3(eb, jb), dim3(kBT), 0, stream, ra,
-                       splits, static_cast<const float *>(rp));
+    float *rg = reinterpret_cast<float *>(at(L.rp_gpart));
+    const unsigned eb = (unsigned)((b.E + kRpE - 1) / kRpE);
+    hipLaunchKernelGGL(router_param_kernel, dim3(eb, (unsigned)(b.d_h / kRpCols), (unsigned)splits),
+                       dim3(kBT), 0, stream, ra, splits, rp, rg);
+    const dim3 rgrid((unsigned)b.E, (unsigned)(b.d_h / kBT));
+#define RP_REDUCE(ZC)                                                                        \
+    hipLaunchKernelGGL(router_param_reduce_kernel<ZC>, rgrid, dim3(kBT), 0, stream, ra, splits, \
+                       static_cast<const float *>(rp), static_cast<const float *>(rg))
+    if (splits <= 1)
+        RP_REDUCE(1);
+    else if (splits <= 4)
+        RP_REDUCE(4);
+    else if (splits <= 8)
+        RP_REDUCE(8);
+    else
+        RP_REDUCE(kRpMaxSplits);
+#undef RP_REDUCE
     return hipGetLastError();
 }
 

@@ -231,6 +231,7 @@ struct BackwardArgs {
     float eps, sharpness;
     int64_t T, d_h, E, d_e, n;
     float *dx, *dw_r, *dgain, *dbias, *dw1, *dw2;
+    int xcds;   // verified round-robin XCD count (0: unknown), for the recomputed router
 };
 hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t stream);
 
