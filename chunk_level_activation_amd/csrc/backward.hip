@@ -30,11 +30,13 @@
 //   3. wgrad_kernel, workgroup = (expert, dW1 or dW2, 128 x 128 output tile): k over the
 //      expert's tiles' tokens; every output element is owned by one workgroup (an
 //      expert no chunk uses gets zeros);
-//   4. dx_kernel, workgroup = (4 tiles, 128 columns, expert split): k over the union of
-//      the 4 chunks' unions x d_e, B = W1^T rows (W1 and W2 are transposed once per call
-//      into the workspace, for the experts some chunk uses, so every product reads
-//      k-contiguous operands); with few tiles the experts are split over workgroups
-//      and the fp32 partials added in split order;
+//   4. dx = sum_e dA_e W1_e, B = W1^T rows (W1 and W2 are transposed once per call into
+//      the workspace, for the experts some chunk uses, so every product reads
+//      k-contiguous operands). With two or more chunk tiles it is the forward's grouped
+//      down-projection (dA in the hidden rows' layout), with an fp32 result; with one
+//      tile, dx_kernel, workgroup = (4 tiles, 128 columns, expert split): k over the
+//      union of the 4 chunks' unions x d_e, the experts split over workgroups and the
+//      fp32 partials added in split order;
 //   5. router_token_kernel: per token, dl and the router's share of dx;
 //      router_param_kernel: dW_r, dgain, dbias as sums over the tokens in order.
 // Every sum runs in a fixed order, so equal inputs give equal bits.
@@ -1095,6 +1097,7 @@ struct BwdLayout {
     size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, rp_gpart, w1t, w2t, dx_part;
     size_t router;        // the forward router's split workspace (0 bytes when it takes none)
     int dx_splits;
+    bool dx_grouped;      // dx on the forward's grouped down-projection (two or more tiles)
     int ds_splits;        // 1, or d_e / 32 with the narrow expert pass
     size_t total;
 };
@@ -1151,8 +1154,11 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
     L.router = take(router_workspace_bytes(T, d_h, E));
     L.w1t = take(2 * (size_t)E * d_e * d_h);
     L.w2t = take(2 * (size_t)E * d_e * d_h);
+    L.dx_grouped = p.grouped;
     L.dx_splits = dx_splits(p.CT, d_h, E);
-    L.dx_part = take(L.dx_splits > 1 ? 4 * (size_t)L.dx_splits * p.CT * kTileM * d_h : 0);
+    L.dx_part = take(L.dx_grouped ? grouped_partial_bytes(p.CT, d_h)
+                     : L.dx_splits > 1 ? 4 * (size_t)L.dx_splits * p.CT * kTileM * d_h
+                                       : 0);
     L.total = off;
     L.p.off_masks = L.masks;
     L.p.off_lists = L.lists;
@@ -1262,22 +1268,31 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     const int64_t wblocks = b.E * 2 * (b.d_e / kTM) * (b.d_h / kTM);
     hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)wblocks), dim3(kBT), 0, stream, wa);
 
-    DxArgs xa;
-    xa.w1t = w1t;
-    xa.da_tu = pa.da_tu;
-    xa.masks = masks;
-    xa.dx = b.dx;
-    xa.part = reinterpret_cast<float *>(at(L.dx_part));
-    xa.splits = L.dx_splits;
-    xa.d = d;
-    hipLaunchKernelGGL(dx_kernel,
-                       dim3((unsigned)((p.CT + kXTiles - 1) / kXTiles), (unsigned)(b.d_h / kTM),
-                            (unsigned)L.dx_splits),
-                       dim3(kBT), 0, stream, xa);
-    if (L.dx_splits > 1) {
-        const int64_t nel = p.CT * kTileM * b.d_h;
-        hipLaunchKernelGGL(dx_reduce_kernel, dim3((unsigned)((nel + kBT - 1) / kBT)), dim3(kBT), 0,
-                           stream, xa);
+    if (L.dx_grouped) {
+        // two or more chunk tiles: dx = sum_e dA_e W1_e is the grouped down-projection's
+        // product (dA in the hidden rows' layout, W1^T in W2's), written in fp32
+        const hipError_t gerr = launch_grouped_down_f32(
+            p, pa.da_tu, w1t, masks, b.dx, reinterpret_cast<float *>(at(L.dx_part)), stream);
+        if (gerr != hipSuccess)
+            return gerr;
+    } else {
+        DxArgs xa;
+        xa.w1t = w1t;
+        xa.da_tu = pa.da_tu;
+        xa.masks = masks;
+        xa.dx = b.dx;
+        xa.part = reinterpret_cast<float *>(at(L.dx_part));
+        xa.splits = L.dx_splits;
+        xa.d = d;
+        hipLaunchKernelGGL(dx_kernel,
+                           dim3((unsigned)((p.CT + kXTiles - 1) / kXTiles), (unsigned)(b.d_h / kTM),
+                                (unsigned)L.dx_splits),
+                           dim3(kBT), 0, stream, xa);
+        if (L.dx_splits > 1) {
+            const int64_t nel = p.CT * kTileM * b.d_h;
+            hipLaunchKernelGGL(dx_reduce_kernel, dim3((unsigned)((nel + kBT - 1) / kBT)), dim3(kBT), 0,
+                               stream, xa);
+        }
     }
 
     RouterArgs ra;

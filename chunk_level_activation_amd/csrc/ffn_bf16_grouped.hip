@@ -65,6 +65,7 @@ struct GroupedArgs {
     int32_t *tile_list;          // [E][CT]
     int32_t *tile_count;         // [E]
     float *dn_part;              // [splits][CT * 32][d_h] when splits > 1
+    float *y32;                  // fp32 output instead of y (the layer backward's dx)
     int64_t T;
     int n, d_h, E, d_e, C, MPC, CT, W;
     int splits;
@@ -260,6 +261,9 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 }
 
 // ------------------------------------------------------------------ down (grouped GEMM)
+// F32: the result goes to y32 in fp32 (the same products serve the layer backward's
+// dx = sum_e dA_e W1_e, with dA in the hidden rows' layout and W1^T in W2's).
+template <bool F32>
 __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs a)
 {
     const int NCT = a.d_h / kDnCols;
@@ -400,15 +404,20 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
             const int64_t t = tile_token(a, tile, acc_row(v, lane));
-            if (t >= 0)
-                a.y[t * a.d_h + cidx] = f32_to_bf16(acc[j][v]);
+            if (t >= 0) {
+                if constexpr (F32)
+                    a.y32[t * a.d_h + cidx] = acc[j][v];
+                else
+                    a.y[t * a.d_h + cidx] = f32_to_bf16(acc[j][v]);
+            }
         }
     }
 }
 
 // ------------------------------------------------------------------ split sum
-// y[t][c] = bf16(sum over the splits, in order, of the partials of t's tile row);
-// thread -> 4 consecutive columns of one tile row.
+// y[t][c] = bf16(sum over the splits, in order, of the partials of t's tile row), or
+// the fp32 sum into y32 (F32); thread -> 4 consecutive columns of one tile row.
+template <bool F32>
 __global__ void __launch_bounds__(256) down_reduce_kernel(GroupedArgs a)
 {
     const int64_t q = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -428,6 +437,10 @@ __global__ void __launch_bounds__(256) down_reduce_kernel(GroupedArgs a)
         sum.y += v.y;
         sum.z += v.z;
         sum.w += v.w;
+    }
+    if constexpr (F32) {
+        *reinterpret_cast<float4 *>(a.y32 + t * a.d_h + c) = sum;
+        return;
     }
     const uint64_t packed = (uint64_t)f32_to_bf16(sum.x) | ((uint64_t)f32_to_bf16(sum.y) << 16) |
                             ((uint64_t)f32_to_bf16(sum.z) << 32) | ((uint64_t)f32_to_bf16(sum.w) << 48);
@@ -515,11 +528,43 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
     const int64_t up_blocks = p.E * ((p.CT + kUpTiles - 1) / kUpTiles);
     hipLaunchKernelGGL(up_grouped_kernel, dim3((unsigned)up_blocks), dim3(kGThreads), 0, stream, a);
     const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols) * a.splits;
-    hipLaunchKernelGGL(down_grouped_kernel, dim3((unsigned)dn_blocks), dim3(kGThreads), 0, stream,
-                       a);
+    hipLaunchKernelGGL(down_grouped_kernel<false>, dim3((unsigned)dn_blocks), dim3(kGThreads), 0,
+                       stream, a);
     if (a.splits > 1) {
         const int64_t q = p.CT * kTileM * (p.d_h / 4);
-        hipLaunchKernelGGL(down_reduce_kernel, dim3((unsigned)((q + 255) / 256)), dim3(256), 0, stream, a);
+        hipLaunchKernelGGL(down_reduce_kernel<false>, dim3((unsigned)((q + 255) / 256)), dim3(256), 0,
+                           stream, a);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_grouped_down_f32(const FfnPlan &p, const uint16_t *act, const uint16_t *w,
+                                   const uint64_t *masks, float *out, float *part,
+                                   hipStream_t stream)
+{
+    GroupedArgs a{};
+    a.hidden = const_cast<uint16_t *>(act);
+    a.w2 = w;
+    a.masks = masks;
+    a.y32 = out;
+    a.dn_part = part;
+    a.T = p.T;
+    a.n = (int)p.n;
+    a.d_h = (int)p.d_h;
+    a.E = (int)p.E;
+    a.d_e = (int)p.d_e;
+    a.C = (int)p.C;
+    a.MPC = (int)p.MPC;
+    a.CT = (int)p.CT;
+    a.W = (int)p.W;
+    a.splits = grouped_down_splits(p.CT, p.d_h);
+    const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols) * a.splits;
+    hipLaunchKernelGGL(down_grouped_kernel<true>, dim3((unsigned)dn_blocks), dim3(kGThreads), 0,
+                       stream, a);
+    if (a.splits > 1) {
+        const int64_t q = p.CT * kTileM * (p.d_h / 4);
+        hipLaunchKernelGGL(down_reduce_kernel<true>, dim3((unsigned)((q + 255) / 256)), dim3(256), 0,
+                           stream, a);
     }
     return hipGetLastError();
 }

@@ -58,6 +58,8 @@ def _check(inp, gain, bias, dy, dp, n, sharpness, got):
 
 CASES = [
     # (label, seed, T, d_h, E, d_e, n, dprobs, idle, no_gain, no_bias, sharpness)
+    # dx: with one chunk tile (one token, decode shape) dx_kernel with its expert split;
+    # with two or more, the grouped down-projection in fp32 (two tiles: k split in 4)
     ("two chunks, partial last", 1, 48, 256, 8, 128, 32, False, False, False, False, 1.0),
     ("n=48 tiles span chunks", 2, 100, 512, 16, 128, 48, True, False, False, False, 2.0),
     ("n=8", 3, 64, 256, 8, 128, 8, True, True, False, False, 1.0),
@@ -65,8 +67,8 @@ CASES = [
     ("one token, no bias", 5, 1, 256, 16, 128, 32, True, False, False, True, 1.0),
     ("decode shape", 6, 32, 2048, 64, 128, 32, True, False, False, False, 1.0),
     ("multi-chunk E=40", 7, 128, 512, 40, 128, 32, True, True, False, False, 1.0),
-    # enough tiles that dx runs one workgroup per (4 tiles, 128 columns), no expert split
-    ("many tiles, unsplit dx", 10, 16384, 256, 4, 128, 32, False, False, False, False, 1.0),
+    # enough tiles that the grouped dx fills the chip with one k range (256 tile pairs)
+    ("many tiles, dx in one k range", 10, 16384, 256, 4, 128, 32, False, False, False, False, 1.0),
     # 300 token groups (the last one of 2 tokens) over 4 column slices: the router's dx
     # runs two 256-column slices per workgroup
     ("router dx in slice runs", 11, 1198, 1024, 16, 128, 32, True, False, False, False, 1.0),
