@@ -20,8 +20,9 @@
 //      (few enough registers for two 8-wave workgroups per CU), 32x32x16 bf16 MFMA,
 //      then Swish and the score (staged in LDS with the rows' tokens); the bf16 hidden
 //      rows go to Ht[tile][e].
-//   4. down_grouped_kernel: workgroup = (2 chunk tiles, 256 output columns): a
-//      64 x 256 GEMM over k = the union of the two chunks' experts x d_e, ascending,
+//   4. down_grouped_kernel: workgroup = (2 or 4 chunk tiles, 256 output columns): a
+//      64 (128) x 256 GEMM over k = the union of the tiles' chunks' experts x d_e
+//      (four tiles where that does not raise the k split below), ascending,
 //      with the hidden rows of a tile whose chunk does not use the expert read as
 //      zero (those terms are exactly zero: the scores are zero there). Every output
 //      element is owned by one workgroup, so there is no cross-workgroup sum, and the
@@ -44,8 +45,6 @@ constexpr int kPitch = kKStep + 8;        // LDS row pitch (bf16): 144 bytes, co
 constexpr int kUpTiles = 4;               // chunk tiles (32 rows each) per up workgroup
 constexpr int kUpRows = kUpTiles * kTileM;    // 128
 constexpr int kUpCols = 128;              // hidden units per pass
-constexpr int kDnTiles = 2;               // chunk tiles per down workgroup
-constexpr int kDnRows = kDnTiles * kTileM;    // 64
 constexpr int kDnCols = 256;              // output columns per down workgroup
 constexpr int kMaxWords = 4;
 constexpr int kDepth = 4;                 // k steps whose loads are in flight ahead of use
@@ -261,50 +260,62 @@ __global__ void __launch_bounds__(kGThreads, 4) up_grouped_kernel(GroupedArgs a)
 }
 
 // ------------------------------------------------------------------ down (grouped GEMM)
+// Workgroup = (TILES consecutive chunk tiles, 256 output columns, k split): a
+// TILES*32 x 256 GEMM over k = the union of the tiles' chunks' experts x d_e. Wave
+// (wm, wn) holds rows wm * TILES * 16 .. (TILES / 2 blocks of 32) x columns wn * 64 ..
+// +64 (two blocks of 32). Four tiles halve the L2 bytes per product of two (48 KB of
+// operands per 4.2 MFLOP and k step, against 40 KB per 2.1), for a union of four
+// chunks instead of two.
 // F32: the result goes to y32 in fp32 (the same products serve the layer backward's
 // dx = sum_e dA_e W1_e, with dA in the hidden rows' layout and W1^T in W2's).
-template <bool F32>
+template <bool F32, int TILES>
 __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs a)
 {
+    static_assert(TILES == 2 || TILES == 4, "two or four chunk tiles per workgroup");
+    constexpr int ROWS = TILES * kTileM;              // 64 or 128
+    constexpr int RB = TILES / 2;                     // 32-row blocks per wave
+    constexpr int AC = ROWS * (kKStep / 8) / kGThreads;   // A chunks per thread and k step
     const int NCT = a.d_h / kDnCols;
-    const int NBT = (a.CT + kDnTiles - 1) / kDnTiles;
+    const int NBT = (a.CT + TILES - 1) / TILES;
     const int ct = blockIdx.x % NCT;
     const int bt = (blockIdx.x / NCT) % NBT;
     const int split = blockIdx.x / NCT / NBT;
-    __shared__ alignas(16) uint16_t As[2][kDnRows * kPitch];   // hidden rows x 64 units
+    __shared__ alignas(16) uint16_t As[2][ROWS * kPitch];      // hidden rows x 64 units
     __shared__ alignas(16) uint16_t Bs[2][kDnCols * kPitch];   // W2 rows (output columns) x 64 units
-    __shared__ uint64_t m_tile[kDnTiles][kMaxWords];
+    __shared__ uint64_t m_tile[TILES][kMaxWords];
     __shared__ int list[256];
     __shared__ int nlist;
 
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
-    const int wm = wave & 1, wn = wave >> 1;       // tile, 64-column quarter
+    const int wm = wave & 1, wn = wave >> 1;       // row half (RB blocks), 64-column quarter
     const int col = lane & 31, kg = lane >> 5;
-    int tile_of[kDnTiles];
-#pragma unroll
-    for (int i = 0; i < kDnTiles; ++i)
-        tile_of[i] = bt * kDnTiles + i < a.CT ? bt * kDnTiles + i : -1;
-    if (tid < kDnTiles * kMaxWords) {
-        const int i = tid / kMaxWords, w = tid % kMaxWords;
-        m_tile[i][w] = (tile_of[i] >= 0 && w < a.W) ? a.masks[(int64_t)(tile_of[i] / a.MPC) * a.W + w]
-                                                   : 0ull;
+    if (tid < TILES * kMaxWords) {
+        const int i = tid / kMaxWords, w = tid % kMaxWords, tile = bt * TILES + i;
+        m_tile[i][w] = (tile < a.CT && w < a.W) ? a.masks[(int64_t)(tile / a.MPC) * a.W + w] : 0ull;
     }
     __syncthreads();
     // ascending list of the experts of the union of the tiles' chunks
+    auto union_word = [&](int w) {
+        uint64_t u = 0ull;
+#pragma unroll
+        for (int i = 0; i < TILES; ++i)
+            u |= m_tile[i][w];
+        return u;
+    };
     if (tid < a.E) {
         const int w = tid >> 6, bit = tid & 63;
-        const uint64_t word = m_tile[0][w] | m_tile[1][w];
+        const uint64_t word = union_word(w);
         if ((word >> bit) & 1ull) {
             int pos = __popcll(word & ((1ull << bit) - 1ull));
             for (int v = 0; v < w; ++v)
-                pos += __popcll(m_tile[0][v] | m_tile[1][v]);
+                pos += __popcll(union_word(v));
             list[pos] = tid;
         }
     }
     if (tid == 0) {
         int c = 0;
         for (int w = 0; w < a.W; ++w)
-            c += __popcll(m_tile[0][w] | m_tile[1][w]);
+            c += __popcll(union_word(w));
         nlist = c;
     }
     __syncthreads();
@@ -312,25 +323,34 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
     const __amdgpu_buffer_rsrc_t rhid =
         make_rsrc(a.hidden, (uint64_t)a.CT * a.E * kTileM * a.d_e * 2);
     const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(a.w2, (uint64_t)a.E * a.d_h * a.d_e * 2);
-    // per thread per k step: 1 A chunk (64 rows x 8 chunks) and 4 B chunks (256 rows x 8)
-    const int arow = tid >> 3, acol = (tid & 7) * 8;
-    const int a_tile_i = arow / kTileM, a_r = arow % kTileM;
-    const int a_tile = tile_of[a_tile_i];
+    // per thread per k step: AC A chunks (ROWS rows x 8 chunks) and 4 B chunks (256 rows
+    // x 8); A chunk j is row (tid + 512 j) / 8
+    int arow[AC], acol[AC], a_ti[AC], a_tile[AC];
+#pragma unroll
+    for (int j = 0; j < AC; ++j) {
+        const int q = tid + j * kGThreads;
+        arow[j] = q >> 3;
+        acol[j] = (q & 7) * 8;
+        a_ti[j] = arow[j] / kTileM;
+        a_tile[j] = bt * TILES + a_ti[j] < a.CT ? bt * TILES + a_ti[j] : -1;
+    }
     const int DK = a.d_e / kKStep;
     // this split's contiguous range [st0, st1) of the k steps
     const int steps_all = nlist * DK;
     const int st0 = (int)((int64_t)split * steps_all / a.splits);
     const int st1 = (int)((int64_t)(split + 1) * steps_all / a.splits);
-    f32x16 acc[2];
+    f32x16 acc[RB][2];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v)
-            acc[j][v] = 0.0f;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int v = 0; v < 16; ++v)
+                acc[rb][j][v] = 0.0f;
 
     // kDepth k steps in flight: every load is issued (a tile whose chunk does not use
     // the expert, and steps past the end, read beyond the buffer and get zero)
-    bf16x8 ra[kDepth], rb[kDepth][4];
+    bf16x8 ra[kDepth][AC], rb[kDepth][4];
     auto issue = [&](int st, int d) {
         // branch-free: the list entry is read even past the end (masked to a valid
         // expert index) and the offsets are replaced afterwards
@@ -338,10 +358,13 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
         const int li = st / DK;
         const int e = list[li < 255 ? li : 255] & 255;
         const int k0 = (st - li * DK) * kKStep;
-        const bool use = ok && a_tile >= 0 && ((m_tile[a_tile_i][e >> 6] >> (e & 63)) & 1ull);
-        const uint32_t aoffs =
-            (uint32_t)((((a_tile * a.E + e) * kTileM + a_r) * a.d_e + k0 + acol) * 2);
-        ra[d] = bload<0>(rhid, use ? aoffs : kOutOfRange);
+#pragma unroll
+        for (int j = 0; j < AC; ++j) {
+            const bool use = ok && a_tile[j] >= 0 && ((m_tile[a_ti[j]][e >> 6] >> (e & 63)) & 1ull);
+            const uint32_t aoffs = (uint32_t)((((a_tile[j] * a.E + e) * kTileM + arow[j] % kTileM) * a.d_e +
+                                               k0 + acol[j]) * 2);
+            ra[d][j] = bload<0>(rhid, use ? aoffs : kOutOfRange);
+        }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int q = tid + i * kGThreads;
@@ -361,7 +384,9 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
         for (int d = 0; d < kDepth; ++d) {
             const int st = s0 + d;
             const int buf = d & 1;
-            *reinterpret_cast<bf16x8 *>(&As[buf][arow * kPitch + acol]) = ra[d];
+#pragma unroll
+            for (int j = 0; j < AC; ++j)
+                *reinterpret_cast<bf16x8 *>(&As[buf][arow[j] * kPitch + acol[j]]) = ra[d][j];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int q = tid + i * kGThreads;
@@ -371,44 +396,52 @@ __global__ void __launch_bounds__(kGThreads, 1) down_grouped_kernel(GroupedArgs 
             issue(st + kDepth, d);
 #pragma unroll
             for (int ks = 0; ks < kKStep / 16; ++ks) {
-                const bf16x8 fa = *reinterpret_cast<const bf16x8 *>(
-                    &As[buf][(wm * 32 + col) * kPitch + ks * 16 + kg * 8]);
+                bf16x8 fa[RB];
+#pragma unroll
+                for (int r = 0; r < RB; ++r)
+                    fa[r] = *reinterpret_cast<const bf16x8 *>(
+                        &As[buf][((wm * RB + r) * 32 + col) * kPitch + ks * 16 + kg * 8]);
 #pragma unroll
                 for (int j = 0; j < 2; ++j) {
                     const bf16x8 fb = *reinterpret_cast<const bf16x8 *>(
                         &Bs[buf][(wn * 64 + j * 32 + col) * kPitch + ks * 16 + kg * 8]);
-                    acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[j], 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < RB; ++r)
+                        acc[r][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[r], fb, acc[r][j], 0, 0, 0);
                 }
             }
         }
     }
-    // y rows of this tile (rows without a token are not written)
-    const int tile = tile_of[wm];
-    if (tile < 0)
-        return;
-    if (a.splits > 1) {
-        // the split's fp32 partial of the tile's rows
-        float *dst = a.dn_part + ((int64_t)split * a.CT + tile) * kTileM * a.d_h;
+    // y rows of the wave's tiles (rows without a token are not written)
+#pragma unroll
+    for (int r = 0; r < RB; ++r) {
+        const int tile = bt * TILES + wm * RB + r;
+        if (tile >= a.CT)
+            continue;
+        if (a.splits > 1) {
+            // the split's fp32 partial of the tile's rows
+            float *dst = a.dn_part + ((int64_t)split * a.CT + tile) * kTileM * a.d_h;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int cidx = ct * kDnCols + wn * 64 + j * 32 + col;
+#pragma unroll
+                for (int v = 0; v < 16; ++v)
+                    dst[(int64_t)acc_row(v, lane) * a.d_h + cidx] = acc[r][j][v];
+            }
+            continue;
+        }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int cidx = ct * kDnCols + wn * 64 + j * 32 + col;
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-                dst[(int64_t)acc_row(v, lane) * a.d_h + cidx] = acc[j][v];
-        }
-        return;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-        const int cidx = ct * kDnCols + wn * 64 + j * 32 + col;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) {
-            const int64_t t = tile_token(a, tile, acc_row(v, lane));
-            if (t >= 0) {
-                if constexpr (F32)
-                    a.y32[t * a.d_h + cidx] = acc[j][v];
-                else
-                    a.y[t * a.d_h + cidx] = f32_to_bf16(acc[j][v]);
+            for (int v = 0; v < 16; ++v) {
+                const int64_t t = tile_token(a, tile, acc_row(v, lane));
+                if (t >= 0) {
+                    if constexpr (F32)
+                        a.y32[t * a.d_h + cidx] = acc[r][j][v];
+                    else
+                        a.y[t * a.d_h + cidx] = f32_to_bf16(acc[r][j][v]);
+                }
             }
         }
     }
@@ -449,13 +482,45 @@ __global__ void __launch_bounds__(256) down_reduce_kernel(GroupedArgs a)
 
 }  // namespace
 
-int grouped_down_splits(int64_t CT, int64_t d_h)
+// k splits for a grid of `blocks` (tiles, column tile) workgroups: doubled while the
+// grid would not fill the chip's 256 CUs, at most 4
+static int down_splits_for(int64_t blocks)
 {
-    const int64_t blocks = ((CT + kDnTiles - 1) / kDnTiles) * (d_h / kDnCols);
     int s = 1;
     while (s < 4 && blocks * s < 256)
         s *= 2;
     return s;
+}
+
+// Four tiles per workgroup read fewer L2 bytes per product than two, but halve the
+// grid; they are taken only where that does not raise the k split (whose fp32
+// partials cost HBM traffic of their own).
+int grouped_down_tiles(int64_t CT, int64_t d_h)
+{
+    const int64_t ncol = d_h / kDnCols;
+    const int64_t b2 = ((CT + 1) / 2) * ncol, b4 = ((CT + 3) / 4) * ncol;
+    return CT >= 4 && down_splits_for(b4) <= down_splits_for(b2) ? 4 : 2;
+}
+
+int grouped_down_splits(int64_t CT, int64_t d_h)
+{
+    const int tiles = grouped_down_tiles(CT, d_h);
+    return down_splits_for(((CT + tiles - 1) / tiles) * (d_h / kDnCols));
+}
+
+// The down-projection launch: TILES chunk tiles per workgroup (grouped_down_tiles),
+// a.splits k ranges.
+template <bool F32>
+static void launch_down(const FfnPlan &p, const GroupedArgs &a, hipStream_t stream)
+{
+    const int tiles = grouped_down_tiles(p.CT, p.d_h);
+    const int64_t dn_blocks = ((p.CT + tiles - 1) / tiles) * (p.d_h / kDnCols) * a.splits;
+    if (tiles == 4)
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(down_grouped_kernel<F32, 4>), dim3((unsigned)dn_blocks), dim3(kGThreads),
+                           0, stream, a);
+    else
+        hipLaunchKernelGGL(HIP_KERNEL_NAME(down_grouped_kernel<F32, 2>), dim3((unsigned)dn_blocks), dim3(kGThreads),
+                           0, stream, a);
 }
 
 size_t grouped_partial_bytes(int64_t CT, int64_t d_h)
@@ -527,9 +592,7 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
     a.dn_part = reinterpret_cast<float *>(base + p.off_dnpart);
     const int64_t up_blocks = p.E * ((p.CT + kUpTiles - 1) / kUpTiles);
     hipLaunchKernelGGL(up_grouped_kernel, dim3((unsigned)up_blocks), dim3(kGThreads), 0, stream, a);
-    const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols) * a.splits;
-    hipLaunchKernelGGL(down_grouped_kernel<false>, dim3((unsigned)dn_blocks), dim3(kGThreads), 0,
-                       stream, a);
+    launch_down<false>(p, a, stream);
     if (a.splits > 1) {
         const int64_t q = p.CT * kTileM * (p.d_h / 4);
         hipLaunchKernelGGL(down_reduce_kernel<false>, dim3((unsigned)((q + 255) / 256)), dim3(256), 0,
@@ -558,9 +621,7 @@ hipError_t launch_grouped_down_f32(const FfnPlan &p, const uint16_t *act, const 
     a.CT = (int)p.CT;
     a.W = (int)p.W;
     a.splits = grouped_down_splits(p.CT, p.d_h);
-    const int64_t dn_blocks = ((p.CT + kDnTiles - 1) / kDnTiles) * (p.d_h / kDnCols) * a.splits;
-    hipLaunchKernelGGL(down_grouped_kernel<true>, dim3((unsigned)dn_blocks), dim3(kGThreads), 0,
-                       stream, a);
+    launch_down<true>(p, a, stream);
     if (a.splits > 1) {
         const int64_t q = p.CT * kTileM * (p.d_h / 4);
         hipLaunchKernelGGL(down_reduce_kernel<true>, dim3((unsigned)((q + 255) / 256)), dim3(256), 0,

@@ -58,9 +58,11 @@ int decode_blocks_per_cu();
 // the bytes of its per-expert tile lists.
 bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_e);
 size_t grouped_tile_bytes(int64_t CT, int64_t E);
-// k splits of its down-projection: 1, or 2 / 4 when the (tile pair, column tile)
-// workgroups would not fill the chip's 256 CUs; the splits' fp32 partials need
+// Its down-projection: chunk tiles per workgroup (4 where that does not raise the k
+// split, else 2) and k splits (1, or 2 / 4 when the (tiles, column tile) workgroups
+// would not fill the chip's 256 CUs); the splits' fp32 partials need
 // grouped_partial_bytes() of scratch.
+int grouped_down_tiles(int64_t CT, int64_t d_h);
 int grouped_down_splits(int64_t CT, int64_t d_h);
 size_t grouped_partial_bytes(int64_t CT, int64_t d_h);
 
