@@ -22,7 +22,7 @@
 //      rows go to Ht[tile][e].
 //   4. down_grouped_kernel: workgroup = (2 or 4 chunk tiles, 256 output columns): a
 //      64 (128) x 256 GEMM over k = the union of the tiles' chunks' experts x d_e
-//      (four tiles where that does not raise the k split below), ascending,
+//      (four tiles from four chunk tiles up), ascending,
 //      with the hidden rows of a tile whose chunk does not use the expert read as
 //      zero (those terms are exactly zero: the scores are zero there). Every output
 //      element is owned by one workgroup, so there is no cross-workgroup sum, and the
@@ -492,14 +492,13 @@ static int down_splits_for(int64_t blocks)
     return s;
 }
 
-// Four tiles per workgroup read fewer L2 bytes per product than two, but halve the
-// grid; they are taken only where that does not raise the k split (whose fp32
-// partials cost HBM traffic of their own).
+// Four tiles per workgroup read fewer L2 bytes per product than two, at the price of
+// a four-chunk union and, where the grid halves below the CU count, a doubled k split
+// (fp32 partials); timed, that pays except for very sparse unions (TLS 90%).
 int grouped_down_tiles(int64_t CT, int64_t d_h)
 {
-    const int64_t ncol = d_h / kDnCols;
-    const int64_t b2 = ((CT + 1) / 2) * ncol, b4 = ((CT + 3) / 4) * ncol;
-    return CT >= 4 && down_splits_for(b4) <= down_splits_for(b2) ? 4 : 2;
+    (void)d_h;
+    return CT >= 4 ? 4 : 2;
 }
 
 int grouped_down_splits(int64_t CT, int64_t d_h)

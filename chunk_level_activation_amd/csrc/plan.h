@@ -58,8 +58,8 @@ int decode_blocks_per_cu();
 // the bytes of its per-expert tile lists.
 bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_e);
 size_t grouped_tile_bytes(int64_t CT, int64_t E);
-// Its down-projection: chunk tiles per workgroup (4 where that does not raise the k
-// split, else 2) and k splits (1, or 2 / 4 when the (tiles, column tile) workgroups
+// Its down-projection: chunk tiles per workgroup (4 from four chunk tiles up, else 2)
+// and k splits (1, or 2 / 4 when the (tiles, column tile) workgroups
 // would not fill the chip's 256 CUs); the splits' fp32 partials need
 // grouped_partial_bytes() of scratch.
 int grouped_down_tiles(int64_t CT, int64_t d_h);
