@@ -82,7 +82,8 @@ __device__ __forceinline__ int64_t tile_token(const Dims &d, int tile, int r)
 
 // The weight-gradient kernel keeps k = one tile's 32 tokens per step with one step of
 // prefetch: its grid (E x 2 x 128-square tiles) already gives each CU several
-// workgroups, and the deeper loop's registers would cost that occupancy.
+// workgroups, and the deeper loop's registers would cost that occupancy (a 4-deep
+// register ring with double-buffered LDS, 168 registers, was timed slower).
 constexpr int kWBK = 32;
 constexpr int kWLP = kWBK + 8;
 
