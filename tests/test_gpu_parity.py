@@ -202,6 +202,8 @@ GROUPED = [
     ("d_e=256", 96, 32, 40, 1024, 256, False),
     ("E=40", 160, 32, 40, 2048, 128, False),
     ("E=128", 96, 32, 128, 512, 128, False),
+    # four mask words, four tiles per down workgroup
+    ("E=256", 128, 32, 256, 256, 128, False),
     ("d_h=256", 64, 32, 16, 256, 128, False),
     ("all experts active", 64, 32, 64, 1024, 128, True),
     ("recommended E=40 d_e=256", 128, 32, 40, 2048, 256, False),
