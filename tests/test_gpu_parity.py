@@ -94,6 +94,17 @@ def test_prefill_full():
     assert rel_err(y, y_ref) <= TOL_BF16
 
 
+def test_rec256_prefill_full():
+    """The recommended shape at 2048 tokens (E=40, d_e=256: two 128-unit passes in the
+    up-projection, four k steps per expert in the down-projection): unions and every
+    row of y."""
+    inp = inputs.make_workload("rec256_prefill", seed=6)
+    y, masks, lists, counts = run_ffn(inp)
+    check_union(inp.scores, inp.n, masks, lists, counts)
+    y_ref = oracle.token_ffn(inp.x, inp.scores, inp.w1, inp.w2)
+    assert rel_err(y, y_ref) <= TOL_BF16
+
+
 @pytest.mark.parametrize("tls,cls,dense", [(0.5, 0.3, False), (0.8, 0.7, False),
                                            (0.9, 0.85, False), (0.8, 0.7, True)])
 def test_large_layer_sweep_full(tls, cls, dense):
