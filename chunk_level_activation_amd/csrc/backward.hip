@@ -35,8 +35,9 @@
 //      k-contiguous operands). With two or more chunk tiles it is the forward's grouped
 //      down-projection (dA in the hidden rows' layout), with an fp32 result; with one
 //      tile, dx_kernel, workgroup = (4 tiles, 128 columns, expert split): k over the
-//      union of the 4 chunks' unions x d_e, the experts split over workgroups and the
-//      fp32 partials added in split order;
+//      union of the 4 chunks' unions x d_e, the experts split over workgroups. Split
+//      partials (either path) are added in split order by the router backward as it
+//      adds its own term, so dx is written once;
 //   5. router_token_kernel: per token, dl and the router's share of dx;
 //      router_param_kernel: dW_r, dgain, dbias as sums over the tokens in order.
 // Every sum runs in a fixed order, so equal inputs give equal bits.
@@ -698,25 +699,6 @@ __global__ void __launch_bounds__(kBT, 2) dx_kernel(DxArgs a)
             }
 }
 
-// dx = the expert splits' partials added in split order (rows with a token only).
-__global__ void __launch_bounds__(kBT) dx_reduce_kernel(DxArgs a)
-{
-    const Dims &d = a.d;
-    const int64_t i = (int64_t)blockIdx.x * kBT + threadIdx.x;    // over CT * 32 * d_h
-    if (i >= (int64_t)d.CT * kTileM * d.d_h)
-        return;
-    const int col = (int)(i % d.d_h);
-    const int64_t rt = i / d.d_h;
-    const int tile = (int)(rt / kTileM), r = (int)(rt % kTileM);
-    const int64_t t = tile_token(d, tile, r);
-    if (t < 0)
-        return;
-    float sum = 0.0f;
-    for (int z = 0; z < a.splits; ++z)
-        sum += a.part[((int64_t)z * d.CT * kTileM + rt) * d.d_h + col];
-    a.dx[t * d.d_h + col] = sum;
-}
-
 // ------------------------------------------------------------------ 5. router backward
 struct RouterArgs {
     const uint16_t *x, *w_r;
@@ -726,11 +708,38 @@ struct RouterArgs {
     const uint64_t *masks;                // [C][W]
     float *dl, *gt;                       // [T][E]
     float *dx, *dw_r, *dgain, *dbias;
+    // the expert products' dx: dx itself (dx_splits == 1), or dx_splits partials
+    // [dx_splits][CT][32][d_h] that the router backward adds in split order
+    const float *dx_part;
+    int dx_splits;
     float eps, sharpness;
     int ds_splits;
     int rt_slices;                        // 256-column slices of dx per router-token workgroup
     Dims d;
 };
+
+// The expert products' dx of token t at columns j .. j + 3: read from dx, or the sum of
+// the k-split partials in split order (the same additions the split sum would make).
+__device__ __forceinline__ float4 expert_dx4(const RouterArgs &a, int64_t t, int j)
+{
+    const Dims &d = a.d;
+    if (a.dx_splits <= 1)
+        return *reinterpret_cast<const float4 *>(&a.dx[t * d.d_h + j]);
+    const int64_t c = t / d.n;
+    const int ic = (int)(t - c * d.n);
+    const int64_t row = (c * d.MPC + ic / kTileM) * kTileM + ic % kTileM;
+    const int64_t stride = (int64_t)d.CT * kTileM * d.d_h;
+    const float *p = a.dx_part + row * d.d_h + j;
+    float4 sum = *reinterpret_cast<const float4 *>(p);
+    for (int z = 1; z < a.dx_splits; ++z) {
+        const float4 v = *reinterpret_cast<const float4 *>(p + z * stride);
+        sum.x += v.x;
+        sum.y += v.y;
+        sum.z += v.z;
+        sum.w += v.w;
+    }
+    return sum;
+}
 
 constexpr int kRtTokens = 4;              // tokens per router-token workgroup (one per wave)
 constexpr int kRtPer = 256 / kWave;       // experts per lane (E <= 256)
@@ -842,7 +851,7 @@ __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
                 if (t >= d.T)
                     continue;
                 float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + jv * 8]);
-                float4 o0 = o[0], o1 = o[1];
+                float4 o0 = expert_dx4(a, t, jv * 8), o1 = expert_dx4(a, t, jv * 8 + 4);
                 o0.x += acc[k][0], o0.y += acc[k][1], o0.z += acc[k][2], o0.w += acc[k][3];
                 o1.x += acc[k][4], o1.y += acc[k][5], o1.z += acc[k][6], o1.w += acc[k][7];
                 o[0] = o0;
@@ -905,7 +914,7 @@ __global__ void __launch_bounds__(kBT) router_token_kernel(RouterArgs a)
                     sum.w += part[g][k][c4 + 3];
                 }
                 float4 *o = reinterpret_cast<float4 *>(&a.dx[t * d.d_h + slice * kRtCols + c4]);
-                float4 o0 = *o;
+                float4 o0 = expert_dx4(a, t, slice * kRtCols + c4);
                 o0.x += sum.x, o0.y += sum.y, o0.z += sum.z, o0.w += sum.w;
                 *o = o0;
             }
@@ -1269,13 +1278,18 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     const int64_t wblocks = b.E * 2 * (b.d_e / kTM) * (b.d_h / kTM);
     hipLaunchKernelGGL(wgrad_kernel, dim3((unsigned)wblocks), dim3(kBT), 0, stream, wa);
 
+    // the expert products' dx, or (k split) their partials, which the router backward
+    // adds up in split order
+    const float *dx_part = reinterpret_cast<const float *>(at(L.dx_part));
+    int dx_parts = 1;
     if (L.dx_grouped) {
         // two or more chunk tiles: dx = sum_e dA_e W1_e is the grouped down-projection's
-        // product (dA in the hidden rows' layout, W1^T in W2's), written in fp32
+        // product (dA in the hidden rows' layout, W1^T in W2's), in fp32
         const hipError_t gerr = launch_grouped_down_f32(
-            p, pa.da_tu, w1t, masks, b.dx, reinterpret_cast<float *>(at(L.dx_part)), stream);
+            p, pa.da_tu, w1t, masks, b.dx, reinterpret_cast<float *>(at(L.dx_part)), false, stream);
         if (gerr != hipSuccess)
             return gerr;
+        dx_parts = grouped_down_splits(p.CT, b.d_h);
     } else {
         DxArgs xa;
         xa.w1t = w1t;
@@ -1289,11 +1303,7 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
                            dim3((unsigned)((p.CT + kXTiles - 1) / kXTiles), (unsigned)(b.d_h / kTM),
                                 (unsigned)L.dx_splits),
                            dim3(kBT), 0, stream, xa);
-        if (L.dx_splits > 1) {
-            const int64_t nel = p.CT * kTileM * b.d_h;
-            hipLaunchKernelGGL(dx_reduce_kernel, dim3((unsigned)((nel + kBT - 1) / kBT)), dim3(kBT), 0,
-                               stream, xa);
-        }
+        dx_parts = L.dx_splits;
     }
 
     RouterArgs ra;
@@ -1314,6 +1324,8 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     ra.eps = b.eps;
     ra.sharpness = b.sharpness;
     ra.ds_splits = L.ds_splits;
+    ra.dx_part = dx_part;
+    ra.dx_splits = dx_parts;
     ra.d = d;
     // a long batch: one workgroup per token group over all of d_h; a short one: the
     // columns split into 256-column slices, rt_slices of them per workgroup, as many as

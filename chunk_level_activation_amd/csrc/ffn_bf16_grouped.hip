@@ -602,7 +602,7 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
 
 hipError_t launch_grouped_down_f32(const FfnPlan &p, const uint16_t *act, const uint16_t *w,
                                    const uint64_t *masks, float *out, float *part,
-                                   hipStream_t stream)
+                                   bool sum_splits, hipStream_t stream)
 {
     GroupedArgs a{};
     a.hidden = const_cast<uint16_t *>(act);
@@ -621,7 +621,7 @@ hipError_t launch_grouped_down_f32(const FfnPlan &p, const uint16_t *act, const 
     a.W = (int)p.W;
     a.splits = grouped_down_splits(p.CT, p.d_h);
     launch_down<true>(p, a, stream);
-    if (a.splits > 1) {
+    if (a.splits > 1 && sum_splits) {
         const int64_t q = p.CT * kTileM * (p.d_h / 4);
         hipLaunchKernelGGL(down_reduce_kernel<true>, dim3((unsigned)((q + 255) / 256)), dim3(256), 0,
                            stream, a);

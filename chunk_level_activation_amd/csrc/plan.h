@@ -181,10 +181,12 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
 // The grouped down-projection with an fp32 result: out[t][c] = sum over the experts e of
 // the union of t's chunk of act[tile][e][row] . w[e][c], act [CT][E][32][d_e] and
 // w [E][d_h][d_e] (bf16), masks [C][W]; part holds grouped_partial_bytes(CT, d_h) bytes
-// (the split partials, when k is split). Sizes as grouped_supported admits.
+// (the split partials, when k is split). With sum_splits the partials are then added
+// into out; without, out is left alone and the caller adds the grouped_down_splits()
+// partials [splits][CT][32][d_h] in split order. Sizes as grouped_supported admits.
 hipError_t launch_grouped_down_f32(const FfnPlan &p, const uint16_t *act, const uint16_t *w,
                                    const uint64_t *masks, float *out, float *part,
-                                   hipStream_t stream);
+                                   bool sum_splits, hipStream_t stream);
 // Per-expert ascending lists of the 32-token chunk tiles whose chunk uses the expert
 // (tile_list [E][CT], tile_count [E]) from the chunk union masks [C][W].
 hipError_t launch_expert_tiles(const FfnPlan &p, const uint64_t *masks, int32_t *tile_list,
