@@ -96,11 +96,14 @@ __device__ __forceinline__ void zero_acc(f32x16 &a)
 }
 
 // ------------------------------------------------------------------ 1. tile transposes
-// dst[tile][j][r] = src[token(tile, r)][j] (zero for rows without a token).
-__global__ void __launch_bounds__(kBT) transpose_tiles_kernel(const uint16_t *src, Dims d,
-                                                              uint16_t *dst)
+// dst[tile][j][r] = src[token(tile, r)][j] (zero for rows without a token), for two
+// sources in one launch (blockIdx.z: x, then dy).
+__global__ void __launch_bounds__(kBT) transpose_tiles_kernel(const uint16_t *src0, const uint16_t *src1,
+                                                              Dims d, uint16_t *dst0, uint16_t *dst1)
 {
     __shared__ alignas(16) uint16_t t[kTileM][kTrCols + 8];
+    const uint16_t *src = blockIdx.z == 0 ? src0 : src1;
+    uint16_t *dst = blockIdx.z == 0 ? dst0 : dst1;
     const int tile = blockIdx.x, jb = blockIdx.y * kTrCols, tid = threadIdx.x;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(src, (uint64_t)d.T * d.d_h * 2);
 #pragma unroll
@@ -123,18 +126,25 @@ __global__ void __launch_bounds__(kBT) transpose_tiles_kernel(const uint16_t *sr
 }
 
 // Per expert, dst[e] = src[e]^T for an R x Cc bf16 matrix (64 x 64 blocks through LDS);
-// experts that no chunk uses are skipped (their copy is never read).
-__global__ void __launch_bounds__(kBT) transpose_weights_kernel(const uint16_t *src, int R, int Cc,
-                                                                const int32_t *tile_count,
-                                                                uint16_t *dst)
+// experts that no chunk uses are skipped (their copy is never read). Two matrices of
+// equal size per launch: blockIdx.z = job * E + e, blockIdx.x = the 64 x 64 block.
+struct TransposeJob {
+    const uint16_t *src;
+    int R, Cc;
+    uint16_t *dst;
+};
+__global__ void __launch_bounds__(kBT) transpose_weights_kernel(TransposeJob j0, TransposeJob j1, int E,
+                                                                const int32_t *tile_count)
 {
     __shared__ alignas(16) uint16_t t[64][64 + 8];
-    const int e = blockIdx.z;
+    const TransposeJob &j = blockIdx.z < (unsigned)E ? j0 : j1;
+    const int e = (int)(blockIdx.z % (unsigned)E);
     if (tile_count[e] == 0)
         return;
-    const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64, tid = threadIdx.x;
-    const uint16_t *s = src + (int64_t)e * R * Cc;
-    uint16_t *o = dst + (int64_t)e * R * Cc;
+    const int R = j.R, Cc = j.Cc, nbx = Cc / 64;
+    const int r0 = (int)(blockIdx.x / nbx) * 64, c0 = (int)(blockIdx.x % nbx) * 64, tid = threadIdx.x;
+    const uint16_t *s = j.src + (int64_t)e * R * Cc;
+    uint16_t *o = j.dst + (int64_t)e * R * Cc;
 #pragma unroll
     for (int q = 0; q < 2; ++q) {
         const int v = q * kBT + tid, row = v / 8, cv = v % 8;
@@ -1235,15 +1245,14 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     uint16_t *w1t = reinterpret_cast<uint16_t *>(at(L.w1t));
     uint16_t *w2t = reinterpret_cast<uint16_t *>(at(L.w2t));
     // W1 [E][d_e][d_h] -> [E][d_h][d_e], W2 [E][d_h][d_e] -> [E][d_e][d_h], used experts only
-    hipLaunchKernelGGL(transpose_weights_kernel, dim3((unsigned)(b.d_h / 64), (unsigned)(b.d_e / 64), (unsigned)b.E),
-                       dim3(kBT), 0, stream, b.w1, (int)b.d_e, (int)b.d_h, tile_count, w1t);
-    hipLaunchKernelGGL(transpose_weights_kernel, dim3((unsigned)(b.d_e / 64), (unsigned)(b.d_h / 64), (unsigned)b.E),
-                       dim3(kBT), 0, stream, b.w2, (int)b.d_h, (int)b.d_e, tile_count, w2t);
+    const TransposeJob tw1{b.w1, (int)b.d_e, (int)b.d_h, w1t}, tw2{b.w2, (int)b.d_h, (int)b.d_e, w2t};
+    hipLaunchKernelGGL(transpose_weights_kernel,
+                       dim3((unsigned)((b.d_h / 64) * (b.d_e / 64)), 1u, (unsigned)(2 * b.E)), dim3(kBT), 0,
+                       stream, tw1, tw2, (int)b.E, tile_count);
     uint16_t *xt = reinterpret_cast<uint16_t *>(at(L.xt));
     uint16_t *dyt = reinterpret_cast<uint16_t *>(at(L.dyt));
-    const dim3 tgrid((unsigned)p.CT, (unsigned)(b.d_h / kTrCols));
-    hipLaunchKernelGGL(transpose_tiles_kernel, tgrid, dim3(kBT), 0, stream, b.x, d, xt);
-    hipLaunchKernelGGL(transpose_tiles_kernel, tgrid, dim3(kBT), 0, stream, b.dy, d, dyt);
+    const dim3 tgrid((unsigned)p.CT, (unsigned)(b.d_h / kTrCols), 2u);
+    hipLaunchKernelGGL(transpose_tiles_kernel, tgrid, dim3(kBT), 0, stream, b.x, b.dy, d, xt, dyt);
 
     PassArgs pa;
     pa.x = b.x;
