@@ -963,8 +963,10 @@ static_assert((kRpCols / 8) * kRpLanes == kBT, "thread = (piece, token lane)");
 // over the tokens tl, tl + 8, ... of the split, 8 of them in flight; the 8 lanes are
 // added in lane order through LDS. The workgroups of column block 0 also sum gt and
 // dl per expert (thread (expert tid % 8, slice tid / 8 of 32), slices in order).
+// With one split (direct) part is dW_r itself and the gain and bias sums go straight to
+// dgain and dbias: no reduction launch follows.
 __global__ void __launch_bounds__(kBT) router_param_kernel(RouterArgs a, int splits, float *part,
-                                                           float *gpart)
+                                                           float *gpart, bool direct)
 {
     const Dims &d = a.d;
     const int e0 = blockIdx.x * kRpE, jb = blockIdx.y, z = blockIdx.z, tid = threadIdx.x;
@@ -1067,8 +1069,15 @@ __global__ void __launch_bounds__(kBT) router_param_kernel(RouterArgs a, int spl
             g += pg[s2 * kRpE + tid];
             bsum += pb[s2 * kRpE + tid];
         }
-        gpart[((int64_t)z * d.E + e0 + tid) * 2] = g;
-        gpart[((int64_t)z * d.E + e0 + tid) * 2 + 1] = bsum;
+        if (direct) {
+            if (a.dgain)
+                a.dgain[e0 + tid] = g;
+            if (a.dbias)
+                a.dbias[e0 + tid] = bsum;
+        } else {
+            gpart[((int64_t)z * d.E + e0 + tid) * 2] = g;
+            gpart[((int64_t)z * d.E + e0 + tid) * 2 + 1] = bsum;
+        }
     }
 }
 
@@ -1355,8 +1364,15 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     float *rp = reinterpret_cast<float *>(at(L.rp_part));
     float *rg = reinterpret_cast<float *>(at(L.rp_gpart));
     const unsigned eb = (unsigned)((b.E + kRpE - 1) / kRpE);
+    // (dW_r takes 16-byte stores; a dW_r the caller did not align that far takes the
+    // reduction path)
+    if (splits == 1 && reinterpret_cast<uintptr_t>(b.dw_r) % 16 == 0) {
+        hipLaunchKernelGGL(router_param_kernel, dim3(eb, (unsigned)(b.d_h / kRpCols), 1u), dim3(kBT), 0,
+                           stream, ra, 1, b.dw_r, rg, true);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(router_param_kernel, dim3(eb, (unsigned)(b.d_h / kRpCols), (unsigned)splits),
-                       dim3(kBT), 0, stream, ra, splits, rp, rg);
+                       dim3(kBT), 0, stream, ra, splits, rp, rg, false);
     const dim3 rgrid((unsigned)b.E, (unsigned)(b.d_h / kBT));
 #define RP_REDUCE(ZC)                                                                        \
     hipLaunchKernelGGL(router_param_reduce_kernel<ZC>, rgrid, dim3(kBT), 0, stream, ra, splits, \
