@@ -18,8 +18,8 @@
 //
 // Kernels, in stream order (all products on 32x32x16 bf16 MFMA, fp32 accumulation):
 //   0. the forward router (recomputed: logits and scores, with its d_h split when it
-//      takes one), the chunk unions and the per-expert tile lists (the forward's
-//      kernels);
+//      takes one); then union_tiles_kernel: the chunk union masks and the per-expert
+//      tile lists in one launch;
 //   1. transpose_tiles_kernel: x and dy copied per 32-token chunk tile as
 //      [tile][d_h][32 tokens], so the weight-gradient products, whose k is the token,
 //      read k-contiguous operands;
@@ -93,6 +93,83 @@ __device__ __forceinline__ void zero_acc(f32x16 &a)
 #pragma unroll
     for (int v = 0; v < 16; ++v)
         a[v] = 0.0f;
+}
+
+// ------------------------------------------------------------------ 0. unions and tile lists
+// From the recomputed scores, in one launch (expert e of a chunk is in its union when
+// some token of the chunk has s[t,e] != 0; -0 is inactive, NaN active, as in the
+// forward's union):
+//   blocks [0, C): chunk c's union mask words, wave w -> word w, lane -> expert;
+//   blocks [C, C + E): expert e's ascending list of the chunk tiles whose chunk holds
+//     it (a chunk's rank is the count of earlier chunks holding e), and their count.
+// Whether s[t,e] != 0 for some t in [t0, t1): 32 loads in flight at a time (tokens past
+// t1 re-read the last one and are masked), so no load waits on its own.
+__device__ __forceinline__ bool any_active(const float *__restrict__ scores, int E, int e, int64_t t0,
+                                           int64_t t1)
+{
+    constexpr int kB = 32;
+    bool f = false;
+    for (int64_t tb = t0; tb < t1; tb += kB) {
+        float v[kB];
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            v[i] = scores[(tb + i < t1 ? tb + i : t1 - 1) * E + e];
+#pragma unroll
+        for (int i = 0; i < kB; ++i)
+            f |= tb + i < t1 && v[i] != 0.0f;
+    }
+    return f;
+}
+
+__global__ void __launch_bounds__(kBT) union_tiles_kernel(const float *__restrict__ scores, Dims d,
+                                                          uint64_t *masks, int32_t *tile_list,
+                                                          int32_t *tile_count)
+{
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid % kWave;
+    if (blockIdx.x < (unsigned)d.C) {
+        const int64_t c = blockIdx.x;
+        const int64_t t0 = c * d.n, t1 = t0 + d.n < d.T ? t0 + d.n : d.T;
+        for (int w = wave; w < d.W; w += kBT / kWave) {
+            const int e = w * kWave + lane;
+            const bool active = e < d.E && any_active(scores, d.E, e, t0, t1);
+            const uint64_t word = __ballot(active);
+            if (lane == 0)
+                masks[c * d.W + w] = word;
+        }
+        return;
+    }
+    const int e = (int)(blockIdx.x - (unsigned)d.C);
+    __shared__ int wsum[kBT / kWave];
+    __shared__ int base;
+    if (tid == 0)
+        base = 0;
+    __syncthreads();
+    for (int c0 = 0; c0 < d.C; c0 += kBT) {
+        const int c = c0 + tid;
+        bool f = false;
+        if (c < d.C) {
+            const int64_t t0 = (int64_t)c * d.n, t1 = t0 + d.n < d.T ? t0 + d.n : d.T;
+            f = any_active(scores, d.E, e, t0, t1);
+        }
+        const uint64_t bal = __ballot(f);
+        const int below = __popcll(bal & ((1ull << lane) - 1ull));
+        if (lane == 0)
+            wsum[wave] = __popcll(bal);
+        __syncthreads();
+        int off = base;
+        for (int w = 0; w < wave; ++w)
+            off += wsum[w];
+        if (f)
+            for (int m = 0; m < d.MPC; ++m)
+                tile_list[(int64_t)e * d.CT + (int64_t)(off + below) * d.MPC + m] = c * d.MPC + m;
+        __syncthreads();
+        if (tid == 0)
+            for (int w = 0; w < kBT / kWave; ++w)
+                base += wsum[w];
+        __syncthreads();
+    }
+    if (tid == 0)
+        tile_count[e] = base * d.MPC;
 }
 
 // ------------------------------------------------------------------ 1. tile transposes
@@ -1121,7 +1198,7 @@ __global__ void __launch_bounds__(kBT) router_param_reduce_kernel(RouterArgs a, 
 // ------------------------------------------------------------------ workspace layout
 struct BwdLayout {
     FfnPlan p;
-    size_t masks, lists, counts, tile_list, tile_count;
+    size_t masks, tile_list, tile_count;
     size_t logits, scores, ds, dl, gt;
     size_t xt, dyt, da_tu, da_ut, sh_ut, rp_part, rp_gpart, w1t, w2t, dx_part;
     size_t router;        // the forward router's split workspace (0 bytes when it takes none)
@@ -1163,8 +1240,6 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
         return o;
     };
     L.masks = take(8 * p.C * p.W);
-    L.lists = take(4 * p.C * E);
-    L.counts = take(4 * p.C);
     L.tile_list = take(4 * E * p.CT);
     L.tile_count = take(4 * E);
     L.logits = take(4 * T * E);
@@ -1190,8 +1265,6 @@ BwdLayout bwd_layout(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t n)
                                        : 0);
     L.total = off;
     L.p.off_masks = L.masks;
-    L.p.off_lists = L.lists;
-    L.p.off_counts = L.counts;
     return L;
 }
 
@@ -1234,13 +1307,9 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
                                         logits, 1.0f, nullptr, rws, rws ? b.xcds : 0, stream);
     if (err != hipSuccess)
         return err;
-    if ((err = launch_union(p, scores, ws, nullptr, nullptr, nullptr, stream)) != hipSuccess)
-        return err;
-    const uint64_t *masks = reinterpret_cast<const uint64_t *>(at(L.masks));
+    uint64_t *masks = reinterpret_cast<uint64_t *>(at(L.masks));
     int32_t *tile_list = reinterpret_cast<int32_t *>(at(L.tile_list));
     int32_t *tile_count = reinterpret_cast<int32_t *>(at(L.tile_count));
-    if ((err = launch_expert_tiles(p, masks, tile_list, tile_count, stream)) != hipSuccess)
-        return err;
     Dims d;
     d.T = b.T;
     d.n = (int)p.n;
@@ -1251,6 +1320,8 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     d.W = (int)p.W;
     d.MPC = (int)p.MPC;
     d.CT = (int)p.CT;
+    hipLaunchKernelGGL(union_tiles_kernel, dim3((unsigned)(p.C + b.E)), dim3(kBT), 0, stream, scores, d,
+                       masks, tile_list, tile_count);
     uint16_t *w1t = reinterpret_cast<uint16_t *>(at(L.w1t));
     uint16_t *w2t = reinterpret_cast<uint16_t *>(at(L.w2t));
     // W1 [E][d_e][d_h] -> [E][d_h][d_e], W2 [E][d_h][d_e] -> [E][d_e][d_h], used experts only

@@ -10,17 +10,14 @@
 // Over many chunks an expert's weights serve every chunk whose union holds it, so
 // each launch should read them once, not once per chunk:
 //   1. union_kernel: per-chunk union masks, lists and counts.
-//   2. (expert_tiles_kernel, for the layer backward: for every expert, the ascending
-//      list of 32-token chunk tiles whose chunk uses it. The forward does without it:
-//      each up workgroup finds its own tiles in the masks.)
-//   3. up_grouped_kernel: workgroup = (expert e, 4 of e's tiles): a 128 x d_e x d_h
+//   2. up_grouped_kernel: workgroup = (expert e, 4 of e's tiles): a 128 x d_e x d_h
 //      GEMM (x rows gathered, W1_e read once per workgroup and shared through the
 //      XCD's L2 by the workgroups of the same expert, which the grid places on one
 //      XCD), double-buffered through LDS with kUpDepth k steps of loads in flight
 //      (few enough registers for two 8-wave workgroups per CU), 32x32x16 bf16 MFMA,
 //      then Swish and the score (staged in LDS with the rows' tokens); the bf16 hidden
 //      rows go to Ht[tile][e].
-//   4. down_grouped_kernel: workgroup = (2 or 4 chunk tiles, 256 output columns): a
+//   3. down_grouped_kernel: workgroup = (2 or 4 chunk tiles, 256 output columns): a
 //      64 (128) x 256 GEMM over k = the union of the tiles' chunks' experts x d_e
 //      (four tiles from four chunk tiles up), ascending,
 //      with the hidden rows of a tile whose chunk does not use the expert read as
@@ -29,7 +26,7 @@
 //      column tiles map to XCDs so each W2 column slice stays in one L2. When those
 //      workgroups would not fill the chip (few chunks, e.g. 16 chunks of a d_h = 4096
 //      layer: 128 workgroups), k is split in 2 or 4 contiguous ranges, each
-//      workgroup writes its fp32 partial tile, and 5. down_reduce_kernel adds the
+//      workgroup writes its fp32 partial tile, and 4. down_reduce_kernel adds the
 //      partials in split order into y.
 #include "common.h"
 #include "plan.h"
@@ -61,8 +58,6 @@ struct GroupedArgs {
     uint16_t *y;
     uint16_t *hidden;            // [CT][E][32][d_e]
     const uint64_t *masks;       // [C][W]
-    int32_t *tile_list;          // [E][CT]
-    int32_t *tile_count;         // [E]
     float *dn_part;              // [splits][CT * 32][d_h] when splits > 1
     float *y32;                  // fp32 output instead of y (the layer backward's dx)
     int64_t T;
@@ -84,40 +79,6 @@ __device__ __forceinline__ int64_t tile_token(const GroupedArgs &a, int tile, in
 // 32x32 accumulator layout: element i of a lane is row (i/4)*8 + (lane/32)*4 + i%4 of
 // column lane%32.
 __device__ __forceinline__ int acc_row(int i, int lane) { return (i / 4) * 8 + (lane >> 5) * 4 + (i % 4); }
-
-// ------------------------------------------------------------------ expert tile lists
-// One workgroup per expert: the chunks whose union holds e, ascending, expanded to
-// their MPC tiles.
-__global__ void __launch_bounds__(256) expert_tiles_kernel(GroupedArgs a)
-{
-    const int e = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-    __shared__ int wsum[4];
-    __shared__ int base;
-    if (tid == 0)
-        base = 0;
-    __syncthreads();
-    for (int c0 = 0; c0 < a.C; c0 += 256) {
-        const int c = c0 + tid;
-        const bool f = c < a.C && ((a.masks[(int64_t)c * a.W + (e >> 6)] >> (e & 63)) & 1ull);
-        const uint64_t bal = __ballot(f);
-        const int below = __popcll(bal & ((1ull << lane) - 1ull));
-        if (lane == 0)
-            wsum[wave] = __popcll(bal);
-        __syncthreads();
-        int off = base;
-        for (int w = 0; w < wave; ++w)
-            off += wsum[w];
-        if (f)
-            for (int m = 0; m < a.MPC; ++m)
-                a.tile_list[(int64_t)e * a.CT + (int64_t)(off + below) * a.MPC + m] = c * a.MPC + m;
-        __syncthreads();
-        if (tid == 0)
-            base += wsum[0] + wsum[1] + wsum[2] + wsum[3];
-        __syncthreads();
-    }
-    if (tid == 0)
-        a.tile_count[e] = base * a.MPC;
-}
 
 // ------------------------------------------------------------------ up (grouped GEMM)
 // At least 4 waves per SIMD (at most 128 registers): two 8-wave workgroups per CU.
@@ -536,29 +497,6 @@ bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_
            (uint64_t)E * d_e * d_h * 2 < 0x7fffffffull;
 }
 
-size_t grouped_tile_bytes(int64_t CT, int64_t E)
-{
-    return (size_t)E * CT * 4 + (size_t)E * 4;
-}
-
-hipError_t launch_expert_tiles(const FfnPlan &p, const uint64_t *masks, int32_t *tile_list,
-                               int32_t *tile_count, hipStream_t stream)
-{
-    GroupedArgs a{};
-    a.masks = masks;
-    a.tile_list = tile_list;
-    a.tile_count = tile_count;
-    a.T = p.T;
-    a.n = (int)p.n;
-    a.E = (int)p.E;
-    a.C = (int)p.C;
-    a.MPC = (int)p.MPC;
-    a.CT = (int)p.CT;
-    a.W = (int)p.W;
-    hipLaunchKernelGGL(expert_tiles_kernel, dim3((unsigned)p.E), dim3(256), 0, stream, a);
-    return hipGetLastError();
-}
-
 hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const float *scores,
                                    const uint16_t *w1, const uint16_t *w2, uint16_t *y, void *ws,
                                    uint64_t *masks_out, int32_t *lists_out, int32_t *counts_out,
@@ -576,8 +514,6 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
     a.y = y;
     a.hidden = reinterpret_cast<uint16_t *>(base + p.off_hidden);
     a.masks = reinterpret_cast<const uint64_t *>(base + p.off_masks);
-    a.tile_list = reinterpret_cast<int32_t *>(base + p.off_tiles);
-    a.tile_count = reinterpret_cast<int32_t *>(base + p.off_tiles + (size_t)p.E * p.CT * 4);
     a.T = p.T;
     a.n = (int)p.n;
     a.d_h = (int)p.d_h;

@@ -54,10 +54,8 @@ bool decode_supported(int64_t CT, int64_t d_h, int64_t E, int64_t d_e, int xcds,
 size_t decode_scratch_bytes(int64_t d_h, int64_t E, int64_t d_e);
 int decode_blocks_per_cu();
 
-// Expert-grouped multi-chunk bf16 schedule (ffn_bf16_grouped.hip): sizes it takes and
-// the bytes of its per-expert tile lists.
+// Expert-grouped multi-chunk bf16 schedule (ffn_bf16_grouped.hip): the sizes it takes.
 bool grouped_supported(int64_t T, int64_t CT, int64_t d_h, int64_t E, int64_t d_e);
-size_t grouped_tile_bytes(int64_t CT, int64_t E);
 // Its down-projection: chunk tiles per workgroup (4 from four chunk tiles up, else 2)
 // and k splits (1, or 2 / 4 when the (tiles, column tile) workgroups
 // would not fill the chip's 256 CUs); the splits' fp32 partials need
@@ -81,7 +79,7 @@ struct FfnPlan {
     bool grouped;         // sizes admit the expert-grouped multi-chunk schedule
     // scratch after the control block (byte offsets)
     size_t off_masks, off_lists, off_counts;   // fp32 path union
-    size_t off_hidden, off_partials, off_tiles;
+    size_t off_hidden, off_partials;
     size_t off_dnpart;    // grouped schedule: the down-projection's split partials
     size_t total_bytes;
 };
@@ -116,9 +114,6 @@ inline FfnPlan make_plan(int64_t T, int64_t d_h, int64_t E, int64_t d_e, int64_t
     if (p.decode && decode_scratch_bytes(d_h, E, d_e) > partials)
         partials = decode_scratch_bytes(d_h, E, d_e);
     off = align_up(off + partials, 256);
-    p.off_tiles = off;
-    if (p.grouped)
-        off = align_up(off + grouped_tile_bytes(p.CT, E), 256);
     p.off_dnpart = off;
     if (p.grouped)
         off = align_up(off + grouped_partial_bytes(p.CT, d_h), 256);
@@ -187,10 +182,6 @@ hipError_t launch_ffn_bf16_grouped(const FfnPlan &p, const uint16_t *x, const fl
 hipError_t launch_grouped_down_f32(const FfnPlan &p, const uint16_t *act, const uint16_t *w,
                                    const uint64_t *masks, float *out, float *part,
                                    bool sum_splits, hipStream_t stream);
-// Per-expert ascending lists of the 32-token chunk tiles whose chunk uses the expert
-// (tile_list [E][CT], tile_count [E]) from the chunk union masks [C][W].
-hipError_t launch_expert_tiles(const FfnPlan &p, const uint64_t *masks, int32_t *tile_list,
-                               int32_t *tile_count, hipStream_t stream);
 hipError_t launch_ffn_f32(const FfnPlan &p, const float *x, const float *scores,
                           const float *w1, const float *w2, float *y, void *ws,
                           hipStream_t stream);
