@@ -465,9 +465,14 @@ __global__ void __launch_bounds__(kPassThreads, 4) expert_pass_kernel(PassArgs a
 constexpr int kNarrowUnits = 32;
 constexpr int kNarrowGroup = kBT;             // 4 waves per product
 constexpr int kNarrowThreads = 2 * kNarrowGroup;
+// k steps of loads in flight: 2 (at most 128 registers, two workgroups per CU), or 4
+// (153 registers, one per CU) when the grid has no more workgroups than CUs: the
+// weight stream then has twice the bytes in flight (T = 32 call 112.7 -> 110.2 us)
 
-__global__ void __launch_bounds__(kNarrowThreads, 2) expert_pass_narrow_kernel(PassArgs a)
+template <int DEPTH>
+__global__ void __launch_bounds__(kNarrowThreads, DEPTH == 2 ? 2 : 1) expert_pass_narrow_kernel(PassArgs a)
 {
+    static_assert(DEPTH % 2 == 0, "the LDS double buffer alternates with the ring slot");
     const Dims &d = a.d;
     const int nub = d.d_e / kNarrowUnits;
     const int e = blockIdx.x % d.E;
@@ -518,7 +523,7 @@ __global__ void __launch_bounds__(kNarrowThreads, 2) expert_pass_narrow_kernel(P
     f32x16 acc;
     zero_acc(acc);
     {
-        u32x4 ra[kPassDepth][4], rb[kPassDepth];
+        u32x4 ra[DEPTH][4], rb[DEPTH];
         auto issue = [&](int st, int dd) {
             const uint32_t okm = 0u - (uint32_t)(st < KS);
             const uint32_t kb = (uint32_t)(st * kPK * 2);
@@ -530,13 +535,13 @@ __global__ void __launch_bounds__(kNarrowThreads, 2) expert_pass_narrow_kernel(P
             rb[dd] = load16(rB, ((boff + kb) & okm) | (kOOB & ~okm));
         };
 #pragma unroll
-        for (int dd = 0; dd < kPassDepth; ++dd) {
+        for (int dd = 0; dd < DEPTH; ++dd) {
             issue(dd, dd);
             __builtin_amdgcn_sched_barrier(0);
         }
-        for (int s0 = 0; s0 < KS; s0 += kPassDepth) {
+        for (int s0 = 0; s0 < KS; s0 += DEPTH) {
 #pragma unroll
-            for (int dd = 0; dd < kPassDepth; ++dd) {
+            for (int dd = 0; dd < DEPTH; ++dd) {
                 const int buf = dd & 1;
 #pragma unroll
                 for (int i = 0; i < 4; ++i)
@@ -544,7 +549,7 @@ __global__ void __launch_bounds__(kNarrowThreads, 2) expert_pass_narrow_kernel(P
                         ra[dd][i];
                 *reinterpret_cast<u32x4 *>(&Bs[g][buf][brow * kPP + acol]) = rb[dd];
                 __syncthreads();
-                issue(s0 + dd + kPassDepth, dd);
+                issue(s0 + dd + DEPTH, dd);
 #pragma unroll
                 for (int ks = 0; ks < kPK / 16; ++ks) {
                     const bf16x8 fa =
@@ -1348,8 +1353,11 @@ hipError_t launch_layer_backward(const BackwardArgs &b, void *ws, hipStream_t st
     pa.sh_ut = reinterpret_cast<uint16_t *>(at(L.sh_ut));
     pa.d = d;
     const int64_t pass_blocks = b.E * ((p.CT + kPassTiles - 1) / kPassTiles);
-    if (L.ds_splits > 1)
-        hipLaunchKernelGGL(expert_pass_narrow_kernel, dim3((unsigned)(pass_blocks * L.ds_splits)),
+    if (L.ds_splits > 1 && pass_blocks * L.ds_splits <= 256)
+        hipLaunchKernelGGL(expert_pass_narrow_kernel<4>, dim3((unsigned)(pass_blocks * L.ds_splits)),
+                           dim3(kNarrowThreads), 0, stream, pa);
+    else if (L.ds_splits > 1)
+        hipLaunchKernelGGL(expert_pass_narrow_kernel<2>, dim3((unsigned)(pass_blocks * L.ds_splits)),
                            dim3(kNarrowThreads), 0, stream, pa);
     else
         hipLaunchKernelGGL(expert_pass_kernel, dim3((unsigned)pass_blocks), dim3(kPassThreads), 0, stream, pa);
